@@ -1,0 +1,328 @@
+"""CPU float64 oracle for one tensor-parallel rank's share of a decoder layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module.  It shares no code with
+the HIP library (no kernels, headers, helpers or tables) and imports nothing
+from it; inputs reach it as plain float64 numpy arrays.
+
+Everything is written as the plain definition of what the method computes,
+with numpy's matmul, exp and scipy's erf as the only library primitives:
+no blocking, fusion or reordering.
+
+Sources (web pages; each function names the section it follows):
+  P1  "Tensor Parallel：当一张 GPU 放不下一个大模型" (mini vLLM series)
+  P2  "张量并行（Tensor Parallelism）推理部署实战：从 Megatron-LM 切分原理到 vLLM
+       多卡配置与性能调优"
+  P3  "Tensor Parallel 深入解析：多加 GPU，推理为什么可能更慢"
+
+Conventions (readings where the pages leave a choice open):
+  * ``Y = X W`` with X ``[tokens, in]``.  Weights are stored as ``nn.Linear``
+    stores them, ``w = W^T`` of shape ``[out, in]`` (P2 section 1.1/1.2
+    sketches; P3 "两张卡如何共同算出一层" notes frameworks may keep the
+    transpose).  ``linear(x, w) = x @ w.T``.
+  * Shards are contiguous blocks in rank order (P1 "Attention 里的 tensor
+    parallel": heads 0..7 on GPU 0, 8..15 on GPU 1, ...; P3: left/right halves).
+  * A fused local QKV weight stacks the rank's q heads, then its k heads, then
+    its v heads, each head ``D`` consecutive output features.
+  * GQA: global q head j reads KV head ``j // (Hq/Hkv)``; with contiguous
+    sharding local q head h reads local KV head ``h // (Hq_l/Hkv_l)``.
+  * Attention scale ``1/sqrt(D)``; causal masking aligned at the end of the key
+    span (key t is visible to query position p iff t <= p); softmax with the
+    row maximum subtracted.
+  * No positional encoding (the pages never specify one); no bias; dropout is
+    the identity at inference (P2 section 二).
+  * RMSNorm ``x * (mean(x^2) + eps)^(-1/2) * gamma`` -- not on the pages,
+    parity unpinned by them (pinned here by closed forms only).
+  * GELU is the exact erf form, ``g * Phi(g)``.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "round_bf16", "linear", "column_shard", "row_shard", "input_shard",
+    "column_linear", "row_linear_partial", "reduce_partials", "concat_columns",
+    "silu", "gelu", "local_activation", "rmsnorm", "attention", "qkv_shard",
+    "mlp_unsharded", "mlp_rank_partial", "attention_block_unsharded",
+    "attention_rank_partial", "layer_unsharded", "layer_sharded",
+]
+
+
+def _identity(a):
+    return a
+
+
+# ---------------------------------------------------------------------------
+# bf16 storage rounding (used only by the storage-faithful diagnostic mode)
+# ---------------------------------------------------------------------------
+
+def round_bf16(a) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits: with ``a = m * 2**e`` and
+    ``0.5 <= |m| < 1`` the result is ``rint(m * 2**8) * 2**(e - 8)``.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+# ---------------------------------------------------------------------------
+# Linear layers and their shards (P1 "Column Parallel Linear：按输出维度切",
+# "Row Parallel Linear：按输入维度切"; P2 sections 1.1 and 1.2; P3
+# "两张卡如何共同算出一层")
+# ---------------------------------------------------------------------------
+
+def linear(x, w):
+    """Unsharded ``Y = X W`` with ``w = W^T`` stored ``[out, in]``."""
+    return np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
+
+
+def _block(n: int, r: int, R: int) -> slice:
+    if R <= 0 or not (0 <= r < R):
+        raise ValueError(f"rank {r} out of range for TP size {R}")
+    if n % R != 0:
+        raise ValueError(f"dimension {n} is not divisible by TP size {R}")
+    b = n // R
+    return slice(r * b, (r + 1) * b)
+
+
+def column_shard(w, r: int, R: int):
+    """Rank r's block of output features: rows ``[r*N/R, (r+1)*N/R)`` of the
+    stored ``[N, K]`` weight (the column block of the math W)."""
+    w = np.asarray(w)
+    return w[_block(w.shape[0], r, R), :]
+
+
+def row_shard(w, r: int, R: int):
+    """Rank r's block of input features: columns ``[r*K/R, (r+1)*K/R)`` of the
+    stored ``[N, K]`` weight (the row block of the math W)."""
+    w = np.asarray(w)
+    return w[:, _block(w.shape[1], r, R)]
+
+
+def input_shard(x, r: int, R: int):
+    """Rank r's block of the last dimension of an activation."""
+    x = np.asarray(x)
+    return x[..., _block(x.shape[-1], r, R)]
+
+
+def column_linear(x, w_shard):
+    """Column-parallel linear on one rank: the full input times the rank's
+    output block gives the rank's output slice ``Y_r = X W_r``; no exchange."""
+    return linear(x, w_shard)
+
+
+def row_linear_partial(x_shard, w_shard):
+    """Row-parallel linear on one rank: the rank's input slice times the rank's
+    input block gives a partial sum of the full output ``Y_r = X_r W_r``."""
+    return linear(x_shard, w_shard)
+
+
+def concat_columns(parts):
+    """Reassemble column-parallel outputs: ``Y = [Y_0, Y_1, ...]``."""
+    return np.concatenate([np.asarray(p, np.float64) for p in parts], axis=-1)
+
+
+def reduce_partials(partials, residual=None):
+    """The arithmetic of the all-reduce: ``Y = sum_r Y_r``, taken in rank order
+    0..R-1, plus an optional residual added once after the sum."""
+    acc = np.zeros_like(np.asarray(partials[0], np.float64))
+    for p in partials:
+        acc = acc + np.asarray(p, np.float64)
+    if residual is not None:
+        acc = acc + np.asarray(residual, np.float64)
+    return acc
+
+
+# ---------------------------------------------------------------------------
+# Local elementwise work (P1 "MLP 里的 tensor parallel": activation(gate_i) *
+# up_i is rank-local; P2 section 二: GELU between fc1 and fc2)
+# ---------------------------------------------------------------------------
+
+def silu(g):
+    g = np.asarray(g, np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def gelu(g):
+    g = np.asarray(g, np.float64)
+    return 0.5 * g * (1.0 + _erf(g / math.sqrt(2.0)))
+
+
+def local_activation(g, u=None, act: str = "swiglu"):
+    """``swiglu``: SiLU(gate) * up;  ``gelu``: GELU(g);  ``none``: g."""
+    if act == "swiglu":
+        return silu(g) * np.asarray(u, np.float64)
+    if act == "gelu":
+        return gelu(g)
+    if act == "none":
+        return np.asarray(g, np.float64)
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def rmsnorm(x, gamma, eps: float):
+    """Row-wise RMS normalisation with a learned scale (pre-norm)."""
+    x = np.asarray(x, np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gamma, np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Attention over the rank's local heads (P1 "Attention 里的 tensor parallel";
+# P2 section 2.1; GQA placement: P3 "权重变小，不代表所有显存都按比例变小")
+# ---------------------------------------------------------------------------
+
+def attention(q, k, v, causal: bool, scale: float | None = None, q_pos=None):
+    """Scaled dot-product attention with grouped KV heads.
+
+    q ``[B, Sq, Hq, D]``, k/v ``[B, Skv, Hkv, D]`` -> o ``[B, Sq, Hq, D]``.
+    q head h reads KV head ``h // (Hq // Hkv)``.  ``q_pos[s]`` is the absolute
+    position of query row s (default: the last Sq positions of the key span);
+    with ``causal`` key t is visible to row s iff ``t <= q_pos[s]``.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, Sq, Hq, D = q.shape
+    _, Skv, Hkv, _ = k.shape
+    if Hq % Hkv != 0:
+        raise ValueError("q heads must be a multiple of KV heads")
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if q_pos is None:
+        q_pos = np.arange(Sq) + (Skv - Sq)
+    q_pos = np.asarray(q_pos)
+    visible = np.arange(Skv)[None, :] <= q_pos[:, None]          # [Sq, Skv]
+    out = np.empty_like(q)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // G
+            s = (q[b, :, h, :] @ k[b, :, hk, :].T) * scale        # [Sq, Skv]
+            if causal:
+                s = np.where(visible, s, -np.inf)
+            s = s - np.max(s, axis=-1, keepdims=True)
+            p = np.exp(s)
+            p = p / np.sum(p, axis=-1, keepdims=True)
+            out[b, :, h, :] = p @ v[b, :, hk, :]
+    return out
+
+
+def qkv_shard(wq, wk, wv, r: int, R: int, head_dim: int):
+    """Rank r's fused QKV weight ``[(Hq_l + 2*Hkv_l)*D, H]``: its block of q
+    heads, then its block of KV heads for k, then for v."""
+    wq, wk, wv = (np.asarray(a) for a in (wq, wk, wv))
+    for a in (wq, wk, wv):
+        if a.shape[0] % head_dim != 0:
+            raise ValueError("projection rows must be whole heads")
+    n_q, n_kv = wq.shape[0] // head_dim, wk.shape[0] // head_dim
+    if n_q % R or n_kv % R:
+        raise ValueError("q and KV heads must divide by the TP size")
+    return np.concatenate([column_shard(wq, r, R), column_shard(wk, r, R),
+                           column_shard(wv, r, R)], axis=0)
+
+
+# ---------------------------------------------------------------------------
+# MLP block (P1 "MLP 里的 tensor parallel"; P2 section 二 MegatronMLP)
+# ---------------------------------------------------------------------------
+
+def mlp_unsharded(x, w_in, w_out, act: str, w_up=None):
+    """Unsharded MLP.  gated: ``(act(x Wg) * (x Wu)) Wd``; gelu: ``GELU(x A) B``;
+    none: ``(x A) B``.  ``w_in`` is the gate (or fc1) weight."""
+    g = linear(x, w_in)
+    u = linear(x, w_up) if act == "swiglu" else None
+    return linear(local_activation(g, u, act), w_out)
+
+
+def mlp_rank_partial(x, w_in, w_out, act: str, r: int, R: int, w_up=None,
+                     store=_identity):
+    """Rank r's MLP share: column-parallel gate/up (or fc1), the local
+    activation on the rank's intermediate slice, row-parallel down (or fc2)
+    giving the rank's partial of the hidden output.  ``store`` is applied where
+    an implementation keeps an intermediate in its storage type."""
+    g = store(column_linear(x, column_shard(w_in, r, R)))
+    u = store(column_linear(x, column_shard(w_up, r, R))) if act == "swiglu" else None
+    h = store(local_activation(g, u, act))
+    return row_linear_partial(h, row_shard(w_out, r, R))
+
+
+# ---------------------------------------------------------------------------
+# Attention block and the pre-norm decoder layer
+# ---------------------------------------------------------------------------
+
+def _split_heads(a, n_heads: int, head_dim: int):
+    M = a.shape[0]
+    return a.reshape(1, M, n_heads, head_dim)
+
+
+def attention_block_unsharded(x, wq, wk, wv, wo, head_dim: int, causal: bool = True,
+                              rows=None):
+    """Unsharded multi-head (GQA) attention block ``attn(x) Wo`` over one
+    sequence ``x [S, H]``.  ``rows`` selects which query rows to return (all
+    keys are always used)."""
+    S = x.shape[0]
+    n_q, n_kv = wq.shape[0] // head_dim, wk.shape[0] // head_dim
+    k = _split_heads(linear(x, wk), n_kv, head_dim)
+    v = _split_heads(linear(x, wv), n_kv, head_dim)
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    q = _split_heads(linear(x[rows], wq), n_q, head_dim)
+    o = attention(q, k, v, causal=causal, q_pos=rows)
+    return linear(o.reshape(len(rows), n_q * head_dim), wo)
+
+
+def attention_rank_partial(x, wq, wk, wv, wo, head_dim: int, r: int, R: int,
+                           causal: bool = True, rows=None, store=_identity):
+    """Rank r's attention share: its fused QKV slice (column-parallel), local
+    attention over its q heads and their KV heads, its o_proj input block
+    (row-parallel) giving a partial of the hidden output."""
+    S = x.shape[0]
+    n_q, n_kv = wq.shape[0] // head_dim, wk.shape[0] // head_dim
+    hq, hkv = n_q // R, n_kv // R
+    wqkv = qkv_shard(wq, wk, wv, r, R, head_dim)
+    dq, dkv = hq * head_dim, hkv * head_dim
+    kv = store(column_linear(x, wqkv[dq:, :]))
+    k = _split_heads(kv[:, :dkv], hkv, head_dim)
+    v = _split_heads(kv[:, dkv:], hkv, head_dim)
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    q = _split_heads(store(column_linear(x[rows], wqkv[:dq, :])), hq, head_dim)
+    o = store(attention(q, k, v, causal=causal, q_pos=rows))
+    return row_linear_partial(o.reshape(len(rows), dq), row_shard(wo, r, R))
+
+
+def layer_unsharded(x, p: dict, head_dim: int, eps: float, act: str = "swiglu",
+                    rows=None):
+    """Pre-norm decoder layer on one sequence, unsharded:
+    ``h = x + attn(rmsnorm(x))``, ``y = h + mlp(rmsnorm(h))``.
+    ``p`` holds g1, wq, wk, wv, wo, g2, wg, wu, wd.  Returns y at ``rows``."""
+    x = np.asarray(x, np.float64)
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    xn = rmsnorm(x, p["g1"], eps)
+    h = x[rows] + attention_block_unsharded(xn, p["wq"], p["wk"], p["wv"], p["wo"],
+                                            head_dim, causal=True, rows=rows)
+    hn = rmsnorm(h, p["g2"], eps)
+    return h + mlp_unsharded(hn, p["wg"], p["wd"], act, w_up=p.get("wu"))
+
+
+def layer_sharded(x, p: dict, head_dim: int, eps: float, R: int, act: str = "swiglu",
+                  rows=None, store=_identity):
+    """The same layer computed the tensor-parallel way: every rank's attention
+    partial, their sum plus the residual, every rank's MLP partial on the
+    normalised sum, their sum plus the residual (two all-reduces per layer:
+    P2 section 2.1 table; P3 "两张卡如何共同算出一层").  Returns
+    ``(y, h, attn_partials, mlp_partials)`` at ``rows``."""
+    x = np.asarray(x, np.float64)
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    xn = store(rmsnorm(x, p["g1"], eps))
+    pa = [attention_rank_partial(xn, p["wq"], p["wk"], p["wv"], p["wo"], head_dim,
+                                 r, R, causal=True, rows=rows, store=store)
+          for r in range(R)]
+    h = store(reduce_partials(pa, residual=x[rows]))
+    hn = store(rmsnorm(h, p["g2"], eps))
+    pm = [mlp_rank_partial(hn, p["wg"], p["wd"], act, r, R, w_up=p.get("wu"),
+                           store=store) for r in range(R)]
+    y = reduce_partials(pm, residual=h)
+    return y, h, pa, pm

@@ -1,0 +1,478 @@
+"""Pins for the CPU oracle: values the pages print, closed forms, invariants of
+the method and brute force on tiny inputs.  CPU only (no GPU, no HIP library).
+
+Sources:
+  P1 "Tensor Parallel：当一张 GPU 放不下一个大模型" (mini vLLM series)
+  P2 "张量并行（Tensor Parallelism）推理部署实战：从 Megatron-LM 切分原理到 vLLM 多卡配置与性能调优"
+  P3 "Tensor Parallel 深入解析：多加 GPU，推理为什么可能更慢"
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.tp_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _worked():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Worked example (P3 "两张卡如何共同算出一层")
+# ---------------------------------------------------------------------------
+
+def check_worked_example():
+    g = _worked()
+    X = np.array(g["X"], np.float64)
+    w = np.array(g["W"], np.float64).T          # stored [out, in]
+    v = np.array(g["V"], np.float64).T
+    assert np.array_equal(O.linear(X, w), np.array(g["Y_full"]))
+    shards = [O.column_linear(X, O.column_shard(w, r, 2)) for r in range(2)]
+    for r in range(2):
+        assert np.array_equal(shards[r], np.array(g["Y_col_shards"][r]))
+    parts = [O.row_linear_partial(shards[r], O.row_shard(v, r, 2)) for r in range(2)]
+    for r in range(2):
+        assert np.array_equal(parts[r], np.array(g["row_partials"][r]))
+    assert np.array_equal(O.reduce_partials(parts), np.array(g["Y_sum"]))
+    assert np.array_equal(O.concat_columns(shards), np.array(g["Y_full"]))
+
+
+def test_worked_example():
+    check_worked_example()
+
+
+# ---------------------------------------------------------------------------
+# Matmul core against pure-Python loops
+# ---------------------------------------------------------------------------
+
+def _loop_matmul(x, w):
+    M, K = len(x), len(x[0])
+    N = len(w)
+    out = [[0.0] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            s = 0.0
+            for k in range(K):
+                s += x[i][k] * w[j][k]
+            out[i][j] = s
+    return np.array(out)
+
+
+def check_linear_bruteforce():
+    rng = np.random.default_rng(7)
+    for (M, K, N) in [(1, 2, 4), (2, 3, 5), (5, 17, 3), (3, 64, 17)]:
+        x = rng.integers(-3, 4, (M, K)).astype(np.float64)
+        w = rng.integers(-3, 4, (N, K)).astype(np.float64)
+        assert np.array_equal(O.linear(x, w), _loop_matmul(x.tolist(), w.tolist()))
+        # non-square, non-symmetric case catches a transposed operand
+        assert O.linear(x, w).shape == (M, N)
+
+
+def test_linear_bruteforce():
+    check_linear_bruteforce()
+
+
+# ---------------------------------------------------------------------------
+# Sharding invariants (P1 "如何验证 tensor parallel 正确": concat of column
+# shards equals the full linear, the sum of row partials equals the full linear)
+# ---------------------------------------------------------------------------
+
+def check_sharding_invariants():
+    rng = np.random.default_rng(11)
+    M, K, N = 5, 64, 48
+    x = rng.integers(-3, 4, (M, K)).astype(np.float64)
+    w = rng.integers(-3, 4, (N, K)).astype(np.float64)
+    full = _loop_matmul(x.tolist(), w.tolist())
+    for R in (1, 2, 4, 8):
+        cols = [O.column_linear(x, O.column_shard(w, r, R)) for r in range(R)]
+        assert np.array_equal(O.concat_columns(cols), full)
+        parts = [O.row_linear_partial(O.input_shard(x, r, R), O.row_shard(w, r, R))
+                 for r in range(R)]
+        assert np.array_equal(O.reduce_partials(parts), full)
+
+
+def test_sharding_invariants():
+    check_sharding_invariants()
+
+
+def test_indivisible_shards_rejected():
+    w = np.zeros((6, 4))
+    with pytest.raises(ValueError):
+        O.column_shard(w, 0, 4)
+    with pytest.raises(ValueError):
+        O.row_shard(w, 0, 3)
+    with pytest.raises(ValueError):
+        O.qkv_shard(np.zeros((8 * 2, 4)), np.zeros((3 * 2, 4)), np.zeros((3 * 2, 4)), 0, 2, 2)
+
+
+def check_toy_mlp_bitexact():
+    """Config toy_mlp_int shapes: X[4,64], W1 64->256 column split, W2 256->64
+    row split, no activation; integer values in {-3..3}, so every partial sum
+    is an integer below 2**24 and the result is exact in any order."""
+    rng = np.random.default_rng(101)
+    x = rng.integers(-3, 4, (4, 64)).astype(np.float64)
+    w1 = rng.integers(-3, 4, (256, 64)).astype(np.float64)
+    w2 = rng.integers(-3, 4, (64, 256)).astype(np.float64)
+    full = _loop_matmul(_loop_matmul(x.tolist(), w1.tolist()).tolist(), w2.tolist())
+    assert np.array_equal(O.mlp_unsharded(x, w1, w2, "none"), full)
+    parts = [O.mlp_rank_partial(x, w1, w2, "none", r, 2) for r in range(2)]
+    assert np.array_equal(O.reduce_partials(parts), full)
+    assert np.max(np.abs(full)) < 2 ** 24
+
+
+def test_toy_mlp_bitexact():
+    check_toy_mlp_bitexact()
+
+
+def test_reduce_order_and_residual():
+    p = [np.array([[1.0, 2.0]]), np.array([[10.0, 20.0]]), np.array([[100.0, 200.0]])]
+    assert np.array_equal(O.reduce_partials(p), [[111.0, 222.0]])
+    assert np.array_equal(O.reduce_partials(p, residual=np.array([[0.5, -0.5]])),
+                          [[111.5, 221.5]])
+    # rank order: (1e16 + 1) - 1e16 is 0 in double, 1e16 - 1e16 + 1 is 1
+    q = [np.array([1e16]), np.array([1.0]), np.array([-1e16])]
+    assert O.reduce_partials(q)[0] == 0.0
+    q2 = [np.array([1e16]), np.array([-1e16]), np.array([1.0])]
+    assert O.reduce_partials(q2)[0] == 1.0
+
+
+# ---------------------------------------------------------------------------
+# Activations: textbook values and symmetries
+# ---------------------------------------------------------------------------
+
+PHI_1 = 0.8413447460685429     # standard normal CDF at 1 (textbook table)
+PHI_2 = 0.9772498680518208     # standard normal CDF at 2
+
+
+def check_activations():
+    assert O.silu(0.0) == 0.0 and O.gelu(0.0) == 0.0
+    # sigmoid(ln 3) = 3/4 exactly
+    assert math.isclose(float(O.silu(math.log(3.0))), 0.75 * math.log(3.0), rel_tol=1e-15)
+    assert math.isclose(float(O.gelu(1.0)), PHI_1, rel_tol=1e-15)
+    assert math.isclose(float(O.gelu(2.0)), 2 * PHI_2, rel_tol=1e-15)
+    assert math.isclose(float(O.gelu(-1.0)), -(1 - PHI_1), rel_tol=1e-14)
+    x = np.linspace(-6, 6, 101)
+    # f(x) - f(-x) = x for both (sigma(x)+sigma(-x)=1, Phi(x)+Phi(-x)=1)
+    assert np.allclose(O.silu(x) - O.silu(-x), x, atol=1e-14)
+    assert np.allclose(O.gelu(x) - O.gelu(-x), x, atol=1e-14)
+    assert abs(float(O.gelu(40.0)) - 40.0) < 1e-12 and abs(float(O.silu(60.0)) - 60.0) < 1e-12
+    g = np.array([1.0, -2.0]); u = np.array([3.0, 5.0])
+    assert np.allclose(O.local_activation(g, u, "swiglu"), O.silu(g) * u)
+    assert np.array_equal(O.local_activation(g, None, "none"), g)
+
+
+def test_activations():
+    check_activations()
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm: closed forms (not on the pages; these pins are all it has)
+# ---------------------------------------------------------------------------
+
+def check_rmsnorm():
+    y = O.rmsnorm(np.array([[3.0, 4.0]]), np.ones(2), eps=0.0)
+    assert np.allclose(y, np.array([[3.0, 4.0]]) / math.sqrt(12.5), rtol=1e-15)
+    c = -2.5
+    y = O.rmsnorm(np.full((1, 8), c), np.full(8, 1.5), eps=1e-5)
+    assert np.allclose(y, 1.5 * c / math.sqrt(c * c + 1e-5), rtol=1e-15)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 32))
+    y = O.rmsnorm(x, np.ones(32), eps=0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-14)
+    assert np.allclose(O.rmsnorm(7.0 * x, np.ones(32), 0.0), y, rtol=1e-14)
+    gamma = rng.standard_normal(32)
+    assert np.allclose(O.rmsnorm(x, gamma, 0.0), y * gamma, rtol=1e-14)
+
+
+def test_rmsnorm():
+    check_rmsnorm()
+
+
+# ---------------------------------------------------------------------------
+# Attention: closed forms and brute force
+# ---------------------------------------------------------------------------
+
+def _loop_attention(q, k, v, causal):
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    out = np.zeros_like(q)
+    for b in range(B):
+        for s in range(Sq):
+            pos = s + Skv - Sq
+            for h in range(Hq):
+                hk = h // G
+                sc = []
+                for t in range(Skv):
+                    if causal and t > pos:
+                        continue
+                    sc.append((t, sum(q[b, s, h, d] * k[b, t, hk, d] for d in range(D)) / math.sqrt(D)))
+                mx = max(val for _, val in sc)
+                ws = [(t, math.exp(val - mx)) for t, val in sc]
+                tot = sum(wv for _, wv in ws)
+                for d in range(D):
+                    out[b, s, h, d] = sum(wv * v[b, t, hk, d] for t, wv in ws) / tot
+    return out
+
+
+def check_attention():
+    rng = np.random.default_rng(5)
+    # one key -> output is that key's value
+    q = rng.standard_normal((2, 1, 4, 8)); k = rng.standard_normal((2, 1, 2, 8))
+    v = rng.standard_normal((2, 1, 2, 8))
+    o = O.attention(q, k, v, causal=False)
+    for h in range(4):
+        assert np.allclose(o[:, 0, h], v[:, 0, h // 2], rtol=1e-15)
+    # zero query -> uniform weights -> mean of visible values
+    q = np.zeros((1, 5, 2, 4)); k = rng.standard_normal((1, 5, 1, 4))
+    v = rng.standard_normal((1, 5, 1, 4))
+    o = O.attention(q, k, v, causal=True)
+    for s in range(5):
+        assert np.allclose(o[0, s, 0], v[0, :s + 1, 0].mean(axis=0), rtol=1e-13)
+        assert np.allclose(o[0, s, 1], v[0, :s + 1, 0].mean(axis=0), rtol=1e-13)
+    # first causal row sees only key 0
+    q = rng.standard_normal((1, 6, 2, 4)); k = rng.standard_normal((1, 6, 2, 4))
+    v = rng.standard_normal((1, 6, 2, 4))
+    o = O.attention(q, k, v, causal=True)
+    assert np.array_equal(o[0, 0], v[0, 0])
+    # two keys, scale 1/sqrt(D): D=4, q=(a,0,0,0), k0=0, k1=(1,0,0,0): p1 = sigmoid(a/2);
+    # a = 2 ln 3 gives p1 = 3/4 exactly
+    a = 2 * math.log(3.0)
+    q = np.zeros((1, 1, 1, 4)); q[0, 0, 0, 0] = a
+    k = np.zeros((1, 2, 1, 4)); k[0, 1, 0, 0] = 1.0
+    v = np.zeros((1, 2, 1, 4)); v[0, 1, 0, :] = 1.0
+    o = O.attention(q, k, v, causal=False)
+    assert np.allclose(o[0, 0, 0], 0.75, rtol=1e-14)
+    # GQA map: constant value c_j per KV head j, query head h must return c_{h // G}
+    Hq, Hkv = 8, 2
+    q = rng.standard_normal((1, 3, Hq, 4)); k = rng.standard_normal((1, 7, Hkv, 4))
+    v = np.zeros((1, 7, Hkv, 4))
+    for j in range(Hkv):
+        v[:, :, j, :] = 10.0 * (j + 1)
+    o = O.attention(q, k, v, causal=True)
+    for h in range(Hq):
+        assert np.allclose(o[0, :, h, :], 10.0 * (h // (Hq // Hkv) + 1), rtol=1e-14)
+    # weights sum to one: all-ones values give all-ones output
+    o = O.attention(q, k, np.ones_like(v), causal=False)
+    assert np.allclose(o, 1.0, rtol=1e-14)
+    # a dominant key takes all the weight
+    k = rng.standard_normal((1, 4, 1, 4)); v = rng.standard_normal((1, 4, 1, 4))
+    q = 500.0 * k[:, 2:3] / np.linalg.norm(k[0, 2, 0])
+    o = O.attention(q, k, v, causal=False)
+    assert np.allclose(o[0, 0, 0], v[0, 2, 0], atol=1e-6)
+    # brute force on tiny shapes, MHA and GQA, causal and not, Sq < Skv
+    for (B, Sq, Skv, Hq, Hkv, D) in [(1, 3, 3, 2, 2, 4), (2, 2, 5, 4, 2, 3), (1, 4, 4, 6, 3, 5)]:
+        q = rng.standard_normal((B, Sq, Hq, D)); k = rng.standard_normal((B, Skv, Hkv, D))
+        v = rng.standard_normal((B, Skv, Hkv, D))
+        for causal in (False, True):
+            assert np.allclose(O.attention(q, k, v, causal), _loop_attention(q, k, v, causal),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_attention():
+    check_attention()
+
+
+def test_attention_rows_subset():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((1, 9, 4, 8)); k = rng.standard_normal((1, 9, 2, 8))
+    v = rng.standard_normal((1, 9, 2, 8))
+    full = O.attention(q, k, v, causal=True)
+    rows = np.array([0, 4, 8])
+    sub = O.attention(q[:, rows], k, v, causal=True, q_pos=rows)
+    assert np.allclose(sub, full[:, rows], rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Whole layer: sharded == unsharded (P1 "如何验证 tensor parallel 正确": TP=1
+# and TP=N must agree; layered check column -> row -> attention -> MLP -> full)
+# ---------------------------------------------------------------------------
+
+def _small_layer(rng, H=32, n_q=8, n_kv=4, D=8, I=64):
+    return {
+        "g1": 1.0 + 0.1 * rng.standard_normal(H), "g2": 1.0 + 0.1 * rng.standard_normal(H),
+        "wq": 0.2 * rng.standard_normal((n_q * D, H)), "wk": 0.2 * rng.standard_normal((n_kv * D, H)),
+        "wv": 0.2 * rng.standard_normal((n_kv * D, H)), "wo": 0.2 * rng.standard_normal((H, n_q * D)),
+        "wg": 0.2 * rng.standard_normal((I, H)), "wu": 0.2 * rng.standard_normal((I, H)),
+        "wd": 0.2 * rng.standard_normal((H, I)),
+    }
+
+
+def check_layer_sharded_equals_unsharded():
+    rng = np.random.default_rng(21)
+    p = _small_layer(rng)
+    x = rng.standard_normal((10, 32))
+    ref = O.layer_unsharded(x, p, 8, 1e-5)
+    for R in (1, 2, 4):
+        y, h, pa, pm = O.layer_sharded(x, p, 8, 1e-5, R)
+        assert len(pa) == R and len(pm) == R
+        assert np.allclose(y, ref, rtol=1e-11, atol=1e-11)
+    rows = np.array([0, 3, 9])
+    assert np.allclose(O.layer_unsharded(x, p, 8, 1e-5, rows=rows), ref[rows], rtol=1e-12)
+    y, *_ = O.layer_sharded(x, p, 8, 1e-5, 2, rows=rows)
+    assert np.allclose(y, ref[rows], rtol=1e-11, atol=1e-11)
+    # the layer is not trivially the residual
+    assert np.max(np.abs(ref - x)) > 0.1
+
+
+def test_layer_sharded_equals_unsharded():
+    check_layer_sharded_equals_unsharded()
+
+
+def test_gelu_mlp_sharded_equals_unsharded():
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((6, 16)); a = rng.standard_normal((64, 16)); b = rng.standard_normal((16, 64))
+    ref = O.mlp_unsharded(x, a, b, "gelu")
+    for R in (1, 2, 4, 8):
+        y = O.reduce_partials([O.mlp_rank_partial(x, a, b, "gelu", r, R) for r in range(R)])
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_attention_block_matches_bruteforce():
+    """The attention block wiring (QKV split, GQA, o_proj) against loops."""
+    rng = np.random.default_rng(29)
+    p = _small_layer(rng, H=8, n_q=4, n_kv=2, D=2, I=8)
+    x = rng.standard_normal((4, 8))
+    q = (x @ p["wq"].T).reshape(1, 4, 4, 2)
+    k = (x @ p["wk"].T).reshape(1, 4, 2, 2)
+    v = (x @ p["wv"].T).reshape(1, 4, 2, 2)
+    o = _loop_attention(q, k, v, causal=True).reshape(4, 8)
+    ref = _loop_matmul(o.tolist(), p["wo"].tolist())
+    assert np.allclose(O.attention_block_unsharded(x, p["wq"], p["wk"], p["wv"], p["wo"], 2), ref,
+                       rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding used by the storage-faithful mode
+# ---------------------------------------------------------------------------
+
+def test_round_bf16():
+    assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0                      # tie -> even
+    assert O.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6      # tie -> even (up)
+    assert O.round_bf16(1.0 + 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7
+    assert O.round_bf16(-3.0) == -3.0 and O.round_bf16(0.0) == 0.0
+    rng = np.random.default_rng(0)
+    a = rng.standard_normal(100000).astype(np.float32)
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_bf16(a.astype(np.float64)), ref)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each plausible slip in the oracle must trip a pin above
+# ---------------------------------------------------------------------------
+
+def _mut_linear_transposed(x, w):
+    x = np.asarray(x, np.float64); w = np.asarray(w, np.float64)
+    return x @ w.reshape(w.shape[1], w.shape[0])
+
+
+def _mut_row_shard_wrong_axis(w, r, R):
+    w = np.asarray(w)
+    b = w.shape[0] // R
+    return w[r * b:(r + 1) * b, :]
+
+
+def _mut_reduce_drops_residual(partials, residual=None):
+    acc = np.zeros_like(np.asarray(partials[0], np.float64))
+    for p in partials:
+        acc = acc + p
+    return acc
+
+
+def _mut_reduce_skips_last(partials, residual=None):
+    acc = np.zeros_like(np.asarray(partials[0], np.float64))
+    for p in partials[:-1]:
+        acc = acc + p
+    return acc if residual is None else acc + residual
+
+
+def _mut_gelu_sign(g):
+    g = np.asarray(g, np.float64)
+    from scipy.special import erf
+    return 0.5 * g * (1.0 - erf(g / math.sqrt(2.0)))
+
+
+def _mut_silu(g):
+    g = np.asarray(g, np.float64)
+    return g / (1.0 + np.exp(g))
+
+
+def _mut_rmsnorm_sum(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * gamma
+
+
+def _mut_rmsnorm_no_gamma(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+_orig_attention = O.attention
+
+
+def _mut_attention_gqa_modulo(q, k, v, causal, scale=None, q_pos=None):
+    # q head h reads KV head h % Hkv instead of h // G
+    Hq, Hkv = q.shape[2], k.shape[2]
+    perm = [h % Hkv for h in range(Hq)]
+    G = Hq // Hkv
+    kk = np.stack([k[:, :, perm[h], :] for h in range(Hq)], axis=2)
+    vv = np.stack([v[:, :, perm[h], :] for h in range(Hq)], axis=2)
+    return _orig_attention(q, kk, vv, causal, scale, q_pos)
+
+
+def _mut_attention_no_scale(q, k, v, causal, scale=None, q_pos=None):
+    return _orig_attention(q, k, v, causal, 1.0, q_pos)
+
+
+def _mut_attention_mask_off_by_one(q, k, v, causal, scale=None, q_pos=None):
+    Sq, Skv = q.shape[1], k.shape[1]
+    if q_pos is None:
+        q_pos = np.arange(Sq) + (Skv - Sq)
+    return _orig_attention(q, k, v, causal, scale, np.minimum(np.asarray(q_pos) + 1, Skv - 1))
+
+
+_orig_qkv_shard = O.qkv_shard
+
+
+def _mut_qkv_order(wq, wk, wv, r, R, head_dim):
+    return _orig_qkv_shard(wq, wv, wk, r, R, head_dim)
+
+
+MUTATIONS = [
+    ("linear", _mut_linear_transposed),
+    ("row_shard", _mut_row_shard_wrong_axis),
+    ("reduce_partials", _mut_reduce_drops_residual),
+    ("reduce_partials", _mut_reduce_skips_last),
+    ("gelu", _mut_gelu_sign),
+    ("silu", _mut_silu),
+    ("rmsnorm", _mut_rmsnorm_sum),
+    ("rmsnorm", _mut_rmsnorm_no_gamma),
+    ("attention", _mut_attention_gqa_modulo),
+    ("attention", _mut_attention_no_scale),
+    ("attention", _mut_attention_mask_off_by_one),
+    ("qkv_shard", _mut_qkv_order),
+]
+
+ALL_CHECKS = [check_worked_example, check_linear_bruteforce, check_sharding_invariants,
+              check_toy_mlp_bitexact, check_activations, check_rmsnorm, check_attention,
+              check_layer_sharded_equals_unsharded]
+
+
+@pytest.mark.parametrize("name,fn", MUTATIONS, ids=[f"{n}:{f.__name__}" for n, f in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(O, name, fn)
+    caught = False
+    for chk in ALL_CHECKS:
+        try:
+            chk()
+        except (AssertionError, ValueError, IndexError):
+            caught = True
+            break
+    assert caught, f"no pin catches the planted mistake in {name}"
