@@ -1,0 +1,349 @@
+"""Benchmark one tensor-parallel rank's decoder-layer shard on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+A step is one pass of the whole path for rank 0 of a TP=2 prefill layer
+(4096 tokens, hidden 8192, 64 q / 8 KV heads, head_dim 128, intermediate
+28672): RMSNorm, fused QKV column-parallel GEMM, causal local attention,
+o_proj row-parallel partial, sum of both ranks' partials + residual, RMSNorm,
+gate|up column-parallel GEMM, SwiGLU, down row-parallel partial, sum of
+partials + residual.  Rank 1's partials (what the all-reduce would deliver)
+are computed once before timing.  Inputs are seeded synthetic tensors already
+resident in HBM.  Prints ONE JSON line.
+
+Secondary figures (same line, key "decode"): the decode MLP shard at TP=8
+(M = 1, 8, 64) and the decode attention shard at TP=4, timed with 4 rotating
+copies of the weights/caches so that the 256 MB Infinity Cache cannot hold
+the working set between steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import tensor_transformer_layer_05_amd as tpl  # noqa: E402
+from tensor_transformer_layer_05_amd import inputs as I  # noqa: E402
+from tensor_transformer_layer_05_amd.shard import AttnShard, LayerShard, MlpShard  # noqa: E402
+
+METRIC = "TFLOP/s + HBM GB/s per TP-rank layer shard (decode M=1..64, prefill M=4096)"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+DEV = "cuda:0"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# prefill layer shard (rank 0 of TP=2)
+# ---------------------------------------------------------------------------
+
+def prefill_setup():
+    c = I.config("prefill_layer_tp2")
+    H, R, D, S = c.hidden, c.tp, c.head_dim, c.tokens[0]
+    hq, hkv, il = c.n_q // R, c.n_kv // R, c.inter // R
+    seed = c.seed
+    t0 = time.time()
+
+    def rank_weights(r):
+        wq = I.normal(seed, "wq", (hq * D, H), c.w_std, rank=r)
+        wk = I.normal(seed, "wk", (hkv * D, H), c.w_std, rank=r)
+        wv = I.normal(seed, "wv", (hkv * D, H), c.w_std, rank=r)
+        wo = I.normal(seed, "wo", (H, hq * D), c.w_std, rank=r)
+        wg = I.normal(seed, "wg", (il, H), c.w_std, rank=r)
+        wu = I.normal(seed, "wu", (il, H), c.w_std, rank=r)
+        wd = I.normal(seed, "wd", (H, il), c.w_std, rank=r)
+        return dict(wq=wq, wk=wk, wv=wv, wo=wo, wg=wg, wu=wu, wd=wd)
+
+    x = I.normal(seed, "x", (S, H), c.x_std)
+    g1 = torch.ones(H, dtype=torch.bfloat16)
+    g2 = torch.ones(H, dtype=torch.bfloat16)
+    shards, host = [], []
+    for r in range(R):
+        w = rank_weights(r)
+        host.append(w)
+        wqkv = torch.cat([w["wq"].dev, w["wk"].dev, w["wv"].dev], 0).to(DEV)
+        wgu = torch.cat([w["wg"].dev, w["wu"].dev], 0).to(DEV)
+        shards.append(LayerShard(g1.to(DEV), g2.to(DEV), wqkv, w["wo"].dev.to(DEV), wgu,
+                                 w["wd"].dev.to(DEV), hq, hkv, D, c.eps, S))
+    log(f"prefill inputs generated in {time.time() - t0:.1f}s")
+    X = x.dev.to(DEV)
+    pa = [torch.empty((S, H), dtype=torch.float32, device=DEV) for _ in range(R)]
+    pm = [torch.empty((S, H), dtype=torch.float32, device=DEV) for _ in range(R)]
+    # every rank's partials once (rank 1's stay as the all-reduce contribution)
+    for r in range(R):
+        shards[r].attn_partial(X, pa[r])
+    h = tpl.reduce_partials(pa, residual=X)
+    for r in range(R):
+        shards[r].mlp_partial(h, pm[r])
+    y = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
+    torch.cuda.synchronize()
+    return dict(c=c, x=x, X=X, shards=shards, host=host, pa=pa, pm=pm, y=y, g1=g1, g2=g2)
+
+
+def prefill_counts(c):
+    H, R, D, S = c.hidden, c.tp, c.head_dim, c.tokens[0]
+    hq, hkv, il = c.n_q // R, c.n_kv // R, c.inter // R
+    nqkv = (hq + 2 * hkv) * D
+    gemm = {  # name: (M, K, N)
+        "qkv": (S, H, nqkv), "o_proj": (S, hq * D, H), "gate_up": (S, H, 2 * il), "down": (S, il, H)}
+    flops = {k: 2.0 * m * kk * n for k, (m, kk, n) in gemm.items()}
+    flops["attention"] = 4.0 * D * (S * (S + 1) / 2) * hq
+    # algorithmic HBM bytes per kernel: each operand read once, each result written once
+    b2, b4 = 2, 4
+    byts = {
+        "rmsnorm1": S * H * b2 * 2 + H * b2,
+        "qkv": (S * H + nqkv * H + S * nqkv) * b2,
+        "attention": S * nqkv * b2 + S * hq * D * b2,
+        "o_proj": (S * hq * D + H * hq * D) * b2 + S * H * b4,
+        "reduce1": R * S * H * b4 + 2 * S * H * b2,
+        "rmsnorm2": S * H * b2 * 2 + H * b2,
+        "gate_up": (S * H + 2 * il * H + S * 2 * il) * b2,
+        "swiglu": S * 2 * il * b2 + S * il * b2,
+        "down": (S * il + H * il) * b2 + S * H * b4,
+        "reduce2": R * S * H * b4 + 2 * S * H * b2,
+    }
+    return gemm, flops, byts
+
+
+def prefill_step(st, ev=None):
+    """Rank 0's step; ``ev`` (dict name -> list of (start, end) events) times each call."""
+    sh, X, pa, pm, y = st["shards"][0], st["X"], st["pa"], st["pm"], st["y"]
+    S = X.shape[0]
+
+    def run(name, fn):
+        if ev is None:
+            fn()
+            return
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        ev.setdefault(name, []).append((e0, e1))
+
+    at, ml = sh.attn, sh.mlp
+    xn, h, hn = sh.xn[:S], sh.h[:S], sh.hn[:S]
+    qkv, o = at.qkv[:S], at.o[:S]
+    q, k, v = at._views(qkv, 1, S)
+    gu, a = ml.gu[:S], ml.a[:S]
+    run("rmsnorm1", lambda: tpl.rmsnorm(X, sh.g1, sh.eps, out=xn))
+    run("qkv", lambda: tpl.column_linear(xn, at.wqkv, out=qkv))
+    run("attention", lambda: tpl.local_attention(q, k, v, causal=True,
+                                                 out=o.view(1, S, at.n_q, at.D)))
+    run("o_proj", lambda: tpl.row_linear_partial(o, at.wo, out=pa[0]))
+    run("reduce1", lambda: tpl.reduce_partials(pa, residual=X, out=h))
+    run("rmsnorm2", lambda: tpl.rmsnorm(h, sh.g2, sh.eps, out=hn))
+    run("gate_up", lambda: tpl.column_linear(hn, ml.w_in, out=gu))
+    run("swiglu", lambda: tpl.swiglu_local(gu[:, :ml.I], gu[:, ml.I:], "swiglu", out=a))
+    run("down", lambda: tpl.row_linear_partial(a, ml.w_out, out=pm[0]))
+    run("reduce2", lambda: tpl.reduce_partials(pm, residual=h, out=y))
+
+
+def time_prefill(st, steps, warmup):
+    for _ in range(warmup):
+        prefill_step(st)
+    torch.cuda.synchronize()
+    ev = {}
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        prefill_step(st, ev)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t0.elapsed_time(t1)
+    per = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    return total_ms / steps, per, wall
+
+
+# ---------------------------------------------------------------------------
+# oracle timing on a bounded sample (rank 0's step on a prefix of the sequence)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(st, target_s=15.0):
+    import oracle.tp_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+    except Exception:  # pragma: no cover
+        threadpool_info = lambda: []
+    c = st["c"]
+    w = st["host"][0]
+    H, D, eps = c.hidden, c.head_dim, c.eps
+    x = st["x"].ref
+    g1 = np.ones(H)
+    g2 = np.ones(H)
+    other_a = np.zeros((1, H))
+    other_m = np.zeros((1, H))
+
+    def run(Sp):
+        xs = x[:Sp]
+        xn = O.rmsnorm(xs, g1, eps)
+        pa = O.attention_rank_partial(xn, w["wq"].ref, w["wk"].ref, w["wv"].ref, w["wo"].ref, D, 0, 1)
+        h = O.reduce_partials([pa, np.broadcast_to(other_a, pa.shape)], residual=xs)
+        hn = O.rmsnorm(h, g2, eps)
+        pm = O.mlp_rank_partial(hn, w["wg"].ref, w["wd"].ref, "swiglu", 0, 1, w_up=w["wu"].ref)
+        return O.reduce_partials([pm, np.broadcast_to(other_m, pm.shape)], residual=h)
+
+    def flops(Sp):
+        R, hq = c.tp, c.n_q // c.tp
+        per_tok = 2.0 * ((hq + 2 * c.n_kv // R) * D * H + hq * D * H + 2 * (c.inter // R) * H
+                         + (c.inter // R) * H)
+        return per_tok * Sp + 4.0 * D * (Sp * (Sp + 1) / 2) * hq
+
+    Sp = 32
+    t = time.perf_counter(); run(Sp); dt = time.perf_counter() - t
+    # grow the prefix to about target_s of work (bounded by the full sequence)
+    Sp2 = int(min(c.tokens[0], max(Sp, Sp * target_s / max(dt, 1e-3))))
+    Sp2 = max(32, (Sp2 // 32) * 32)
+    t = time.perf_counter(); run(Sp2); dt = time.perf_counter() - t
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {"value": flops(Sp2) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"rank-0 layer-shard step on the first {Sp2} of 4096 tokens "
+                      f"(float64 numpy oracle, {dt:.1f}s, {os.cpu_count()} host CPUs visible)",
+            "seconds": dt}
+
+
+# ---------------------------------------------------------------------------
+# decode figures (secondary)
+# ---------------------------------------------------------------------------
+
+def _median_ms(fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn(i)
+        e1.record()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ts]))
+
+
+def decode_figures(steps=30, warmup=5, copies=4):
+    out = {}
+    c = I.config("decode_mlp_tp8")
+    H, il = c.hidden, c.inter // c.tp
+    # weights drawn once on the host, replicated on the GPU (copies defeat the MALL)
+    wg = I.normal(c.seed, "wg", (il, H), c.w_std).dev
+    wu = I.normal(c.seed, "wu", (il, H), c.w_std).dev
+    wd = I.normal(c.seed, "wd", (H, il), c.w_std).dev
+    wgu = torch.cat([wg, wu], 0)
+    mlps = [MlpShard(wgu.to(DEV).clone(), wd.to(DEV).clone(), "swiglu", 64) for _ in range(copies)]
+    wbytes = (wgu.numel() + wd.numel()) * 2
+    for M in c.tokens:
+        X = I.normal(c.seed, "x", (M, H)).dev.to(DEV)
+        P = torch.empty((M, H), dtype=torch.float32, device=DEV)
+        ms = _median_ms(lambda i: mlps[i % copies].partial(X, P), steps, warmup)
+        byts = wbytes + M * H * 2 + M * 2 * il * 2 * 2 + M * il * 2 * 2 + M * H * 4
+        fl = 2.0 * M * (H * 2 * il + il * H)
+        out[f"mlp_tp8_M{M}"] = {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
+                                "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS}
+    del mlps
+    c = I.config("decode_attn_tp4")
+    H, R, D, B, L = c.hidden, c.tp, c.head_dim, c.batch, c.kv_len
+    hq, hkv = c.n_q // R, c.n_kv // R
+    x = I.normal(c.seed, "x", (B, H)).dev.to(DEV)
+    wqkv = I.normal(c.seed, "wqkv", ((hq + 2 * hkv) * D, H), c.w_std).dev
+    wo = I.normal(c.seed, "wo", (H, hq * D), c.w_std).dev
+    kc = I.normal(c.seed, "kcache", (B, hkv, L, D)).dev
+    vc = I.normal(c.seed, "vcache", (B, hkv, L, D)).dev
+    sets = []
+    for _ in range(copies):
+        sets.append((AttnShard(wqkv.to(DEV), wo.to(DEV), hq, hkv, D, B),
+                     kc.to(DEV), vc.to(DEV)))
+    P = torch.empty((B, H), dtype=torch.float32, device=DEV)
+
+    def step(i):
+        a, k_, v_ = sets[i % copies]
+        a.decode_partial(x, k_.transpose(1, 2), v_.transpose(1, 2), L - 1, P)
+
+    ms = _median_ms(step, steps, warmup)
+    byts = (wqkv.numel() + wo.numel() + kc.numel() + vc.numel()) * 2 + B * H * 2 + B * H * 4
+    fl = 2.0 * B * H * (hq + 2 * hkv) * D + 4.0 * B * hq * L * D + 2.0 * B * hq * D * H
+    out["attn_tp4_B32_L2048"] = {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
+                                 "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS}
+    return out
+
+
+# ---------------------------------------------------------------------------
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the multi-GPU all-reduce is "
+              "emulated in HBM on one device and runs at N=1.", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 2
+    tpl.lib()
+    st = prefill_setup()
+    gemm, flops, byts = prefill_counts(st["c"])
+    log("timing prefill layer shard")
+    ms, per, wall = time_prefill(st, a.steps, a.warmup)
+    tot_flops = sum(flops.values())
+    tot_bytes = sum(byts.values())
+    m, k, n = gemm["gate_up"]
+    dom_ms = per["gate_up"]
+    dom = {"bound": "mfma", "kernel": "column_linear gate|up (gemm_bf16_mfma)",
+           "achieved": flops["gate_up"] / dom_ms / 1e9, "peak": PEAK_BF16_TFLOPS,
+           "unit": "TFLOP/s", "frac": flops["gate_up"] / dom_ms / 1e9 / PEAK_BF16_TFLOPS,
+           "traffic": None, "flop_per_launch": flops["gate_up"], "avg_launch_ms": dom_ms,
+           "shape_mkn": [m, k, n]}
+    kernels = {}
+    for name, t in per.items():
+        d = {"ms": round(t, 4)}
+        if name in flops:
+            d["TFLOP/s"] = round(flops[name] / t / 1e9, 1)
+        d["GB/s"] = round(byts[name] / t / 1e6, 1)
+        kernels[name] = d
+    res = {
+        "metric": METRIC, "value": round(tot_flops / ms / 1e9, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) activations)",
+        "config": {"workload": "prefill_layer_tp2 (rank 0 of TP=2: 4096 tokens, hidden 8192, "
+                               "32/4 local q/KV heads x 128, local intermediate 14336, SwiGLU, "
+                               "RMSNorm pre-norm, 2-rank partial sums in HBM)",
+                   "tokens": 4096, "hidden": 8192, "tp": 2, "rank": 0},
+        "hbm_gbps": round(tot_bytes / ms / 1e6, 1),
+        "flop_per_step": tot_flops, "bytes_per_step": tot_bytes,
+        "roofline": dom, "kernels": kernels,
+    }
+    if not a.no_decode:
+        log("timing decode shards")
+        res["decode"] = decode_figures()
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(st)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,184 @@
+/*
+ * tplayer.h -- C ABI of the tensor-parallel decoder-layer shard library
+ * (libtplayer.so, HIP kernels for MI355X / gfx950).
+ *
+ * Each entry point computes one step of ONE tensor-parallel rank's share of a
+ * Megatron-style pre-norm decoder layer.  Sources (web pages):
+ *   P1 "Tensor Parallel：当一张 GPU 放不下一个大模型" (mini vLLM series)
+ *   P2 "张量并行（Tensor Parallelism）推理部署实战：从 Megatron-LM 切分原理到
+ *       vLLM 多卡配置与性能调优"
+ *   P3 "Tensor Parallel 深入解析：多加 GPU，推理为什么可能更慢"
+ *
+ * Common rules for every call:
+ *   - Tensor arguments are DEVICE pointers owned by the caller (the library
+ *     never allocates, frees or keeps them).  Matrices are row-major and
+ *     contiguous unless strides are given.  Strides are in elements.
+ *   - Weights use the nn.Linear layout [out_features, in_features]: the
+ *     input dimension is contiguous, i.e. the stored array is W^T of the
+ *     mathematical Y = X W (P2 sections 1.1 / 1.2 sketches; P3 "两张卡如何共同
+ *     算出一层" notes that the stored form may be the transpose).
+ *   - There is no rank argument: a call acts on the shard it is given.  Host
+ *     code slices shards (contiguous blocks in rank order).
+ *   - `stream` is a hipStream_t (NULL: the default stream).  Calls enqueue
+ *     work and return without synchronising.  Arguments are validated on the
+ *     host before anything is enqueued; a non-TP_OK status means nothing was
+ *     launched, except TP_ERR_HIP, which reports a failed launch (see
+ *     tp_last_error()).
+ *   - dtype: TP_BF16 = bfloat16 storage, TP_F32 = float32 storage.
+ *     Accumulation is always float32.  bf16 results are rounded to nearest
+ *     even.
+ *   - Fast vector paths need 16-byte aligned base pointers and row lengths
+ *     that are multiples of 16 bytes; other inputs take a slower element path
+ *     with the same results.
+ */
+#ifndef TPLAYER_H
+#define TPLAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_NULL = 1,         /* a required pointer is NULL                        */
+  TP_ERR_SHAPE = 2,        /* non-positive or inconsistent sizes, Hq % Hkv != 0  */
+  TP_ERR_DTYPE = 3,        /* dtype / activation enum out of range or unsupported */
+  TP_ERR_ALIGN = 4,        /* pointer alignment below the element size          */
+  TP_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required        */
+  TP_ERR_HIP = 6,          /* a HIP runtime call failed (tp_last_error has text) */
+  TP_ERR_UNSUPPORTED = 7   /* valid request outside what the kernels implement  */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+typedef enum { TP_ACT_NONE = 0, TP_ACT_SWIGLU = 1, TP_ACT_GELU = 2 } tp_act;
+
+/*
+ * Column-parallel linear on one rank (P1 "Column Parallel Linear：按输出维度切";
+ * P2 1.1; P3 "两张卡如何共同算出一层").  Every rank holds the full input and a
+ * block of output features; the result is that rank's output slice and needs
+ * no exchange:
+ *     y[m, n] = sum_k x[m, k] * w[n, k]        (Y_r = X W_r)
+ *   x : [M, K]  dtype dt      (the replicated full input)
+ *   w : [N, K]  dtype dt      (the rank's output-feature block, N = N_full / R)
+ *   y : [M, N]  dtype dt
+ * M <= 64 takes the weight-streaming path (decode); larger M the MFMA tile path.
+ */
+tp_status tp_column_linear(const void* x, const void* w, void* y,
+                           int64_t M, int64_t K, int64_t N,
+                           tp_dtype dt, void* stream);
+
+/*
+ * Row-parallel linear on one rank (P1 "Row Parallel Linear：按输入维度切";
+ * P2 1.2).  Input and weight are split along the input dimension; the result
+ * is this rank's float32 PARTIAL of the full output, which must be summed over
+ * ranks (tp_reduce_partials) -- never concatenated:
+ *     partial[m, n] = sum_k x[m, k] * w[n, k]  (Y_r = X_r W_r)
+ *   x       : [M, K]  dtype dt   (the rank's input slice, K = K_full / R)
+ *   w       : [N, K]  dtype dt   (the rank's input-feature block)
+ *   partial : [M, N]  float32
+ */
+tp_status tp_row_linear_partial(const void* x, const void* w, float* partial,
+                                int64_t M, int64_t K, int64_t N,
+                                tp_dtype dt, void* stream);
+
+/*
+ * Rank-local activation on the intermediate slice (P1 "MLP 里的 tensor
+ * parallel": activation(gate_i) * up_i needs no exchange; P2 section 二:
+ * GELU between fc1 and fc2).
+ *     TP_ACT_SWIGLU: h = g * sigmoid(g) * u
+ *     TP_ACT_GELU:   h = 0.5 * g * (1 + erf(g / sqrt(2)))    (u unused)
+ *     TP_ACT_NONE:   h = g                                   (u unused)
+ *   gate : element (m, i) at gate[m * ld + i]   dtype dt
+ *   up   : element (m, i) at up[m * ld + i]     dtype dt (SWIGLU only; else may be NULL)
+ *   h    : [M, I] contiguous                    dtype dt
+ * A fused gate|up projection output [M, 2I] is passed as gate = base,
+ * up = base + I, ld = 2I.
+ */
+tp_status tp_swiglu_local(const void* gate, const void* up, void* h,
+                          int64_t M, int64_t I, int64_t ld,
+                          tp_act act, tp_dtype dt, void* stream);
+
+/*
+ * Attention over the rank's local heads (P1 "Attention 里的 tensor parallel":
+ * each rank attends only over its own heads and keeps their KV; P2 2.1).
+ * Grouped KV heads (P3 "权重变小，不代表所有显存都按比例变小"): local q head h
+ * reads local KV head h / (Hq / Hkv).
+ *     o[b,s,h,:] = softmax_t(scale * q[b,s,h,:] . k[b,t,h/G,:]) v[b,t,h/G,:]
+ * Causal masking is aligned to the end of the key span: query row s sits at
+ * position s + Skv - Sq and sees keys t <= that position.  Decode is Sq = 1.
+ *   q : element (b,s,h,d) at q[b*qs[0] + s*qs[1] + h*qs[2] + d]
+ *   k, v : element (b,t,j,d) at k[b*kvs[0] + t*kvs[1] + j*kvs[2] + d] (same strides)
+ *   o : element (b,s,h,d) at o[b*os[0] + s*os[1] + h*os[2] + d]
+ *   dt must be TP_BF16; D must be 128 (TP_ERR_UNSUPPORTED otherwise).
+ *   workspace: device scratch of at least tp_local_attention_workspace(...)
+ *   bytes (may be NULL when that is 0), owned by the caller, used only during
+ *   the call's execution on `stream`.
+ */
+tp_status tp_local_attention(const void* q, const int64_t qs[3],
+                             const void* k, const void* v, const int64_t kvs[3],
+                             void* o, const int64_t os[3],
+                             int64_t B, int64_t Sq, int64_t Skv,
+                             int64_t Hq, int64_t Hkv, int64_t D,
+                             int causal, float scale, tp_dtype dt,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+size_t tp_local_attention_workspace(int64_t B, int64_t Sq, int64_t Skv,
+                                    int64_t Hq, int64_t Hkv, int64_t D);
+
+/*
+ * Append the current decode token's k and v to the rank's local KV cache at
+ * key position `pos` (P1 "Tensor parallel 对 KV cache 的影响": each rank keeps
+ * the cache of its own heads only).
+ *   k_new, v_new : element (b,j,d) at k_new[b*new_stride + j*D + d]
+ *   k_cache, v_cache : element (b,t,j,d) at k_cache[b*cs[0] + t*cs[1] + j*cs[2] + d]
+ *   dt must be TP_BF16.
+ */
+tp_status tp_kv_append(const void* k_new, const void* v_new, int64_t new_stride,
+                       void* k_cache, void* v_cache, const int64_t cs[3],
+                       int64_t B, int64_t Hkv, int64_t D, int64_t pos,
+                       tp_dtype dt, void* stream);
+
+/*
+ * The arithmetic of the all-reduce after a row-parallel linear (P1 "Row
+ * Parallel Linear": the partial outputs are summed; P2 section 二
+ * all_reduce(output); P3: partials must be summed, not concatenated),
+ * emulated on one GPU as an in-HBM sum of every rank's partial:
+ *     y[m, n] = (residual[m, n] if residual) + sum_{r=0}^{R-1} partials[r][m, n]
+ * summed in float32 in rank order 0..R-1, the residual added last, then
+ * stored as out_dt.
+ *   partials : host array of R device pointers to [M, N] float32 buffers
+ *   residual : [M, N] out_dt or NULL
+ *   y        : [M, N] out_dt (may alias residual)
+ *   1 <= R <= 16
+ */
+tp_status tp_reduce_partials(const float* const* partials, int64_t R,
+                             const void* residual, void* y,
+                             int64_t M, int64_t N, tp_dtype out_dt, void* stream);
+
+/*
+ * Replicated pre-norm RMSNorm (every rank normalises the full hidden row):
+ *     y[m, :] = x[m, :] * rsqrt(mean_n x[m, n]^2 + eps) * gamma[:]
+ * in float32 arithmetic.  x, gamma, y in dtype dt; x, y are [M, N].
+ * Not on the source pages (a standard pre-norm layer's normalisation).
+ */
+tp_status tp_rmsnorm(const void* x, const void* gamma, void* y,
+                     int64_t M, int64_t N, float eps, tp_dtype dt, void* stream);
+
+/* Static text for a status code. */
+const char* tp_status_string(tp_status s);
+
+/* Text of the last TP_ERR_HIP failure on the calling thread ("" if none). */
+const char* tp_last_error(void);
+
+/* Library version string. */
+const char* tp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPLAYER_H */

@@ -1,0 +1,316 @@
+"""Python binding of libtplayer: one tensor-parallel rank's share of a
+Megatron-style decoder layer on MI355X (gfx950) HIP kernels.
+
+This module only marshals arguments: it checks devices/dtypes/contiguity,
+allocates outputs with torch (device memory plumbing) and calls the C ABI
+declared in ``include/tplayer.h`` on torch's current HIP stream.  Every step of
+the computation runs in the library's kernels; there is no CPU or torch
+fallback -- if the library is missing the calls raise.
+
+Entry points (same names as the C ABI, without the ``tp_`` prefix):
+``column_linear``, ``row_linear_partial``, ``swiglu_local``,
+``local_attention``, ``kv_append``, ``reduce_partials``, ``rmsnorm``.
+Weights use the nn.Linear layout ``[out_features, in_features]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "lib", "library_path", "TPError",
+    "column_linear", "row_linear_partial", "swiglu_local", "local_attention",
+    "local_attention_workspace", "kv_append", "reduce_partials", "rmsnorm",
+    "shard_column", "shard_row", "shard_qkv",
+    "F32", "BF16", "ACT_NONE", "ACT_SWIGLU", "ACT_GELU",
+]
+
+F32, BF16 = 0, 1
+ACT_NONE, ACT_SWIGLU, ACT_GELU = 0, 1, 2
+_ACTS = {"none": ACT_NONE, "swiglu": ACT_SWIGLU, "gelu": ACT_GELU}
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libtplayer.so")
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+_SIGS = {
+    "tp_column_linear": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp]),
+    "tp_row_linear_partial": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp]),
+    "tp_swiglu_local": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]),
+    "tp_local_attention": (ctypes.c_int, [_vp, _i64p, _vp, _vp, _i64p, _vp, _i64p, _i64, _i64, _i64,
+                                          _i64, _i64, _i64, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                          _vp, ctypes.c_size_t, _vp]),
+    "tp_local_attention_workspace": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64, _i64]),
+    "tp_kv_append": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64p, _i64, _i64, _i64, _i64,
+                                    ctypes.c_int, _vp]),
+    "tp_reduce_partials": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, _vp, _vp, _i64, _i64,
+                                          ctypes.c_int, _vp]),
+    "tp_rmsnorm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, ctypes.c_float, ctypes.c_int, _vp]),
+    "tp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tp_last_error": (ctypes.c_char_p, []),
+    "tp_version": (ctypes.c_char_p, []),
+}
+
+EXPORTED = tuple(_SIGS)
+
+
+class TPError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        l = lib()
+        msg = l.tp_status_string(status).decode()
+        if status == 6:
+            msg += ": " + l.tp_last_error().decode()
+        super().__init__(f"{fn} failed with status {status} ({msg})")
+        self.status = status
+
+
+def lib():
+    """Load (once) and return the ctypes handle of libtplayer.so."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "(there is no fallback path)")
+        l = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise TPError(fn, status)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in _DT:
+        raise ValueError(f"{name}: unsupported dtype {t.dtype}")
+    return t
+
+
+def _contig(t: torch.Tensor, name: str):
+    _dev(t, name)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _arr3(strides):
+    return (ctypes.c_int64 * 3)(*[int(s) for s in strides])
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def column_linear(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None):
+    """Rank's output slice ``y = x @ w.T`` (x ``[M,K]``, w ``[N,K]``)."""
+    _contig(x, "x"); _contig(w, "w")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or w.dtype != x.dtype:
+        raise ValueError("w must be [N, K] with the dtype of x")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _contig(out, "out")
+    _check("tp_column_linear", lib().tp_column_linear(x.data_ptr(), w.data_ptr(), out.data_ptr(),
+                                                      M, K, N, _DT[x.dtype], _stream(x)))
+    return out
+
+
+def row_linear_partial(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None):
+    """Rank's float32 partial ``p = x_r @ w_r.T`` (x ``[M,K_r]``, w ``[N,K_r]``)."""
+    _contig(x, "x"); _contig(w, "w")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or w.dtype != x.dtype:
+        raise ValueError("w must be [N, K] with the dtype of x")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _contig(out, "out")
+    if out.dtype != torch.float32:
+        raise ValueError("partials are float32")
+    _check("tp_row_linear_partial", lib().tp_row_linear_partial(
+        x.data_ptr(), w.data_ptr(), out.data_ptr(), M, K, N, _DT[x.dtype], _stream(x)))
+    return out
+
+
+def swiglu_local(gate: torch.Tensor, up: torch.Tensor | None = None, act: str = "swiglu",
+                 out: torch.Tensor | None = None):
+    """Rank-local activation.  ``gate``/``up`` are ``[M, I]`` views that may
+    share a row stride (e.g. the two halves of a fused gate|up output)."""
+    _dev(gate, "gate")
+    if gate.dim() != 2 or gate.stride(1) != 1:
+        raise ValueError("gate must be a 2-D row-major view")
+    M, I = gate.shape
+    ld = gate.stride(0)
+    a = _act(act)
+    if a == ACT_SWIGLU:
+        if up is None:
+            raise ValueError("swiglu needs up")
+        _dev(up, "up")
+        if up.shape != gate.shape or up.stride() != gate.stride() or up.dtype != gate.dtype:
+            raise ValueError("up must match gate's shape, strides and dtype")
+    if out is None:
+        out = torch.empty((M, I), dtype=gate.dtype, device=gate.device)
+    _contig(out, "out")
+    _check("tp_swiglu_local", lib().tp_swiglu_local(
+        gate.data_ptr(), up.data_ptr() if (up is not None and a == ACT_SWIGLU) else None,
+        out.data_ptr(), M, I, ld, a, _DT[gate.dtype], _stream(gate)))
+    return out
+
+
+def _act(act):
+    if isinstance(act, int):
+        return act
+    return _ACTS[act]
+
+
+def local_attention_workspace(B, Sq, Skv, Hq, Hkv, D) -> int:
+    return int(lib().tp_local_attention_workspace(B, Sq, Skv, Hq, Hkv, D))
+
+
+def local_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+                    scale: float | None = None, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None):
+    """Attention over local heads.  q ``[B,Sq,Hq,D]``, k/v ``[B,Skv,Hkv,D]``
+    (any strides with a contiguous last dim; k and v share strides).
+    Returns o ``[B,Sq,Hq,D]`` (or writes the given ``out`` view)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{n} must be 4-D with a contiguous last dimension")
+    if k.stride() != v.stride() or k.shape != v.shape:
+        raise ValueError("k and v must have the same shape and strides")
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=q.dtype, device=q.device)
+    if out.dim() != 4 or out.stride(3) != 1:
+        raise ValueError("out must be 4-D with a contiguous last dimension")
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    need = local_attention_workspace(B, Sq, Skv, Hq, Hkv, D)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    qs = _arr3([q.stride(0), q.stride(1), q.stride(2)])
+    kvs = _arr3([k.stride(0), k.stride(1), k.stride(2)])
+    os_ = _arr3([out.stride(0), out.stride(1), out.stride(2)])
+    _check("tp_local_attention", lib().tp_local_attention(
+        q.data_ptr(), qs, k.data_ptr(), v.data_ptr(), kvs, out.data_ptr(), os_,
+        B, Sq, Skv, Hq, Hkv, D, int(bool(causal)), float(scale), _DT[q.dtype],
+        workspace.data_ptr() if need else None, need, _stream(q)))
+    return out
+
+
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+              v_cache: torch.Tensor, pos: int):
+    """Write the current token's k/v (``[B, Hkv, D]`` views with a shared row
+    stride) into the caches ``[B, T, Hkv, D]`` (any strides, last dim
+    contiguous) at key position ``pos``."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    B, H, D = k_new.shape
+    if k_new.stride(2) != 1 or k_new.stride(1) != D or v_new.stride() != k_new.stride():
+        raise ValueError("k_new/v_new must be [B, Hkv, D] rows of one stride")
+    if k_cache.stride() != v_cache.stride() or k_cache.stride(3) != 1:
+        raise ValueError("caches must share strides with a contiguous last dim")
+    if not (0 <= pos < k_cache.shape[1]):
+        raise ValueError("pos outside the cache")
+    cs = _arr3([k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)])
+    _check("tp_kv_append", lib().tp_kv_append(
+        k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_cache.data_ptr(), v_cache.data_ptr(),
+        cs, B, H, D, pos, _DT[k_new.dtype], _stream(k_new)))
+
+
+def reduce_partials(partials, residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    out_dtype: torch.dtype | None = None):
+    """``y = residual + sum_r partials[r]`` in rank order (float32 sums)."""
+    parts = list(partials)
+    if not parts:
+        raise ValueError("need at least one partial")
+    for i, p in enumerate(parts):
+        _contig(p, f"partials[{i}]")
+        if p.dtype != torch.float32 or p.shape != parts[0].shape:
+            raise ValueError("partials must be float32 tensors of one shape")
+    M, N = parts[0].shape
+    if out is None:
+        dt = out_dtype or (residual.dtype if residual is not None else torch.float32)
+        out = torch.empty((M, N), dtype=dt, device=parts[0].device)
+    _contig(out, "out")
+    if residual is not None:
+        _contig(residual, "residual")
+        if residual.dtype != out.dtype or residual.shape != out.shape:
+            raise ValueError("residual must match out")
+    arr = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    _check("tp_reduce_partials", lib().tp_reduce_partials(
+        arr, len(parts), residual.data_ptr() if residual is not None else None, out.data_ptr(),
+        M, N, _DT[out.dtype], _stream(parts[0])))
+    return out
+
+
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, out: torch.Tensor | None = None):
+    _contig(x, "x"); _contig(gamma, "gamma")
+    M, N = x.shape
+    if gamma.shape != (N,) or gamma.dtype != x.dtype:
+        raise ValueError("gamma must be [N] with the dtype of x")
+    if out is None:
+        out = torch.empty_like(x)
+    _contig(out, "out")
+    _check("tp_rmsnorm", lib().tp_rmsnorm(x.data_ptr(), gamma.data_ptr(), out.data_ptr(), M, N,
+                                          float(eps), _DT[x.dtype], _stream(x)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# host-side shard slicing (contiguous blocks in rank order)
+# ---------------------------------------------------------------------------
+
+def _block(n: int, r: int, R: int):
+    if R <= 0 or not (0 <= r < R):
+        raise ValueError(f"rank {r} out of range for TP size {R}")
+    if n % R:
+        raise ValueError(f"dimension {n} is not divisible by TP size {R}")
+    b = n // R
+    return r * b, b
+
+
+def shard_column(w: torch.Tensor, r: int, R: int) -> torch.Tensor:
+    """Rank r's output-feature block (rows) of an ``[N, K]`` weight."""
+    s, b = _block(w.shape[0], r, R)
+    return w.narrow(0, s, b).contiguous()
+
+
+def shard_row(w: torch.Tensor, r: int, R: int) -> torch.Tensor:
+    """Rank r's input-feature block (columns) of an ``[N, K]`` weight."""
+    s, b = _block(w.shape[1], r, R)
+    return w.narrow(1, s, b).contiguous()
+
+
+def shard_qkv(wq: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor, r: int, R: int,
+              head_dim: int) -> torch.Tensor:
+    """Rank r's fused ``[q heads | k heads | v heads]`` weight."""
+    for t in (wq, wk, wv):
+        if t.shape[0] % head_dim:
+            raise ValueError("projection rows must be whole heads")
+    if (wq.shape[0] // head_dim) % R or (wk.shape[0] // head_dim) % R:
+        raise ValueError("q and KV heads must divide by the TP size")
+    return torch.cat([shard_column(wq, r, R), shard_column(wk, r, R), shard_column(wv, r, R)], 0)

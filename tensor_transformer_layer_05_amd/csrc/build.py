@@ -1,0 +1,88 @@
+"""Build libtplayer.so (HIP kernels + C ABI) for gfx950, in-tree.
+
+    python -m tensor_transformer_layer_05_amd.csrc.build [--force] [--jobs N]
+
+Each .hip source is compiled to an object with hipcc, then all objects are
+linked into ``tensor_transformer_layer_05_amd/libtplayer.so``.  Objects live in
+``_build/`` next to this file.  ``build(force=True)`` always recompiles.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.dirname(HERE)
+ROOT = os.path.dirname(PKG)
+OUT = os.path.join(PKG, "libtplayer.so")
+OBJDIR = os.path.join(HERE, "_build")
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+
+# Packed fp32 instructions are disabled for all device code (the compiler
+# would otherwise form them from float2 / paired scalar code).
+DEVICE_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-munsafe-fp-atomics", "-Wall", "-Wno-unused-variable",
+    f"-I{os.path.join(ROOT, 'include')}",
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(HERE, "*.hip")))
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {os.path.basename(src)}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(force: bool = True, jobs: int | None = None, verbose: bool = False) -> str:
+    """Compile every HIP source and link the shared library; returns its path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = sources()
+    headers = glob.glob(os.path.join(HERE, "*.h")) + glob.glob(os.path.join(ROOT, "include", "*.h"))
+    newest_hdr = max((os.path.getmtime(h) for h in headers), default=0.0)
+    todo = []
+    for s in srcs:
+        obj = os.path.join(OBJDIR, os.path.basename(s) + ".o")
+        if force or not os.path.exists(obj) or os.path.getmtime(obj) < max(os.path.getmtime(s), newest_hdr):
+            todo.append(s)
+    jobs = jobs or min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
+    if todo:
+        with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+            for obj in ex.map(_compile, todo):
+                if verbose:
+                    print("compiled", os.path.basename(obj))
+    objs = [os.path.join(OBJDIR, os.path.basename(s) + ".o") for s in srcs]
+    tmp = OUT + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, OUT)
+    return OUT
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--force", action="store_true")
+    ap.add_argument("--jobs", type=int, default=None)
+    a = ap.parse_args(argv)
+    out = build(force=a.force, jobs=a.jobs, verbose=True)
+    print(out)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

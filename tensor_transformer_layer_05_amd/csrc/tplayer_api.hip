@@ -1,0 +1,200 @@
+// extern "C" entry points of libtplayer: argument validation on the host
+// (before any HIP call, so invalid requests never launch anything), then
+// dispatch to the kernel launchers.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace tpl {
+tp_status gemm_bf16_mfma(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                         bool out_f32, bool aligned, hipStream_t s, int force_tile);
+tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                           bool out_f32, hipStream_t s);
+tp_status gemm_f32(const float* x, const float* w, float* y, int64_t M, int64_t N, int64_t K,
+                   hipStream_t s);
+tp_status act_local(const void* g, const void* u, void* h, int64_t M, int64_t I, int64_t ld,
+                    int act, bool bf16, bool vec, hipStream_t s);
+tp_status reduce_partials(const float* const* partials, int R, const void* residual, void* y,
+                          int64_t total, bool bf16, bool vec, hipStream_t s);
+tp_status rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t N, float eps,
+                  bool bf16, bool vec, hipStream_t s);
+tp_status kv_append(const void* kn, const void* vn, int64_t new_stride, void* kc, void* vc,
+                    const int64_t cs[3], int64_t B, int64_t H, int64_t D, int64_t pos,
+                    hipStream_t s);
+tp_status attn_decode(const void* q, const int64_t qs[3], const void* k, const void* v,
+                      const int64_t kvs[3], void* o, const int64_t os[3], int64_t B, int64_t Skv,
+                      int64_t Hq, int64_t Hkv, float scale, void* ws, hipStream_t s);
+size_t attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv);
+tp_status attn_prefill(const void* q, const int64_t qs[3], const void* k, const void* v,
+                       const int64_t kvs[3], void* o, const int64_t os[3], int64_t B, int64_t Sq,
+                       int64_t Skv, int64_t Hq, int64_t Hkv, int causal, float scale,
+                       hipStream_t s);
+
+static thread_local char g_last_error[512] = "";
+
+void set_hip_error(const char* where, hipError_t e) {
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+}  // namespace tpl
+
+namespace {
+
+constexpr int64_t kIntMax = 0x7fffffff;
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline size_t esize(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
+inline bool dtype_ok(tp_dtype dt) { return dt == TP_F32 || dt == TP_BF16; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+tp_status linear_common(const void* x, const void* w, void* y, int64_t M, int64_t K, int64_t N,
+                        tp_dtype dt, void* stream, bool out_f32) {
+  if (!x || !w || !y) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (M <= 0 || K <= 0 || N <= 0) return TP_ERR_SHAPE;
+  if (M > kIntMax || K > kIntMax || N > kIntMax) return TP_ERR_UNSUPPORTED;
+  const size_t es = esize(dt);
+  if (!aligned(x, es) || !aligned(w, es) || !aligned(y, out_f32 ? 4 : es)) return TP_ERR_ALIGN;
+  hipStream_t s = as_stream(stream);
+  if (dt == TP_F32)
+    return tpl::gemm_f32(static_cast<const float*>(x), static_cast<const float*>(w),
+                         static_cast<float*>(y), M, N, K, s);
+  const bool vec = (K % 8 == 0) && aligned(x, 16) && aligned(w, 16);
+  if (M <= 64 && vec) return tpl::gemm_bf16_stream(x, w, y, M, N, K, out_f32, s);
+  return tpl::gemm_bf16_mfma(x, w, y, M, N, K, out_f32, vec, s, -1);
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_column_linear(const void* x, const void* w, void* y, int64_t M, int64_t K, int64_t N,
+                           tp_dtype dt, void* stream) {
+  return linear_common(x, w, y, M, K, N, dt, stream, /*out_f32=*/dt == TP_F32);
+}
+
+tp_status tp_row_linear_partial(const void* x, const void* w, float* partial, int64_t M, int64_t K,
+                                int64_t N, tp_dtype dt, void* stream) {
+  return linear_common(x, w, partial, M, K, N, dt, stream, /*out_f32=*/true);
+}
+
+tp_status tp_swiglu_local(const void* gate, const void* up, void* h, int64_t M, int64_t I,
+                          int64_t ld, tp_act act, tp_dtype dt, void* stream) {
+  if (!gate || !h) return TP_ERR_NULL;
+  if (act != TP_ACT_NONE && act != TP_ACT_SWIGLU && act != TP_ACT_GELU) return TP_ERR_DTYPE;
+  if (act == TP_ACT_SWIGLU && !up) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (M <= 0 || I <= 0 || ld < I) return TP_ERR_SHAPE;
+  const size_t es = esize(dt);
+  if (!aligned(gate, es) || !aligned(h, es) || (up && !aligned(up, es))) return TP_ERR_ALIGN;
+  bool vec = (I % 8 == 0) && (ld % 8 == 0) && aligned(gate, 16) && aligned(h, 16) &&
+             (act != TP_ACT_SWIGLU || aligned(up, 16));
+  return tpl::act_local(gate, up, h, M, I, ld, (int)act, dt == TP_BF16, vec, as_stream(stream));
+}
+
+size_t tp_local_attention_workspace(int64_t B, int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv,
+                                    int64_t D) {
+  if (B <= 0 || Sq <= 0 || Skv <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return 0;
+  const int64_t G = Hq / Hkv;
+  if (Sq == 1 && (G == 1 || G == 2 || G == 4 || G == 8))
+    return tpl::attn_decode_workspace(B, Hq, Hkv, Skv);
+  return 0;
+}
+
+tp_status tp_local_attention(const void* q, const int64_t qs[3], const void* k, const void* v,
+                             const int64_t kvs[3], void* o, const int64_t os[3], int64_t B,
+                             int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv, int64_t D,
+                             int causal, float scale, tp_dtype dt, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !qs || !kvs || !os) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (B <= 0 || Sq <= 0 || Skv <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return TP_ERR_SHAPE;
+  if (Hq % Hkv != 0) return TP_ERR_SHAPE;
+  if (causal && Sq > Skv) return TP_ERR_SHAPE;
+  if (!isfinite(scale)) return TP_ERR_SHAPE;
+  if (dt != TP_BF16 || D != 128) return TP_ERR_UNSUPPORTED;
+  if (B > 65535 || Hq > 65535 || Skv > kIntMax || Sq > kIntMax) return TP_ERR_UNSUPPORTED;
+  for (int i = 0; i < 3; ++i) {
+    if (qs[i] < 0 || kvs[i] < 0 || os[i] < 0) return TP_ERR_SHAPE;
+    if (qs[i] % 8 || kvs[i] % 8 || os[i] % 4) return TP_ERR_ALIGN;
+  }
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 8)) return TP_ERR_ALIGN;
+  hipStream_t s = as_stream(stream);
+  const size_t need = tp_local_attention_workspace(B, Sq, Skv, Hq, Hkv, D);
+  if (Sq == 1 && need == 0 && (Hq / Hkv == 1 || Hq / Hkv == 2 || Hq / Hkv == 4 || Hq / Hkv == 8))
+    return tpl::attn_decode(q, qs, k, v, kvs, o, os, B, Skv, Hq, Hkv, scale, nullptr, s);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return TP_ERR_ALIGN;
+    return tpl::attn_decode(q, qs, k, v, kvs, o, os, B, Skv, Hq, Hkv, scale, workspace, s);
+  }
+  return tpl::attn_prefill(q, qs, k, v, kvs, o, os, B, Sq, Skv, Hq, Hkv, causal, scale, s);
+}
+
+tp_status tp_kv_append(const void* k_new, const void* v_new, int64_t new_stride, void* k_cache,
+                       void* v_cache, const int64_t cs[3], int64_t B, int64_t Hkv, int64_t D,
+                       int64_t pos, tp_dtype dt, void* stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !cs) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (dt != TP_BF16) return TP_ERR_UNSUPPORTED;
+  if (B <= 0 || Hkv <= 0 || D <= 0 || pos < 0 || new_stride < Hkv * D) return TP_ERR_SHAPE;
+  if (cs[0] < 0 || cs[1] < 0 || cs[2] < 0) return TP_ERR_SHAPE;
+  if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(k_cache, 2) || !aligned(v_cache, 2))
+    return TP_ERR_ALIGN;
+  return tpl::kv_append(k_new, v_new, new_stride, k_cache, v_cache, cs, B, Hkv, D, pos,
+                        as_stream(stream));
+}
+
+tp_status tp_reduce_partials(const float* const* partials, int64_t R, const void* residual,
+                             void* y, int64_t M, int64_t N, tp_dtype out_dt, void* stream) {
+  if (!partials || !y) return TP_ERR_NULL;
+  if (R < 1 || R > 16) return TP_ERR_SHAPE;
+  for (int64_t r = 0; r < R; ++r)
+    if (!partials[r]) return TP_ERR_NULL;
+  if (!dtype_ok(out_dt)) return TP_ERR_DTYPE;
+  if (M <= 0 || N <= 0) return TP_ERR_SHAPE;
+  const size_t es = esize(out_dt);
+  if (!aligned(y, es) || (residual && !aligned(residual, es))) return TP_ERR_ALIGN;
+  bool vec = ((M * N) % 4 == 0) && aligned(y, 4 * es) && (!residual || aligned(residual, 4 * es));
+  for (int64_t r = 0; r < R; ++r) {
+    if (!aligned(partials[r], 4)) return TP_ERR_ALIGN;
+    vec = vec && aligned(partials[r], 16);
+  }
+  return tpl::reduce_partials(partials, (int)R, residual, y, M * N, out_dt == TP_BF16, vec,
+                              as_stream(stream));
+}
+
+tp_status tp_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t N, float eps,
+                     tp_dtype dt, void* stream) {
+  if (!x || !gamma || !y) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (M <= 0 || N <= 0 || !(eps >= 0.f) || !isfinite(eps)) return TP_ERR_SHAPE;
+  if (M > kIntMax) return TP_ERR_UNSUPPORTED;
+  const size_t es = esize(dt);
+  if (!aligned(x, es) || !aligned(gamma, es) || !aligned(y, es)) return TP_ERR_ALIGN;
+  const bool vec = dt == TP_BF16 && (N % 8 == 0) && aligned(x, 16) && aligned(gamma, 16) &&
+                   aligned(y, 16);
+  return tpl::rmsnorm(x, gamma, y, M, N, eps, dt == TP_BF16, vec, as_stream(stream));
+}
+
+const char* tp_status_string(tp_status s) {
+  switch (s) {
+    case TP_OK: return "ok";
+    case TP_ERR_NULL: return "null pointer argument";
+    case TP_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case TP_ERR_DTYPE: return "invalid dtype or activation";
+    case TP_ERR_ALIGN: return "misaligned pointer or stride";
+    case TP_ERR_WORKSPACE: return "workspace missing or too small";
+    case TP_ERR_HIP: return "HIP runtime error";
+    case TP_ERR_UNSUPPORTED: return "request outside the implemented kernels";
+  }
+  return "unknown status";
+}
+
+const char* tp_last_error(void) { return tpl::g_last_error; }
+
+const char* tp_version(void) { return "tplayer 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,186 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/tplayer.h, and rejects invalid arguments with the
+documented status before launching anything.
+
+The invalid-argument cases pass made-up non-NULL addresses; each is built so
+that validation must reject it.  They are skipped where a GPU is visible, so
+that a validation bug can never turn one into a launch on a bogus address.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import tensor_transformer_layer_05_amd as tpl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tplayer.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, HIP, UNSUPPORTED = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tpl.library_path):
+        from tensor_transformer_layer_05_amd.csrc import build
+        build.build(force=False)
+    return tpl.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("tp_column_linear", "tp_swiglu_local", "tp_local_attention", "tp_row_linear_partial",
+              "tp_reduce_partials", "tp_rmsnorm", "tp_kv_append", "tp_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared():
+        assert hasattr(lib, n), f"{n} declared in tplayer.h but not exported"
+    assert set(_declared()) == set(tpl.EXPORTED)
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.tp_status_string(s)
+    assert lib.tp_status_string(99) == b"unknown status"
+    assert b"gfx950" in lib.tp_version()
+
+
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="fake-address validation cases run only where no GPU is visible")
+
+P = 0x10000          # a made-up, 64 KiB aligned address (never dereferenced)
+S = None             # default stream
+
+
+@no_gpu
+def test_linear_validation(lib):
+    for fn in (lib.tp_column_linear, lib.tp_row_linear_partial):
+        assert fn(None, P, P, 4, 8, 8, 1, S) == NULL
+        assert fn(P, None, P, 4, 8, 8, 1, S) == NULL
+        assert fn(P, P, None, 4, 8, 8, 1, S) == NULL
+        assert fn(P, P, P, 0, 8, 8, 1, S) == SHAPE
+        assert fn(P, P, P, 4, -1, 8, 1, S) == SHAPE
+        assert fn(P, P, P, 4, 8, 0, 1, S) == SHAPE
+        assert fn(P, P, P, 4, 8, 8, 7, S) == DTYPE
+        assert fn(P + 1, P, P, 4, 8, 8, 1, S) == ALIGN
+        assert fn(P, P + 2, P, 4, 8, 8, 0, S) == ALIGN       # fp32 needs 4-byte alignment
+        assert fn(P, P, P, 1 << 31, 8, 8, 1, S) == UNSUPPORTED
+    assert lib.tp_row_linear_partial(P, P, P + 2, 4, 8, 8, 1, S) == ALIGN   # fp32 partial
+
+
+@no_gpu
+def test_activation_validation(lib):
+    f = lib.tp_swiglu_local
+    assert f(None, P, P, 2, 8, 8, 1, 1, S) == NULL
+    assert f(P, None, P, 2, 8, 8, 1, 1, S) == NULL          # swiglu needs up
+    assert f(P, P, P, 2, 8, 4, 1, 1, S) == SHAPE            # ld < I
+    assert f(P, P, P, 0, 8, 8, 1, 1, S) == SHAPE
+    assert f(P, P, P, 2, 8, 8, 9, 1, S) == DTYPE            # bad activation
+    assert f(P, P, P, 2, 8, 8, 1, 5, S) == DTYPE            # bad dtype
+    assert f(P + 1, P, P, 2, 8, 8, 1, 1, S) == ALIGN
+
+
+def _s3(*v):
+    return (ctypes.c_int64 * 3)(*v)
+
+
+@no_gpu
+def test_attention_validation(lib):
+    f = lib.tp_local_attention
+    qs, kvs, os_ = _s3(1024, 1024, 128), _s3(2 * 64 * 128, 128, 64 * 128), _s3(1024, 1024, 128)
+    args = dict(B=2, Sq=1, Skv=64, Hq=8, Hkv=2, D=128)
+
+    def call(q=P, k=P, v=P, o=P, qs=qs, kvs=kvs, os_=os_, B=2, Sq=1, Skv=64, Hq=8, Hkv=2, D=128,
+             causal=1, scale=0.088, dt=1, ws=None, wsb=0):
+        return f(q, qs, k, v, kvs, o, os_, B, Sq, Skv, Hq, Hkv, D, causal, scale, dt, ws, wsb, S)
+
+    assert call(q=None) == NULL
+    assert call(os_=None) == NULL
+    assert call(Hq=6, Hkv=4) == SHAPE                        # Hq % Hkv != 0
+    assert call(Sq=65, Skv=64) == SHAPE                      # causal with more queries than keys
+    assert call(B=0) == SHAPE
+    assert call(scale=float("inf")) == SHAPE
+    assert call(D=64) == UNSUPPORTED
+    assert call(dt=0) == UNSUPPORTED
+    assert call(dt=3) == DTYPE
+    assert call(qs=_s3(1024, 1024, 100)) == ALIGN            # head stride not a multiple of 8
+    assert call(q=P + 2) == ALIGN
+    # decode with enough sequences x KV heads never needs a workspace; with a
+    # long span and few pairs it does
+    need = lib.tp_local_attention_workspace(1, 1, 4096, 8, 2, 128)
+    assert need > 0
+    assert call(B=1, Skv=4096, kvs=_s3(2 * 4096 * 128, 128, 4096 * 128)) == WORKSPACE
+    assert call(B=1, Skv=4096, kvs=_s3(2 * 4096 * 128, 128, 4096 * 128), ws=P, wsb=need - 1) == WORKSPACE
+    assert lib.tp_local_attention_workspace(1, 128, 4096, 8, 2, 128) == 0   # prefill: none
+    assert lib.tp_local_attention_workspace(1, 1, 4096, 6, 4, 128) == 0     # invalid: none
+
+
+@no_gpu
+def test_reduce_validation(lib):
+    f = lib.tp_reduce_partials
+    arr = (ctypes.c_void_p * 2)(P, P)
+    assert f(None, 2, None, P, 4, 4, 0, S) == NULL
+    assert f(arr, 0, None, P, 4, 4, 0, S) == SHAPE
+    assert f(arr, 17, None, P, 4, 4, 0, S) == SHAPE
+    bad = (ctypes.c_void_p * 2)(P, None)
+    assert f(bad, 2, None, P, 4, 4, 0, S) == NULL
+    assert f(arr, 2, None, P, 0, 4, 0, S) == SHAPE
+    assert f(arr, 2, None, P, 4, 4, 4, S) == DTYPE
+    assert f(arr, 2, P + 2, P, 4, 4, 0, S) == ALIGN
+    odd = (ctypes.c_void_p * 2)(P, P + 2)
+    assert f(odd, 2, None, P, 4, 4, 0, S) == ALIGN
+
+
+@no_gpu
+def test_rmsnorm_and_append_validation(lib):
+    assert lib.tp_rmsnorm(None, P, P, 4, 8, 1e-5, 1, S) == NULL
+    assert lib.tp_rmsnorm(P, P, P, 4, 8, -1.0, 1, S) == SHAPE
+    assert lib.tp_rmsnorm(P, P, P, 4, 8, float("nan"), 1, S) == SHAPE
+    assert lib.tp_rmsnorm(P, P, P, 0, 8, 1e-5, 1, S) == SHAPE
+    assert lib.tp_rmsnorm(P, P, P + 1, 4, 8, 1e-5, 1, S) == ALIGN
+    cs = _s3(2 * 64 * 128, 128, 64 * 128)
+    f = lib.tp_kv_append
+    assert f(None, P, 256, P, P, cs, 2, 2, 128, 0, 1, S) == NULL
+    assert f(P, P, 128, P, P, cs, 2, 2, 128, 0, 1, S) == SHAPE     # row stride < Hkv*D
+    assert f(P, P, 256, P, P, cs, 2, 2, 128, -1, 1, S) == SHAPE
+    assert f(P, P, 256, P, P, cs, 2, 2, 128, 0, 0, S) == UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# host-side shard slicing of the binding (CPU tensors; pure indexing)
+# ---------------------------------------------------------------------------
+
+def test_shard_helpers_match_oracle_slices():
+    import oracle.tp_oracle as O
+    w = torch.arange(8 * 12, dtype=torch.float32).reshape(8, 12)
+    for R in (1, 2, 4):
+        for r in range(R):
+            assert np.array_equal(tpl.shard_column(w, r, R).numpy(), O.column_shard(w.numpy(), r, R))
+            assert np.array_equal(tpl.shard_row(w, r, R).numpy(), O.row_shard(w.numpy(), r, R))
+    with pytest.raises(ValueError):
+        tpl.shard_column(w, 0, 3)
+    with pytest.raises(ValueError):
+        tpl.shard_row(w, 0, 5)
+    wq, wk, wv = (torch.randn(n * 4, 6) for n in (8, 2, 2))
+    for r in range(2):
+        assert np.array_equal(tpl.shard_qkv(wq, wk, wv, r, 2, 4).numpy(),
+                              O.qkv_shard(wq.numpy(), wk.numpy(), wv.numpy(), r, 2, 4))
+    with pytest.raises(ValueError):
+        tpl.shard_qkv(wq, wk, wv, 0, 4, 4)     # 2 KV heads over 4 ranks
+
+
+def test_binding_rejects_cpu_tensors():
+    x = torch.zeros(2, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tpl.column_linear(x, x)
