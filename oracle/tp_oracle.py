@@ -6,7 +6,7 @@ the HIP library (no kernels, headers, helpers or tables) and imports nothing
 from it; inputs reach it as plain float64 numpy arrays.
 
 Everything is written as the plain definition of what the method computes,
-with numpy's matmul, exp and scipy's erf as the only library primitives:
+with numpy's matmul, exp and scipy's erfc as the only library primitives:
 no blocking, fusion or reordering.
 
 Sources (web pages; each function names the section it follows):
@@ -33,14 +33,14 @@ Conventions (readings where the pages leave a choice open):
     the identity at inference (P2 section 二).
   * RMSNorm ``x * (mean(x^2) + eps)^(-1/2) * gamma`` -- not on the pages,
     parity unpinned by them (pinned here by closed forms only).
-  * GELU is the exact erf form, ``g * Phi(g)``.
+  * GELU is the exact (erf/erfc) form, ``g * Phi(g)``, not the tanh approximation.
 """
 from __future__ import annotations
 
 import math
 
 import numpy as np
-from scipy.special import erf as _erf
+from scipy.special import erfc as _erfc
 
 __all__ = [
     "round_bf16", "linear", "column_shard", "row_shard", "input_shard",
@@ -149,8 +149,11 @@ def silu(g):
 
 
 def gelu(g):
+    """``g * Phi(g)`` with the standard normal CDF ``Phi(g) = erfc(-g/sqrt 2)/2``
+    (equal to ``(1 + erf(g/sqrt 2))/2``; the erfc form does not cancel for
+    negative g)."""
     g = np.asarray(g, np.float64)
-    return 0.5 * g * (1.0 + _erf(g / math.sqrt(2.0)))
+    return 0.5 * g * _erfc(-g / math.sqrt(2.0))
 
 
 def local_activation(g, u=None, act: str = "swiglu"):

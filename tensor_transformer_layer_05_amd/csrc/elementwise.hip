@@ -11,7 +11,9 @@ namespace tpl {
 template <int ACT>
 __device__ __forceinline__ float act_fn(float g, float u) {
   if constexpr (ACT == TP_ACT_SWIGLU) return g / (1.0f + expf(-g)) * u;
-  else if constexpr (ACT == TP_ACT_GELU) return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
+  // GELU(g) = g * Phi(g) with Phi(g) = erfc(-g / sqrt 2) / 2: the erfc form
+  // keeps full relative accuracy for negative g, where 1 + erf(.) cancels.
+  else if constexpr (ACT == TP_ACT_GELU) return 0.5f * g * erfcf(-g * 0.70710678118654752f);
   else return g;
 }
 

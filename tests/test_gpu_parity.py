@@ -235,7 +235,7 @@ def test_attention_strided_qkv_views():
     ref = O.attention(r[None, :, :Hq * D].reshape(1, S, Hq, D),
                       r[None, :, Hq * D:(Hq + Hkv) * D].reshape(1, S, Hkv, D),
                       r[None, :, (Hq + Hkv) * D:].reshape(1, S, Hkv, D), causal=True)
-    assert_within(out, ref.reshape(S, Hq * D), _attn_bound(ref, r), "strided views")
+    assert_within(out, ref.reshape(S, Hq * D), _attn_bound(ref, r).reshape(S, Hq * D), "strided views")
 
 
 def test_kv_append_exact():

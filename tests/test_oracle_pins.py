@@ -149,6 +149,7 @@ def test_reduce_order_and_residual():
 
 PHI_1 = 0.8413447460685429     # standard normal CDF at 1 (textbook table)
 PHI_2 = 0.9772498680518208     # standard normal CDF at 2
+PHI_M10 = 7.6198530241605e-24  # standard normal CDF at -10 (upper tail at 10)
 
 
 def check_activations():
@@ -158,6 +159,8 @@ def check_activations():
     assert math.isclose(float(O.gelu(1.0)), PHI_1, rel_tol=1e-15)
     assert math.isclose(float(O.gelu(2.0)), 2 * PHI_2, rel_tol=1e-15)
     assert math.isclose(float(O.gelu(-1.0)), -(1 - PHI_1), rel_tol=1e-14)
+    # far tail: full relative accuracy where 1 + erf(.) would cancel to 0
+    assert math.isclose(float(O.gelu(-10.0)), -10.0 * PHI_M10, rel_tol=1e-10)
     x = np.linspace(-6, 6, 101)
     # f(x) - f(-x) = x for both (sigma(x)+sigma(-x)=1, Phi(x)+Phi(-x)=1)
     assert np.allclose(O.silu(x) - O.silu(-x), x, atol=1e-14)
