@@ -1,0 +1,209 @@
+"""Every workload at its full size, in the launch configuration the benchmark
+uses (the ``shard`` orchestration classes), against the float64 oracle.
+
+Multi-rank configurations run every rank's shard one after another on the one
+GPU and sum the partials in HBM (the arithmetic of the all-reduce), then
+compare with the UNSHARDED oracle layer: sharded output must equal unsharded
+output (mini vLLM TP page, "如何验证 tensor parallel 正确").  Where the oracle
+cannot afford every output row, a fixed sample of rows (first, last and
+seeded interior rows) is compared element by element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.tp_oracle as O
+import tensor_transformer_layer_05_amd as tpl
+from tensor_transformer_layer_05_amd import inputs as I
+from tensor_transformer_layer_05_amd.shard import AttnShard, LayerShard, MlpShard
+from util import assert_bitexact, assert_normwise, log
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def sample_rows(n, k, seed):
+    rng = np.random.default_rng(seed)
+    inner = rng.choice(np.arange(1, n - 1), size=min(k - 2, n - 2), replace=False)
+    return np.unique(np.concatenate([[0, n - 1], inner]))
+
+
+# ---------------------------------------------------------------------------
+
+def test_toy_mlp_int_bitexact():
+    c = I.config("toy_mlp_int")
+    log("config toy_mlp_int")
+    M, H, F, R = c.tokens[0], c.hidden, c.inter, c.tp
+    x = I.uniform_int(c.seed, "x", (M, H))
+    w1 = [I.uniform_int(c.seed, "w1", (F // R, H), rank=r) for r in range(R)]
+    w2 = [I.uniform_int(c.seed, "w2", (H, F // R), rank=r) for r in range(R)]
+    W1 = np.concatenate([w.ref for w in w1], 0)
+    W2 = np.concatenate([w.ref for w in w2], 1)
+    ref = O.mlp_unsharded(x.ref, W1, W2, "none")
+    X = x.dev.to(DEV)
+    parts = []
+    for r in range(R):
+        sh = MlpShard(w1[r].dev.to(DEV), w2[r].dev.to(DEV), "none", M)
+        p = torch.empty((M, H), dtype=torch.float32, device=DEV)
+        sh.partial(X, p)
+        assert_bitexact(p, O.mlp_rank_partial(x.ref, W1, W2, "none", r, R), f"rank {r} partial")
+        parts.append(p)
+    assert_bitexact(tpl.reduce_partials(parts), ref, "sum of partials == unsharded")
+
+
+@pytest.mark.parametrize("M", [1, 8, 64])
+def test_decode_mlp_tp8_rank0(M):
+    c = I.config("decode_mlp_tp8")
+    log(f"config decode_mlp_tp8 rank 0 M={M}")
+    H, il = c.hidden, c.inter // c.tp
+    x = I.normal(c.seed, "x", (M, H))
+    wg = I.normal(c.seed, "wg", (il, H), c.w_std, rank=0)
+    wu = I.normal(c.seed, "wu", (il, H), c.w_std, rank=0)
+    wd = I.normal(c.seed, "wd", (H, il), c.w_std, rank=0)
+    sh = MlpShard(torch.cat([wg.dev, wu.dev], 0).to(DEV), wd.dev.to(DEV), "swiglu", 64)
+    p = torch.empty((M, H), dtype=torch.float32, device=DEV)
+    sh.partial(x.dev.to(DEV), p)
+    ref = O.mlp_rank_partial(x.ref, wg.ref, wd.ref, "swiglu", 0, 1, w_up=wu.ref)
+    assert_normwise(p, ref, 1e-2, f"rank-0 partial M={M}")
+    # storage-faithful oracle (bf16 intermediates where the kernels store them)
+    ref_s = O.mlp_rank_partial(x.ref, wg.ref, wd.ref, "swiglu", 0, 1, w_up=wu.ref,
+                               store=O.round_bf16)
+    assert_normwise(p, ref_s, 2e-3, f"rank-0 partial vs storage-faithful M={M}")
+
+
+def test_decode_mlp_tp8_all_ranks_equal_unsharded():
+    c = I.config("decode_mlp_tp8")
+    M, H, R, il = 8, c.hidden, c.tp, c.inter // c.tp
+    log(f"config decode_mlp_tp8 all {R} ranks M={M}")
+    x = I.normal(c.seed, "x", (M, H))
+    X = x.dev.to(DEV)
+    parts, gs, us, ds = [], [], [], []
+    for r in range(R):
+        wg = I.normal(c.seed, "wg", (il, H), c.w_std, rank=r)
+        wu = I.normal(c.seed, "wu", (il, H), c.w_std, rank=r)
+        wd = I.normal(c.seed, "wd", (H, il), c.w_std, rank=r)
+        gs.append(wg.ref); us.append(wu.ref); ds.append(wd.ref)
+        sh = MlpShard(torch.cat([wg.dev, wu.dev], 0).to(DEV), wd.dev.to(DEV), "swiglu", M)
+        p = torch.empty((M, H), dtype=torch.float32, device=DEV)
+        parts.append(sh.partial(X, p))
+        del sh
+    y = tpl.reduce_partials(parts, out_dtype=torch.bfloat16)
+    ref = O.mlp_unsharded(x.ref, np.concatenate(gs, 0), np.concatenate(ds, 1), "swiglu",
+                          w_up=np.concatenate(us, 0))
+    assert_normwise(y, ref, 1e-2, "8-rank sum vs unsharded MLP")
+
+
+def test_decode_attn_tp4_rank0():
+    c = I.config("decode_attn_tp4")
+    H, R, D, B, L = c.hidden, c.tp, c.head_dim, c.batch, c.kv_len
+    hq, hkv = c.n_q // R, c.n_kv // R
+    log(f"config decode_attn_tp4 rank 0 B={B} L={L}")
+    x = I.normal(c.seed, "x", (B, H))
+    wqkv = I.normal(c.seed, "wqkv", ((hq + 2 * hkv) * D, H), c.w_std)
+    wo = I.normal(c.seed, "wo", (H, hq * D), c.w_std)
+    kc = I.normal(c.seed, "kcache", (B, hkv, L, D))
+    vc = I.normal(c.seed, "vcache", (B, hkv, L, D))
+    sh = AttnShard(wqkv.dev.to(DEV), wo.dev.to(DEV), hq, hkv, D, B)
+    K, V = kc.dev.to(DEV), vc.dev.to(DEV)
+    p = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    sh.decode_partial(x.dev.to(DEV), K.transpose(1, 2), V.transpose(1, 2), L - 1, p)
+    # oracle: the new token's k/v replace key position L-1, then attention over L keys
+    qkv = O.linear(x.ref, wqkv.ref)
+    q = qkv[:, :hq * D].reshape(B, 1, hq, D)
+    kn = qkv[:, hq * D:(hq + hkv) * D].reshape(B, hkv, D)
+    vn = qkv[:, (hq + hkv) * D:].reshape(B, hkv, D)
+    k = kc.ref.copy(); v = vc.ref.copy()
+    k[:, :, L - 1] = kn; v[:, :, L - 1] = vn
+    o = O.attention(q, k.transpose(0, 2, 1, 3), v.transpose(0, 2, 1, 3), causal=True)
+    ref = O.row_linear_partial(o.reshape(B, hq * D), wo.ref)
+    assert_normwise(p, ref, 1e-2, "decode attention shard partial")
+    # the appended cache slot holds the projected k/v (bf16 of the column linear)
+    assert_normwise(K[:, :, L - 1], kn, 1e-2, "appended k")
+    assert_normwise(V[:, :, L - 1], vn, 1e-2, "appended v")
+
+
+def _layer_weights(c, R):
+    H, D = c.hidden, c.head_dim
+    hq, hkv, il = c.n_q // R, c.n_kv // R, c.inter // R
+    out = []
+    for r in range(R):
+        out.append(dict(
+            wq=I.normal(c.seed, "wq", (hq * D, H), c.w_std, rank=r),
+            wk=I.normal(c.seed, "wk", (hkv * D, H), c.w_std, rank=r),
+            wv=I.normal(c.seed, "wv", (hkv * D, H), c.w_std, rank=r),
+            wo=I.normal(c.seed, "wo", (H, hq * D), c.w_std, rank=r),
+            wg=I.normal(c.seed, "wg", (il, H), c.w_std, rank=r),
+            wu=I.normal(c.seed, "wu", (il, H), c.w_std, rank=r),
+            wd=I.normal(c.seed, "wd", (H, il), c.w_std, rank=r)))
+    return out
+
+
+@pytest.mark.slow
+def test_prefill_layer_tp2_equals_unsharded():
+    c = I.config("prefill_layer_tp2")
+    H, R, D, S = c.hidden, c.tp, c.head_dim, c.tokens[0]
+    hq, hkv = c.n_q // R, c.n_kv // R
+    log(f"config prefill_layer_tp2 S={S} H={H} (both ranks)")
+    x = I.normal(c.seed, "x", (S, H), c.x_std)
+    g1 = I.normal(c.seed, "g1", (H,), 1.0)      # random RMSNorm scales (gamma = 1 in the bench)
+    g2 = I.normal(c.seed, "g2", (H,), 1.0)
+    ws = _layer_weights(c, R)
+    X = x.dev.to(DEV)
+    shards = []
+    for r in range(R):
+        w = ws[r]
+        shards.append(LayerShard(g1.dev.to(DEV), g2.dev.to(DEV),
+                                 torch.cat([w["wq"].dev, w["wk"].dev, w["wv"].dev], 0).to(DEV),
+                                 w["wo"].dev.to(DEV), torch.cat([w["wg"].dev, w["wu"].dev], 0).to(DEV),
+                                 w["wd"].dev.to(DEV), hq, hkv, D, c.eps, S))
+    pa = [torch.empty((S, H), dtype=torch.float32, device=DEV) for _ in range(R)]
+    pm = [torch.empty((S, H), dtype=torch.float32, device=DEV) for _ in range(R)]
+    for r in range(R):
+        shards[r].attn_partial(X, pa[r])
+    h = tpl.reduce_partials(pa, residual=X)
+    for r in range(R):
+        shards[r].mlp_partial(h, pm[r])
+    y = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
+    # the benchmark's step for rank 0, with rank 1's partials already in place
+    shards[0].step(X, pa, pm, 0, y)
+    torch.cuda.synchronize()
+    rows = sample_rows(S, 48, 104)
+    cat0 = lambda n: np.concatenate([ws[r][n].ref for r in range(R)], 0)
+    cat1 = lambda n: np.concatenate([ws[r][n].ref for r in range(R)], 1)
+    p = dict(g1=g1.ref, g2=g2.ref, wq=cat0("wq"), wk=cat0("wk"), wv=cat0("wv"), wo=cat1("wo"),
+             wg=cat0("wg"), wu=cat0("wu"), wd=cat1("wd"))
+    ref = O.layer_unsharded(x.ref, p, D, c.eps, rows=rows)
+    yr = y.to("cpu", torch.float64).numpy()[rows]
+    assert_normwise(yr, ref, 1e-2, f"layer output, {len(rows)} sampled rows vs unsharded")
+    # the layer output minus the residual path (the two sub-blocks' sum) is
+    # the part the shards compute; check it separately so the residual cannot
+    # hide an error
+    hr = h.to("cpu", torch.float64).numpy()[rows]
+    attn_ref = O.attention_block_unsharded(O.rmsnorm(x.ref, g1.ref, c.eps), p["wq"], p["wk"],
+                                           p["wv"], p["wo"], D, causal=True, rows=rows)
+    assert_normwise(hr - x.ref[rows], attn_ref, 1e-2, "attention sub-block (h - x)")
+    assert_normwise(yr - hr, ref - (x.ref[rows] + attn_ref), 1e-2, "MLP sub-block (y - h)")
+
+
+@pytest.mark.slow
+def test_gelu_mlp_tp8_all_ranks_equal_unsharded():
+    c = I.config("gelu_mlp_tp8")
+    M, H, F, R = c.tokens[0], c.hidden, c.inter, c.tp
+    log(f"config gelu_mlp_tp8 M={M} H={H} 4H={F}, all {R} ranks")
+    x = I.normal(c.seed, "x", (M, H), c.x_std)
+    X = x.dev.to(DEV)
+    parts, w1s, w2s = [], [], []
+    for r in range(R):
+        w1 = I.normal(c.seed, "w1", (F // R, H), c.w_std, rank=r)
+        w2 = I.normal(c.seed, "w2", (H, F // R), c.w_std, rank=r)
+        w1s.append(w1.ref); w2s.append(w2.ref)
+        sh = MlpShard(w1.dev.to(DEV), w2.dev.to(DEV), "gelu", M)
+        p = torch.empty((M, H), dtype=torch.float32, device=DEV)
+        parts.append(sh.partial(X, p))
+        del sh
+    y = tpl.reduce_partials(parts, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 32, 105)
+    ref = O.mlp_unsharded(x.ref[rows], np.concatenate(w1s, 0), np.concatenate(w2s, 1), "gelu")
+    assert_normwise(y.to("cpu", torch.float64).numpy()[rows], ref, 1e-2,
+                    f"8-rank sum, {len(rows)} sampled rows vs unsharded FFN")
