@@ -1,0 +1,267 @@
+// Large-M bf16 GEMM on MFMA with direct global->LDS tile loads (gfx950).
+//
+//   Y[m, n] = sum_k X[m, k] * W[n, k]          (Y = X W with W stored [N, K])
+//
+// This is the path of the column- and row-parallel linears at prefill sizes
+// (M > 64) when the operands allow 16-byte loads.  Design points for CDNA4:
+//
+//  * Tiles reach LDS through `buffer_load_dwordx4 ... lds`: each wave-level
+//    load writes 1 KB (8 rows of 64 bf16) straight into LDS, so tile staging
+//    costs no VGPRs and no ds_write instructions.  The buffer resource is
+//    bounded to the tile's valid rows and out-of-range lanes get an offset
+//    past that bound, so ragged edges (rows >= M or N, k >= K) read as zero
+//    without any branch.
+//  * LDS rows are 128 bytes (BK = 64); the 16-byte chunk index is XOR-ed with
+//    (row / 2) % 8.  The loads realise the swizzle by choosing which global
+//    chunk each lane fetches, and the MFMA fragment reads (16 lanes = 16 rows
+//    of one chunk column) land on 16 distinct 16-byte bank groups.
+//  * The W tile is the A operand and the X tile the B operand of
+//    v_mfma_f32_32x32x16_bf16, so a lane's accumulators hold 4 consecutive
+//    output features of one token: the epilogue writes 16-byte (fp32) or
+//    8-byte (bf16) vectors.
+//  * Two LDS stages, one barrier per 64-k step.  The step's body is pinned
+//    with scheduling barriers: fragment reads for sub-step kk+1 are issued
+//    before the MFMAs of sub-step kk, the next step's tile loads go out in the
+//    first two sub-steps, and the last sub-step's MFMAs are split around the
+//    barrier so that the next step's first fragment reads overlap them.
+//  * 256x256 tiles run 8 waves (2 per SIMD, 128x64 per wave, accumulators in
+//    128 VGPRs); 128x128 tiles run 4 waves with 2 workgroups per CU, for grids
+//    too small to fill 256 CUs with 256x256 tiles.
+//  * Workgroup ids are remapped so that consecutive tile ids share an XCD
+//    (one L2 per XCD), walking groups of 8 M-tiles.
+#include "common.h"
+
+namespace tpl {
+
+#define TPL_LDS __attribute__((address_space(3)))
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
+constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0), others unconstrained
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct DmaTile {
+  static constexpr int BM = BM_, BN = BN_, BK = 64, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = NW * kWave;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // per-wave extents (tokens, features)
+  static constexpr int FB = TM / 32, FA = TN / 32;  // 32-row fragments: B = X side, A = W side
+  static constexpr int XL = BM / 8 / NW, WL = BN / 8 / NW;  // 1 KB loads per wave per step
+  static constexpr int STAGE = (BM + BN) * BK;              // bf16 elements per LDS stage
+  static_assert(XL * NW * 8 == BM && WL * NW * 8 == BN, "load split");
+  static_assert(FA >= 2 && FA % 2 == 0, "the last sub-step splits the A fragments in two");
+};
+
+__device__ __forceinline__ int dswz(int row, int kc) { return kc ^ ((row >> 1) & 7); }
+
+template <class C, bool OUT_F32, bool VEC_OUT>
+__global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
+    int M, int N, int K) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
+
+  const int tiles_m = (M + C::BM - 1) / C::BM;
+  const int tiles_n = (N + C::BN - 1) / C::BN;
+  const int ntile = tiles_m * tiles_n;
+  const int pid = xcd_remap(blockIdx.x, ntile);
+  constexpr int GROUP_M = 8;
+  const int in_group = GROUP_M * tiles_n;
+  const int first_m = (pid / in_group) * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (pid % in_group) % gsize;
+  const int tn = (pid % in_group) / gsize;
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  // Buffer resources based at the tile's first row, bounded to its valid rows.
+  const uint32_t xrows = (uint32_t)min(C::BM, M - m0), wrows = (uint32_t)min(C::BN, N - n0);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + (int64_t)m0 * K), 0, xrows * (uint32_t)K * 2u, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * K), 0, wrows * (uint32_t)K * 2u, 0x00020000);
+
+  // Load i of this wave fills LDS rows (wave*L + i)*8 .. +7; lane -> row lane/8,
+  // LDS chunk lane%8, which holds global chunk dswz(row, lane%8).
+  const int lrow = lane >> 3, lpos = lane & 7;
+  uint32_t xoff[C::XL], woff[C::WL];
+  int xk[C::XL], wk[C::WL];
+#pragma unroll
+  for (int i = 0; i < C::XL; ++i) {
+    const int row = (wave * C::XL + i) * 8 + lrow;
+    xk[i] = 8 * dswz(row, lpos);
+    xoff[i] = (uint32_t)(row * K + xk[i]) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < C::WL; ++i) {
+    const int row = (wave * C::WL + i) * 8 + lrow;
+    wk[i] = 8 * dswz(row, lpos);
+    woff[i] = (uint32_t)(row * K + wk[i]) * 2u;
+  }
+  auto load_x = [&](int k0, int stage) {
+    TPL_LDS uint16_t* base = (TPL_LDS uint16_t*)lds + stage * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::XL; ++i) {
+      const uint32_t off = (k0 + xk[i] < K) ? xoff[i] + (uint32_t)k0 * 2u : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (TPL_LDS void*)(base + (wave * C::XL + i) * 8 * C::BK), 16, off, 0, 0, 0);
+    }
+  };
+  auto load_w = [&](int k0, int stage) {
+    TPL_LDS uint16_t* base = (TPL_LDS uint16_t*)lds + stage * C::STAGE + C::BM * C::BK;
+#pragma unroll
+    for (int i = 0; i < C::WL; ++i) {
+      const uint32_t off = (k0 + wk[i] < K) ? woff[i] + (uint32_t)k0 * 2u : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr, (TPL_LDS void*)(base + (wave * C::WL + i) * 8 * C::BK), 16, off, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[C::FA][C::FB];
+#pragma unroll
+  for (int i = 0; i < C::FA; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Fragment of sub-step kk: lane reads row (lane & 31) of its 32-row block,
+  // 16-byte chunk 2*kk + lane/32.
+  const int frow = lane & 31, fh = lane >> 5;
+  bf16x8 fa[2][C::FA], fb[2][C::FB];
+  auto read_frags = [&](int stage, int kk, int buf) {
+    const uint16_t* base = lds + stage * C::STAGE;
+    const int kc = 2 * kk + fh;
+#pragma unroll
+    for (int i = 0; i < C::FA; ++i) {
+      const int row = wn * C::TN + i * 32 + frow;
+      fa[buf][i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+          base + C::BM * C::BK + row * C::BK + dswz(row, kc) * 8));
+    }
+#pragma unroll
+    for (int j = 0; j < C::FB; ++j) {
+      const int row = wm * C::TM + j * 32 + frow;
+      fb[buf][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + row * C::BK + dswz(row, kc) * 8));
+    }
+  };
+  auto mfmas = [&](int buf, int i0, int i1) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  };
+  auto pin = []() { __builtin_amdgcn_sched_barrier(0); };
+
+  const int nk = (K + C::BK - 1) / C::BK;
+  load_x(0, 0);
+  load_w(0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  read_frags(0, 0, 0);
+  pin();
+  for (int t = 0; t < nk; ++t) {
+    const int st = t & 1;
+    const bool more = t + 1 < nk;
+    // sub-step 0 (stage st+1 was last read before the previous barrier)
+    read_frags(st, 1, 1);
+    if (more) load_x((t + 1) * C::BK, st ^ 1);
+    mfmas(0, 0, C::FA);
+    pin();
+    // sub-step 1
+    read_frags(st, 2, 0);
+    if (more) load_w((t + 1) * C::BK, st ^ 1);
+    mfmas(1, 0, C::FA);
+    pin();
+    // sub-step 2
+    read_frags(st, 3, 1);
+    mfmas(0, 0, C::FA);
+    pin();
+    // sub-step 3, split around the barrier that publishes the next stage
+    mfmas(1, 0, C::FA / 2);
+    pin();
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_barrier();
+    pin();
+    if (more) read_frags(st ^ 1, 0, 0);
+    mfmas(1, C::FA / 2, C::FA);
+    pin();
+  }
+
+  // Epilogue.  acc[i][j] lane holds token m = wm*TM + 32j + (lane&31) and
+  // features n = wn*TN + 32i + 8*(r/4) + 4*(lane/32) + r%4, r = 0..15.
+#pragma unroll
+  for (int i = 0; i < C::FA; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::FB; ++j) {
+      const int m = m0 + wm * C::TM + j * 32 + frow;
+      if (m >= M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * C::TN + i * 32 + 8 * q + 4 * fh;
+        const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]};
+        if (VEC_OUT && n + 3 < N) {
+          if constexpr (OUT_F32) {
+            const f32x4 o = {v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Y) + (int64_t)m * N + n) = o;
+          } else {
+            const u32x2 o = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(Y) + (int64_t)m * N + n) = o;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (n + e < N) {
+              if constexpr (OUT_F32)
+                reinterpret_cast<float*>(Y)[(int64_t)m * N + n + e] = v[e];
+              else
+                reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n + e] = (uint16_t)f2bf_bits(v[e]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+using Dma256 = DmaTile<256, 256, 2, 4>;   // 8 waves, one workgroup per CU
+using Dma128 = DmaTile<128, 128, 2, 2>;   // 4 waves, two workgroups per CU
+
+template <class C>
+static tp_status launch_dma(const void* x, const void* w, void* y, int M, int N, int K,
+                            bool out_f32, bool vec_out, hipStream_t s) {
+  const int ntile = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  dim3 grid(ntile), block(C::NT);
+  auto X = static_cast<const uint16_t*>(x);
+  auto Wp = static_cast<const uint16_t*>(w);
+  if (out_f32) {
+    if (vec_out) hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, true, true>), grid, block, 0, s, X, Wp, y, M, N, K);
+    else hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, true, false>), grid, block, 0, s, X, Wp, y, M, N, K);
+  } else {
+    if (vec_out) hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, false, true>), grid, block, 0, s, X, Wp, y, M, N, K);
+    else hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, false, false>), grid, block, 0, s, X, Wp, y, M, N, K);
+  }
+  TPL_LAUNCH_CHECK("gemm_bf16_dma");
+  return TP_OK;
+}
+
+// 0 = 256x256 (8 waves), 1 = 128x128 (4 waves).  Estimated time = full-chip
+// rounds x round time; a round of 128x128 tiles (two per CU) does half the
+// work of a 256x256 round at ~85% of its efficiency (measured on gate|up- and
+// qkv-shaped problems).
+int gemm_dma_pick_tile(int M, int N) {
+  const double t256 = ceil((double)((M + 255) / 256) * ((N + 255) / 256) / 256.0);
+  const double t128 = ceil((double)((M + 127) / 128) * ((N + 127) / 128) / 512.0) * 0.5 / 0.85;
+  return t128 < t256 ? 1 : 0;
+}
+
+// Requires K % 8 == 0, 16-byte aligned X and W, and 256*K*2 < 2^31.
+tp_status gemm_bf16_dma(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                        bool out_f32, bool vec_out, hipStream_t s, int force_tile) {
+  const int pick = force_tile >= 0 ? force_tile : gemm_dma_pick_tile((int)M, (int)N);
+  if (pick == 0) return launch_dma<Dma256>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
+  return launch_dma<Dma128>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
+}
+
+}  // namespace tpl

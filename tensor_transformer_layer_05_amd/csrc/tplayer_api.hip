@@ -10,6 +10,8 @@
 namespace tpl {
 tp_status gemm_bf16_mfma(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                          bool out_f32, bool aligned, hipStream_t s, int force_tile);
+tp_status gemm_bf16_dma(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                        bool out_f32, bool vec_out, hipStream_t s, int force_tile);
 tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                            bool out_f32, hipStream_t s);
 tp_status gemm_f32(const float* x, const float* w, float* y, int64_t M, int64_t N, int64_t K,
@@ -63,6 +65,11 @@ tp_status linear_common(const void* x, const void* w, void* y, int64_t M, int64_
                          static_cast<float*>(y), M, N, K, s);
   const bool vec = (K % 8 == 0) && aligned(x, 16) && aligned(w, 16);
   if (M <= 64 && vec) return tpl::gemm_bf16_stream(x, w, y, M, N, K, out_f32, s);
+  // Direct-to-LDS tile path: 32-bit buffer offsets cover a 256-row tile.
+  if (vec && K < (int64_t{1} << 21)) {
+    const bool vec_out = (N % 4 == 0) && aligned(y, out_f32 ? 16 : 8);
+    return tpl::gemm_bf16_dma(x, w, y, M, N, K, out_f32, vec_out, s, -1);
+  }
   return tpl::gemm_bf16_mfma(x, w, y, M, N, K, out_f32, vec, s, -1);
 }
 
