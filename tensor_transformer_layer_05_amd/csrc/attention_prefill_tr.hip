@@ -1,0 +1,286 @@
+// Prefill attention over a rank's local heads (many query rows), gfx950.
+//
+// Flash-attention structure: a workgroup owns 256 query rows of one q head
+// (8 waves x 32 rows, two waves per SIMD) and walks the key span in tiles of
+// 64 keys with an online softmax, so scores never reach HBM.
+//
+//  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
+//    (A = K rows straight from LDS, B = the wave's Q^T fragments kept in
+//    registers).  A lane then owns one query and 32 of the tile's 64 keys;
+//    the other 32 sit in lane ^ 32, so row statistics are an in-register
+//    reduction plus one v_permlane32_swap.
+//  * The probabilities are already in the B-operand layout of O^T = V^T P^T
+//    (8 keys per lane per 16-key step).  The matching V^T operand comes from
+//    V stored naturally ([key][d]) in LDS through ds_read_b64_tr_b16: within
+//    each 16-lane group, lane s addresses the 4 d of row k0 + s/4 starting at
+//    d0 + 4 (s % 4), and lane j receives V[k0 + e][d0 + j], e = 0..3.
+//  * K and V tiles reach LDS through buffer_load_dwordx4 ... lds (1 KB = 4
+//    key rows per wave-level load), double-buffered, one barrier per tile.
+//    Rows past the key span read as zero through the buffer bound.  LDS rows
+//    are 256 bytes; K's 16-byte chunks are XOR-ed with (key % 16) so that the
+//    16 rows of an A-fragment read hit distinct banks, V's with 4 (key % 4)
+//    so that the 4 rows x 4 chunks of a transposed read do.
+//  * Causal masking is aligned to the end of the key span; tiles entirely
+//    above a wave's last query are skipped by that wave.  Workgroups are
+//    ordered longest first across all heads to balance the causal triangle.
+#include "common.h"
+
+namespace tpl {
+
+namespace {
+
+constexpr int kD = 128;         // head dimension
+constexpr int kBQ = 256;        // query rows per workgroup
+constexpr int kQW = 32;         // query rows per wave
+constexpr int kBK = 64;         // keys per tile
+constexpr int kRowB = kD * 2;   // bytes per K/V row
+constexpr int kTileE = kBK * kD;  // bf16 elements per K (or V) tile
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define TPL_LDS __attribute__((address_space(3)))
+
+struct TrArgs {
+  const uint16_t* q; int64_t qs0, qs1, qs2;
+  const uint16_t* k; const uint16_t* v; int64_t ks0, ks1, ks2;
+  uint16_t* o; int64_t os0, os1, os2;
+  int B, Sq, Skv, Hq, Hkv, causal;
+  float scale_log2;
+};
+
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kTileE];  // [stage][K | V]
+
+  // longest-first over (query block, head, batch)
+  const int nqb = (a.Sq + kBQ - 1) / kBQ;
+  const int hb = a.Hq * a.B;
+  const int id = blockIdx.x;
+  const int qblk = nqb - 1 - id / hb;
+  const int h = (id % hb) % a.Hq, b = (id % hb) / a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int off = a.Skv - a.Sq;
+  const int s0 = qblk * kBQ;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c32 = lane & 31, hl = lane >> 5;
+  const int qw0 = s0 + wave * kQW;
+
+  // Q^T fragments: query qw0 + c32, d = 16 kk + 8 hl .. +7
+  const uint16_t* qbase = a.q + b * a.qs0 + h * a.qs2;
+  bf16x8 qf[8];
+  {
+    const int s = qw0 + c32;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      u32x4 v4 = {0u, 0u, 0u, 0u};
+      if (s < a.Sq) v4 = *reinterpret_cast<const u32x4*>(qbase + (int64_t)s * a.qs1 + kk * 16 + hl * 8);
+      qf[kk] = as_bf16x8(v4);
+    }
+  }
+
+  // key span of the workgroup and of this wave
+  int kv_end = a.Skv;
+  if (a.causal) kv_end = min(a.Skv, min(s0 + kBQ, a.Sq) + off);
+  const int nkt = (kv_end + kBK - 1) / kBK;
+  const int wave_last_key = a.causal ? min(a.Skv - 1, min(qw0 + kQW, a.Sq) - 1 + off) : a.Skv - 1;
+  const bool wave_active = qw0 < a.Sq;
+
+  // DMA tile loads: 4 per wave per tile (2 K, 2 V), each 4 key rows x 256 B.
+  const uint32_t nrec = (uint32_t)(((int64_t)(a.Skv - 1) * a.ks1 + kD) * 2);
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.k + b * a.ks0 + hk * a.ks2), 0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.v + b * a.ks0 + hk * a.ks2), 0, nrec, 0x00020000);
+  const int lr = lane >> 4, lp = lane & 15;   // row within the 4-row load, LDS chunk
+  const uint32_t row_bytes = (uint32_t)(a.ks1 * 2);
+  auto issue = [&](int kt) {
+    const int stage = kt & 1;
+    TPL_LDS uint16_t* kdst = (TPL_LDS uint16_t*)lds + stage * 2 * kTileE;
+    TPL_LDS uint16_t* vdst = kdst + kTileE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (wave * 2 + i) * 4 + lr;           // 0..63 within the tile
+      const int t = kt * kBK + row;
+      const int kc = lp ^ (row & 15), vc = lp ^ (4 * (row & 3));
+      const uint32_t rb = (uint32_t)t * row_bytes;
+      const bool ok = t < a.Skv;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TPL_LDS void*)(kdst + (wave * 2 + i) * 4 * kD), 16,
+                                               ok ? rb + (uint32_t)kc * 16u : 0x80000000u, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TPL_LDS void*)(vdst + (wave * 2 + i) * 4 * kD), 16,
+                                               ok ? rb + (uint32_t)vc * 16u : 0x80000000u, 0, 0, 0);
+    }
+  };
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;
+
+  // transposed-read addressing (per 16-lane group g16 = lane/16): lane s of the
+  // group reads row k0 + s/4, d = d0 + 4 (s % 4) with d0 = 32 db + 16 (g16 & 1)
+  const int g16 = lane >> 4, sidx = lane & 15;
+  const int tr_row = sidx >> 2;                      // + k0
+  const int tr_d = 16 * (g16 & 1) + 4 * (sidx & 3);  // + 32 db
+
+  if (nkt > 0) issue(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 1 < nkt) issue(kt + 1);
+    const int t_first = kt * kBK;
+    const uint16_t* ks = lds + (kt & 1) * 2 * kTileE;
+    const uint16_t* vs = ks + kTileE;
+
+    if (wave_active && t_first <= wave_last_key) {
+      // S^T[key, query] for 2 blocks of 32 keys
+      f32x16 st[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int row = kb * 32 + c32;
+          const int ch = (2 * kk + hl) ^ (row & 15);
+          const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + row * kD + ch * 8));
+          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], st[kb], 0, 0, 0);
+        }
+      }
+
+      // scale into the log2 domain, mask, online softmax for query c32
+      const bool need_mask = (t_first + kBK > a.Skv) ||
+                             (a.causal && t_first + kBK - 1 > qw0 + off);
+      const int qpos = qw0 + c32 + off;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = st[kb][r] * a.scale_log2;
+          if (need_mask) {
+            const int t = t_first + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            if (t >= a.Skv || (a.causal && t > qpos)) x = -INFINITY;
+          }
+          st[kb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = pair_max(mx);
+      const float mnew = fmaxf(mrun, mx);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = exp2f(mrun - muse);
+      mrun = mnew;
+      bf16x8 pb[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = exp2f(st[kb][half * 8 + e] - muse);
+            psum += p[e];
+          }
+          pb[kb * 2 + half] = as_bf16x8(pack8(p));
+        }
+      lrun = lrun * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+      // O^T[d, query] += V^T[d, keys] P^T[keys, query], 16 keys per step.
+      // Step (kb, half) covers keys kb*32 + 16 half + {4 hl + 0..3, 8 + 4 hl + 0..3}.
+#pragma unroll
+      for (int step = 0; step < 4; ++step) {
+        const int k0 = (step >> 1) * 32 + (step & 1) * 16 + 4 * hl;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int d = 32 * db + tr_d;
+          s16x4 lo, hi;
+          {
+            const int row = k0 + tr_row;
+            const int pos = ((d >> 3) ^ (4 * (row & 3))) * 8 + (d & 7);
+            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (TPL_LDS s16x4*)((TPL_LDS uint16_t*)vs + row * kD + pos));
+          }
+          {
+            const int row = k0 + 8 + tr_row;
+            const int pos = ((d >> 3) ^ (4 * (row & 3))) * 8 + (d & 7);
+            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (TPL_LDS s16x4*)((TPL_LDS uint16_t*)vs + row * kD + pos));
+          }
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          const bf16x8 af = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[step], oacc[db], 0, 0, 0);
+        }
+      }
+    }
+
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+
+  // normalise and store O[s, h, d]; lane holds query c32 and, per 32-d block,
+  // d = 8 (r/4) + 4 hl + r%4
+  const float ltot = pair_sum(lrun);
+  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+  const int s = qw0 + c32;
+  if (s < a.Sq) {
+    uint16_t* orow = a.o + b * a.os0 + (int64_t)s * a.os1 + h * a.os2;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int d = db * 32 + grp * 8 + 4 * hl;
+        *reinterpret_cast<u32x2*>(orow + d) =
+            u32x2{pack_bf2(oacc[db][grp * 4 + 0] * inv, oacc[db][grp * 4 + 1] * inv),
+                  pack_bf2(oacc[db][grp * 4 + 2] * inv, oacc[db][grp * 4 + 3] * inv)};
+      }
+  }
+}
+
+// Requires D == 128, key/value row stride >= D, and the key span addressable
+// with 32-bit offsets (checked by the caller).
+tp_status attn_prefill_tr(const void* q, const int64_t qs[3], const void* k, const void* v,
+                          const int64_t kvs[3], void* o, const int64_t os[3], int64_t B,
+                          int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv, int causal, float scale,
+                          hipStream_t s) {
+  TrArgs a;
+  a.q = static_cast<const uint16_t*>(q); a.qs0 = qs[0]; a.qs1 = qs[1]; a.qs2 = qs[2];
+  a.k = static_cast<const uint16_t*>(k); a.v = static_cast<const uint16_t*>(v);
+  a.ks0 = kvs[0]; a.ks1 = kvs[1]; a.ks2 = kvs[2];
+  a.o = static_cast<uint16_t*>(o); a.os0 = os[0]; a.os1 = os[1]; a.os2 = os[2];
+  a.B = (int)B; a.Sq = (int)Sq; a.Skv = (int)Skv; a.Hq = (int)Hq; a.Hkv = (int)Hkv;
+  a.causal = causal;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const int64_t nblk = ((Sq + kBQ - 1) / kBQ) * Hq * B;
+  hipLaunchKernelGGL(attn_prefill_tr_kernel, dim3((unsigned)nblk), dim3(512), 0, s, a);
+  TPL_LAUNCH_CHECK("attn_prefill_tr");
+  return TP_OK;
+}
+
+bool attn_prefill_tr_ok(const int64_t kvs[3], int64_t Skv, int64_t D) {
+  if (D != kD) return false;
+  if (kvs[1] < D) return false;
+  const int64_t span = ((Skv - 1) * kvs[1] + D) * 2;
+  return span < (int64_t{1} << 31);
+}
+
+}  // namespace tpl

@@ -28,6 +28,11 @@ tp_status kv_append(const void* kn, const void* vn, int64_t new_stride, void* kc
 tp_status attn_decode(const void* q, const int64_t qs[3], const void* k, const void* v,
                       const int64_t kvs[3], void* o, const int64_t os[3], int64_t B, int64_t Skv,
                       int64_t Hq, int64_t Hkv, float scale, void* ws, hipStream_t s);
+tp_status attn_prefill_tr(const void* q, const int64_t qs[3], const void* k, const void* v,
+                          const int64_t kvs[3], void* o, const int64_t os[3], int64_t B,
+                          int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv, int causal, float scale,
+                          hipStream_t s);
+bool attn_prefill_tr_ok(const int64_t kvs[3], int64_t Skv, int64_t D);
 size_t attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv);
 tp_status attn_prefill(const void* q, const int64_t qs[3], const void* k, const void* v,
                        const int64_t kvs[3], void* o, const int64_t os[3], int64_t B, int64_t Sq,
@@ -137,6 +142,8 @@ tp_status tp_local_attention(const void* q, const int64_t qs[3], const void* k, 
     if (!aligned(workspace, 16)) return TP_ERR_ALIGN;
     return tpl::attn_decode(q, qs, k, v, kvs, o, os, B, Skv, Hq, Hkv, scale, workspace, s);
   }
+  if (tpl::attn_prefill_tr_ok(kvs, Skv, D) && B * Hq * ((Sq + 255) / 256) <= kIntMax)
+    return tpl::attn_prefill_tr(q, qs, k, v, kvs, o, os, B, Sq, Skv, Hq, Hkv, causal, scale, s);
   return tpl::attn_prefill(q, qs, k, v, kvs, o, os, B, Sq, Skv, Hq, Hkv, causal, scale, s);
 }
 
