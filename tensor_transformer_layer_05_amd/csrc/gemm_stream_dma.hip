@@ -1,0 +1,212 @@
+// Small-M (decode, M <= 64 tokens) bf16 linear through LDS: weight streaming.
+//
+//   Y[m, n] = sum_k X[m, k] * W[n, k]
+//
+// At decode the weight matrix is read once per call and dominates the bytes,
+// so the kernel is built around a coalesced, deeply pipelined weight stream:
+//   * a workgroup owns RT tiles of 16 consecutive weight rows and all of K;
+//     its WAVES waves split K into contiguous 128-k-aligned ranges;
+//   * every wave streams its (16 RT) x krange weight slice through a private
+//     S-stage LDS ring with buffer_load_dwordx4 ... lds: one wave-level load
+//     writes 4 rows x 256 contiguous bytes, so each load instruction is fully
+//     coalesced (the MFMA operand layout, one row per lane, is not);
+//   * the 256-byte LDS rows keep 16-byte chunk c of row r at position
+//     c ^ (r % 16), so the A-fragment reads of v_mfma_f32_16x16x32_bf16 (16
+//     rows x one chunk per quarter-wave) hit 16 distinct bank groups;
+//   * X (the tokens, a few KB resident in L2) comes straight from global
+//     memory as the B operand, one 16-byte buffer load per lane and 32 k;
+//   * out-of-range rows, tokens and k read as zero through the buffer bounds,
+//     so the loop is branch-free and waits for exactly the chunk it uses;
+//   * no workgroup barrier inside the loop (the rings are per wave); the
+//     WAVES partial tiles are summed in LDS in wave order at the end, so the
+//     result does not depend on timing.
+#include "common.h"
+
+namespace tpl {
+
+namespace {
+
+constexpr uint32_t kSOob = 0x80000000u;   // offset past any buffer bound -> reads 0
+#define TPL_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ u32x4 sbload(const __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding)
+#define TPL_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+#define TPL_LGKM0 0xC07F
+
+}  // namespace
+
+template <int WAVES, int MT, int RT, int S, bool OUT_F32>
+__global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
+    int M, int N, int K, int kw) {
+  constexpr int ROWS = 16 * RT;
+  constexpr int STAGE = ROWS * 128;                   // bf16 elements per stage (256 B rows)
+  constexpr int RING = S * STAGE;                      // per wave
+  constexpr int RED = WAVES * RT * MT * 256;           // floats for the final reduction
+  constexpr int LDS_E = (WAVES * RING * 2 > RED * 4) ? WAVES * RING : RED * 2;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_E];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * ROWS;
+  const int g = lane >> 4;         // k-group of this lane inside a 32-k step
+  const int i16 = lane & 15;       // weight row / token inside a 16-tile
+
+  const int wrows = min(ROWS, N - n0);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * K), 0, (uint32_t)wrows * (uint32_t)K * 2u, 0x00020000);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)X, 0, (uint32_t)M * (uint32_t)K * 2u, 0x00020000);
+
+  const int kb = wave * kw;
+  const int ke = min(K, kb + kw);
+  const int nc = ke > kb ? (ke - kb + 127) / 128 : 0;   // 128-k chunks of this wave
+
+  // DMA lane mapping: load d of a chunk covers rows 4d .. 4d+3; lane -> row
+  // 4d + lane/16, LDS chunk position lane%16 holding logical chunk
+  // (lane%16) ^ (row % 16).
+  const int drow = lane >> 4, dpos = lane & 15;
+  TPL_LDS uint16_t* ring = (TPL_LDS uint16_t*)lds + wave * RING;
+  auto issue = [&](int c) {   // chunk c of this wave into stage c % S
+    const int k0 = kb + c * 128;
+    TPL_LDS uint16_t* dst = ring + (c % S) * STAGE;
+#pragma unroll
+    for (int d = 0; d < ROWS / 4; ++d) {
+      const int row = 4 * d + drow;
+      const int k = k0 + 8 * (dpos ^ (row & 15));
+      const uint32_t off = k < ke ? (uint32_t)(row * K + k) * 2u : kSOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (TPL_LDS void*)(dst + d * 4 * 128), 16, off, 0, 0, 0);
+    }
+  };
+
+  f32x4 acc[RT][MT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint32_t xoff[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) xoff[t] = (uint32_t)((t * 16 + i16) * K) * 2u;
+  auto load_x = [&](int c, u32x4 (&xv)[MT][4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = kb + c * 128 + q * 32 + g * 8;
+      const bool ok = k < ke;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) xv[t][q] = sbload(xr, ok ? xoff[t] + (uint32_t)k * 2u : kSOob);
+    }
+  };
+
+  // Memory operations complete in issue order, so each iteration issues the
+  // next chunk's X loads BEFORE the next weight DMA: waiting for X(c) then
+  // leaves the newest DMA in flight.  Chunk c is consumed once DMA(c) and
+  // X(c) have landed:
+  //   c = 0: prologue order DMA(0), X(0), DMA(1..S-2) -> (S-2) DMAs may pend;
+  //   c > 0: order ... X(c), DMA(c+S-2) -> one DMA may pend.
+  // Chunks past the end (odd count, the trailing DMAs) read as zero.
+  constexpr int DPC = ROWS / 4;   // DMA instructions per chunk
+  auto step = [&](int c, const u32x4 (&xv)[MT][4], u32x4 (&xn)[MT][4], bool first) {
+    if (first) __builtin_amdgcn_s_waitcnt(TPL_VMCNT((S - 2) * DPC));
+    else __builtin_amdgcn_s_waitcnt(TPL_VMCNT(DPC));
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* st = lds + wave * RING + (c % S) * STAGE;
+    u32x4 wv[RT][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int row = r * 16 + i16;
+        wv[r][q] = *reinterpret_cast<const u32x4*>(st + row * 128 + ((4 * q + g) ^ (row & 15)) * 8);
+      }
+    load_x(c + 1, xn);
+    issue(c + S - 1);   // refills the stage of chunk c-1, whose reads completed last iteration
+    __builtin_amdgcn_s_waitcnt(TPL_LGKM0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[r][q]), as_bf16x8(xv[t][q]),
+                                                              acc[r][t], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (nc > 0) {
+    u32x4 xa[MT][4], xb[MT][4];
+    issue(0);
+    load_x(0, xa);
+#pragma unroll
+    for (int c = 1; c < S - 1; ++c) issue(c);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int c = 0; c < nc; c += 2) {
+      step(c, xa, xb, c == 0);
+      step(c + 1, xb, xa, false);
+    }
+  }
+  // Drain the trailing (out-of-range) DMA before the LDS is reused.
+  __builtin_amdgcn_s_waitcnt(TPL_VMCNT(0));
+  __syncthreads();
+
+  // 16x16 accumulator layout: lane holds column (token) lane & 15 and rows
+  // (lane >> 4) * 4 + e.  Park every wave's partial in LDS, sum in wave order.
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[(((wave * RT + r) * MT + t) * 64 + lane) * 4 + e] = acc[r][t][e];
+  __syncthreads();
+
+  constexpr int PER = RT * MT * 256;
+  for (int v = threadIdx.x; v < PER; v += WAVES * 64) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) s += red[w * PER + v];
+    const int rt = v / (MT * 256), t = (v / 256) % MT, l = (v >> 2) & 63, e = v & 3;
+    const int m = t * 16 + (l & 15);
+    const int n = n0 + rt * 16 + (l >> 4) * 4 + e;
+    if (m < M && n < N) {
+      if constexpr (OUT_F32)
+        reinterpret_cast<float*>(Y)[(int64_t)m * N + n] = s;
+      else
+        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] = (uint16_t)f2bf_bits(s);
+    }
+  }
+}
+
+template <int WAVES, int MT, int RT, int S>
+static void launch_stream_dma(const void* x, const void* w, void* y, int M, int N, int K, int kw,
+                              bool out_f32, hipStream_t s) {
+  dim3 grid((N + 16 * RT - 1) / (16 * RT)), block(WAVES * 64);
+  auto X = static_cast<const uint16_t*>(x);
+  auto Wp = static_cast<const uint16_t*>(w);
+  if (out_f32)
+    hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, true>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+  else
+    hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, false>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+}
+
+// Requires 33 <= M <= 64, K % 8 == 0, 16-byte aligned X and W, M*K and
+// 32*K elements addressable with 32-bit byte offsets.  Two waves per
+// workgroup, two row tiles per wave, an 8-stage ring (128 KB of LDS).
+tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                               int64_t K, bool out_f32, hipStream_t s) {
+  constexpr int WV = 2;
+  int kw = (int)((K + WV - 1) / WV);
+  kw = (kw + 127) & ~127;
+  const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
+  if (M > 48) launch_stream_dma<WV, 4, 2, 8>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
+  else launch_stream_dma<WV, 3, 2, 8>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
+  TPL_LAUNCH_CHECK("gemm_bf16_stream_dma");
+  return TP_OK;
+}
+
+}  // namespace tpl

@@ -69,7 +69,7 @@ tp_status linear_common(const void* x, const void* w, void* y, int64_t M, int64_
     return tpl::gemm_f32(static_cast<const float*>(x), static_cast<const float*>(w),
                          static_cast<float*>(y), M, N, K, s);
   const bool vec = (K % 8 == 0) && aligned(x, 16) && aligned(w, 16);
-  if (M <= 64 && vec) return tpl::gemm_bf16_stream(x, w, y, M, N, K, out_f32, s);
+  if (M <= 64 && vec && K < (int64_t{1} << 24)) return tpl::gemm_bf16_stream(x, w, y, M, N, K, out_f32, s);
   // Direct-to-LDS tile path: 32-bit buffer offsets cover a 256-row tile.
   if (vec && K < (int64_t{1} << 21)) {
     const bool vec_out = (N % 4 == 0) && aligned(y, out_f32 ? 16 : 8);
