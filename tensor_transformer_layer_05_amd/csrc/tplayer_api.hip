@@ -110,8 +110,7 @@ size_t tp_local_attention_workspace(int64_t B, int64_t Sq, int64_t Skv, int64_t 
                                     int64_t D) {
   if (B <= 0 || Sq <= 0 || Skv <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return 0;
   const int64_t G = Hq / Hkv;
-  if (Sq == 1 && (G == 1 || G == 2 || G == 4 || G == 8))
-    return tpl::attn_decode_workspace(B, Hq, Hkv, Skv);
+  if (Sq == 1 && G <= 32) return tpl::attn_decode_workspace(B, Hq, Hkv, Skv);
   return 0;
 }
 
@@ -135,7 +134,9 @@ tp_status tp_local_attention(const void* q, const int64_t qs[3], const void* k, 
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 8)) return TP_ERR_ALIGN;
   hipStream_t s = as_stream(stream);
   const size_t need = tp_local_attention_workspace(B, Sq, Skv, Hq, Hkv, D);
-  if (Sq == 1 && need == 0 && (Hq / Hkv == 1 || Hq / Hkv == 2 || Hq / Hkv == 4 || Hq / Hkv == 8))
+  // The decode kernel addresses one sequence's key span with 32-bit offsets.
+  if (Sq == 1 && ((Skv - 1) * kvs[1] + D) * 2 >= (int64_t{1} << 31)) return TP_ERR_UNSUPPORTED;
+  if (Sq == 1 && need == 0 && Hq / Hkv <= 32)
     return tpl::attn_decode(q, qs, k, v, kvs, o, os, B, Skv, Hq, Hkv, scale, nullptr, s);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
