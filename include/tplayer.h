@@ -114,9 +114,14 @@ tp_status tp_swiglu_local(const void* gate, const void* up, void* h,
  *   k, v : element (b,t,j,d) at k[b*kvs[0] + t*kvs[1] + j*kvs[2] + d] (same strides)
  *   o : element (b,s,h,d) at o[b*os[0] + s*os[1] + h*os[2] + d]
  *   dt must be TP_BF16; D must be 128 (TP_ERR_UNSUPPORTED otherwise).
+ *   Decode (Sq = 1) with G = Hq/Hkv <= 32 takes a split-key path: one pass
+ *   writes per-chunk partials into the workspace and a second pass combines
+ *   them; it needs ((Skv-1) * kvs[1] + D) * 2 < 2^31 (TP_ERR_UNSUPPORTED
+ *   otherwise).  Other shapes (prefill, or G > 32) need no workspace.
  *   workspace: device scratch of at least tp_local_attention_workspace(...)
  *   bytes (may be NULL when that is 0), owned by the caller, used only during
- *   the call's execution on `stream`.
+ *   the call's execution on `stream`; calls that overlap in time must not
+ *   share one workspace.
  */
 tp_status tp_local_attention(const void* q, const int64_t qs[3],
                              const void* k, const void* v, const int64_t kvs[3],
