@@ -103,6 +103,25 @@ tp_status tp_swiglu_local(const void* gate, const void* up, void* h,
                           tp_act act, tp_dtype dt, void* stream);
 
 /*
+ * Column-parallel linear with the rank-local activation fused into its
+ * epilogue (P1 "MLP 里的 tensor parallel": gate_i and up_i are both local to
+ * rank i, so activation(gate_i) * up_i needs no exchange; P2 section 二: GELU
+ * directly after the column-parallel fc1).  The result equals tp_column_linear
+ * followed by tp_swiglu_local bit for bit (the products are rounded to bf16
+ * before the activation, as the unfused path stores them), without writing
+ * the [M, 2I] gate|up intermediate:
+ *     TP_ACT_SWIGLU: h[m, i] = act(x . w[i, :], x . w[I + i, :])   w: [2I, K]
+ *                    (gate rows, then the matching up rows)
+ *     TP_ACT_GELU:   h[m, i] = gelu(x . w[i, :])                    w: [I, K]
+ *     TP_ACT_NONE:   same as tp_column_linear (N = I)
+ *   x : [M, K], h : [M, I] contiguous.  dt must be TP_BF16 for SWIGLU/GELU;
+ *   K % 8 == 0 and 16-byte aligned x and w (TP_ERR_UNSUPPORTED otherwise).
+ */
+tp_status tp_column_linear_act(const void* x, const void* w, void* h,
+                               int64_t M, int64_t K, int64_t I,
+                               tp_act act, tp_dtype dt, void* stream);
+
+/*
  * Attention over the rank's local heads (P1 "Attention 里的 tensor parallel":
  * each rank attends only over its own heads and keeps their KV; P2 2.1).
  * Grouped KV heads (P3 "权重变小，不代表所有显存都按比例变小"): local q head h
@@ -163,6 +182,21 @@ tp_status tp_kv_append(const void* k_new, const void* v_new, int64_t new_stride,
 tp_status tp_reduce_partials(const float* const* partials, int64_t R,
                              const void* residual, void* y,
                              int64_t M, int64_t N, tp_dtype out_dt, void* stream);
+
+/*
+ * The all-reduce's arithmetic followed by the next sub-block's pre-norm, in
+ * one pass (P2 section 二 all_reduce(output) + the residual; the RMSNorm is
+ * the standard pre-norm of a decoder layer, not on the source pages):
+ *     y  = (residual if residual) + sum_{r=0}^{R-1} partials[r]   (as tp_reduce_partials)
+ *     yn = y * rsqrt(mean_n y^2 + eps) * gamma                   (as tp_rmsnorm on the stored y)
+ * Both outputs equal the two unfused calls bit for bit.
+ *   partials : host array of R device pointers to [M, N] float32 buffers
+ *   residual : [M, N] dt or NULL;  y, yn : [M, N] dt (y may alias residual);
+ *   gamma : [N] dt;  1 <= R <= 16
+ */
+tp_status tp_reduce_partials_rmsnorm(const float* const* partials, int64_t R,
+                                     const void* residual, void* y, const void* gamma, void* yn,
+                                     int64_t M, int64_t N, float eps, tp_dtype dt, void* stream);
 
 /*
  * Replicated pre-norm RMSNorm (every rank normalises the full hidden row):

@@ -8,8 +8,9 @@ the computation runs in the library's kernels; there is no CPU or torch
 fallback -- if the library is missing the calls raise.
 
 Entry points (same names as the C ABI, without the ``tp_`` prefix):
-``column_linear``, ``row_linear_partial``, ``swiglu_local``,
-``local_attention``, ``kv_append``, ``reduce_partials``, ``rmsnorm``.
+``column_linear``, ``column_linear_act``, ``row_linear_partial``,
+``swiglu_local``, ``local_attention``, ``kv_append``, ``reduce_partials``,
+``reduce_partials_rmsnorm``, ``rmsnorm``.
 Weights use the nn.Linear layout ``[out_features, in_features]``.
 """
 from __future__ import annotations
@@ -21,8 +22,9 @@ import torch
 
 __all__ = [
     "lib", "library_path", "TPError",
-    "column_linear", "row_linear_partial", "swiglu_local", "local_attention",
-    "local_attention_workspace", "kv_append", "reduce_partials", "rmsnorm",
+    "column_linear", "column_linear_act", "row_linear_partial", "swiglu_local",
+    "local_attention", "local_attention_workspace", "kv_append", "reduce_partials",
+    "reduce_partials_rmsnorm", "rmsnorm",
     "shard_column", "shard_row", "shard_qkv",
     "F32", "BF16", "ACT_NONE", "ACT_SWIGLU", "ACT_GELU",
 ]
@@ -43,6 +45,8 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 
 _SIGS = {
     "tp_column_linear": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp]),
+    "tp_column_linear_act": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int,
+                                            ctypes.c_int, _vp]),
     "tp_row_linear_partial": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp]),
     "tp_swiglu_local": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]),
     "tp_local_attention": (ctypes.c_int, [_vp, _i64p, _vp, _vp, _i64p, _vp, _i64p, _i64, _i64, _i64,
@@ -53,6 +57,8 @@ _SIGS = {
                                     ctypes.c_int, _vp]),
     "tp_reduce_partials": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, _vp, _vp, _i64, _i64,
                                           ctypes.c_int, _vp]),
+    "tp_reduce_partials_rmsnorm": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, _vp, _vp, _vp, _vp,
+                                                  _i64, _i64, ctypes.c_float, ctypes.c_int, _vp]),
     "tp_rmsnorm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, ctypes.c_float, ctypes.c_int, _vp]),
     "tp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -133,6 +139,33 @@ def column_linear(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = N
     _contig(out, "out")
     _check("tp_column_linear", lib().tp_column_linear(x.data_ptr(), w.data_ptr(), out.data_ptr(),
                                                       M, K, N, _DT[x.dtype], _stream(x)))
+    return out
+
+
+def column_linear_act(x: torch.Tensor, w: torch.Tensor, act: str = "swiglu",
+                      out: torch.Tensor | None = None):
+    """Column-parallel linear with the rank-local activation in its epilogue.
+    swiglu: w ``[2I, K]`` (gate rows then up rows) -> ``[M, I]``;
+    gelu: w ``[I, K]`` -> ``[M, I]``.  Equals ``column_linear`` followed by
+    ``swiglu_local`` bit for bit, without the ``[M, 2I]`` intermediate."""
+    _contig(x, "x"); _contig(w, "w")
+    M, K = x.shape
+    a = _act(act)
+    if w.dim() != 2 or w.shape[1] != K or w.dtype != x.dtype:
+        raise ValueError("w must be [N, K] with the dtype of x")
+    if a == ACT_SWIGLU:
+        if w.shape[0] % 2:
+            raise ValueError("swiglu needs a [2I, K] gate|up weight")
+        I_ = w.shape[0] // 2
+    else:
+        I_ = w.shape[0]
+    if out is None:
+        out = torch.empty((M, I_), dtype=x.dtype, device=x.device)
+    _contig(out, "out")
+    if out.shape != (M, I_) or out.dtype != x.dtype:
+        raise ValueError("out must be [M, I] with the dtype of x")
+    _check("tp_column_linear_act", lib().tp_column_linear_act(
+        x.data_ptr(), w.data_ptr(), out.data_ptr(), M, K, I_, a, _DT[x.dtype], _stream(x)))
     return out
 
 
@@ -265,6 +298,43 @@ def reduce_partials(partials, residual: torch.Tensor | None = None, out: torch.T
         arr, len(parts), residual.data_ptr() if residual is not None else None, out.data_ptr(),
         M, N, _DT[out.dtype], _stream(parts[0])))
     return out
+
+
+def reduce_partials_rmsnorm(partials, gamma: torch.Tensor, residual: torch.Tensor | None = None,
+                            eps: float = 1e-5, out: torch.Tensor | None = None,
+                            out_norm: torch.Tensor | None = None):
+    """``y = residual + sum_r partials[r]`` (as ``reduce_partials``) and
+    ``yn = rmsnorm(y) * gamma`` (as ``rmsnorm`` on the stored y) in one pass.
+    Returns ``(y, yn)`` in gamma's dtype."""
+    parts = list(partials)
+    if not parts:
+        raise ValueError("need at least one partial")
+    for i, p in enumerate(parts):
+        _contig(p, f"partials[{i}]")
+        if p.dtype != torch.float32 or p.shape != parts[0].shape:
+            raise ValueError("partials must be float32 tensors of one shape")
+    M, N = parts[0].shape
+    _contig(gamma, "gamma")
+    dt = gamma.dtype
+    if gamma.shape != (N,):
+        raise ValueError("gamma must be [N]")
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=parts[0].device)
+    if out_norm is None:
+        out_norm = torch.empty((M, N), dtype=dt, device=parts[0].device)
+    for t, n in ((out, "out"), (out_norm, "out_norm")):
+        _contig(t, n)
+        if t.dtype != dt or t.shape != (M, N):
+            raise ValueError(f"{n} must be [M, N] with gamma's dtype")
+    if residual is not None:
+        _contig(residual, "residual")
+        if residual.dtype != dt or residual.shape != (M, N):
+            raise ValueError("residual must be [M, N] with gamma's dtype")
+    arr = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    _check("tp_reduce_partials_rmsnorm", lib().tp_reduce_partials_rmsnorm(
+        arr, len(parts), residual.data_ptr() if residual is not None else None, out.data_ptr(),
+        gamma.data_ptr(), out_norm.data_ptr(), M, N, float(eps), _DT[dt], _stream(parts[0])))
+    return out, out_norm
 
 
 def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, out: torch.Tensor | None = None):

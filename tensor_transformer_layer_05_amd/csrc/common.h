@@ -51,6 +51,18 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// ---- rank-local activation (shared by the elementwise kernel and the fused
+// GEMM epilogues, so both round and evaluate identically) --------------------
+
+template <int ACT>
+__device__ __forceinline__ float act_fn(float g, float u) {
+  if constexpr (ACT == TP_ACT_SWIGLU) return g / (1.0f + expf(-g)) * u;
+  // GELU(g) = g * Phi(g) with Phi(g) = erfc(-g / sqrt 2) / 2: the erfc form
+  // keeps full relative accuracy for negative g, where 1 + erf(.) cancels.
+  else if constexpr (ACT == TP_ACT_GELU) return 0.5f * g * erfcf(-g * 0.70710678118654752f);
+  else return g;
+}
+
 // ---- wave reductions ---------------------------------------------------------
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -8,15 +8,6 @@ namespace tpl {
 
 // ---- activation ------------------------------------------------------------
 
-template <int ACT>
-__device__ __forceinline__ float act_fn(float g, float u) {
-  if constexpr (ACT == TP_ACT_SWIGLU) return g / (1.0f + expf(-g)) * u;
-  // GELU(g) = g * Phi(g) with Phi(g) = erfc(-g / sqrt 2) / 2: the erfc form
-  // keeps full relative accuracy for negative g, where 1 + erf(.) cancels.
-  else if constexpr (ACT == TP_ACT_GELU) return 0.5f * g * erfcf(-g * 0.70710678118654752f);
-  else return g;
-}
-
 // One thread per 8 consecutive outputs of a row (vector path).
 template <int ACT, bool BF16>
 __global__ __launch_bounds__(256) void act_vec_kernel(const void* __restrict__ gate,
@@ -238,6 +229,74 @@ tp_status rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t 
     hipLaunchKernelGGL((rmsnorm_kernel<false, false>), grid, block, 0, s, x, gamma, y, N, eps);
   }
   TPL_LAUNCH_CHECK("rmsnorm");
+  return TP_OK;
+}
+
+// ---- sum of rank partials + residual, then RMSNorm (fused) ------------------------
+
+// One 256-thread workgroup per row, bf16 storage, N % 8 == 0, 16-byte aligned
+// rows.  Pass 1 forms h = residual + sum_r partials[r] exactly as reduce_kernel
+// does (fp32, rank order, residual last, RNE to bf16), stores it and
+// accumulates the squares of the stored bf16 values in rmsnorm_kernel's order;
+// pass 2 re-reads this thread's own h values (still in L2) and normalises them
+// exactly as rmsnorm_kernel does.  So y and yn equal the two unfused calls bit
+// for bit, with one launch and one less pass over h in HBM.
+__global__ __launch_bounds__(256) void reduce_rmsnorm_kernel(PartialPtrs P, int R,
+                                                             const uint16_t* residual,
+                                                             uint16_t* y,   // may alias residual
+                                                             const uint16_t* __restrict__ gamma,
+                                                             uint16_t* __restrict__ yn, int64_t N,
+                                                             float eps) {
+  __shared__ float wsum[4];
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x;
+  float ss = 0.f;
+  for (int64_t c = tid * 8; c < N; c += 256 * 8) {
+    const int64_t o = m * N + c;
+    float h[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      f32x4 acc = *reinterpret_cast<const f32x4*>(P.p[0] + o + 4 * half);
+      for (int r = 1; r < R; ++r) acc += *reinterpret_cast<const f32x4*>(P.p[r] + o + 4 * half);
+      if (residual) {
+        const u32x2 rv = *reinterpret_cast<const u32x2*>(residual + o + 4 * half);
+        acc[0] += bf_lo(rv[0]); acc[1] += bf_hi(rv[0]);
+        acc[2] += bf_lo(rv[1]); acc[3] += bf_hi(rv[1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[4 * half + i] = acc[i];
+    }
+    const u32x4 hb = pack8(h);
+    *reinterpret_cast<u32x4*>(y + o) = hb;
+    float f[8];
+    unpack8(hb, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  const float inv = rsqrtf(tot / (float)N + eps);
+  for (int64_t c = tid * 8; c < N; c += 256 * 8) {
+    float f[8], gm[8], o[8];
+    unpack8(*reinterpret_cast<const u32x4*>(y + m * N + c), f);
+    unpack8(*reinterpret_cast<const u32x4*>(gamma + c), gm);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = f[i] * inv * gm[i];
+    *reinterpret_cast<u32x4*>(yn + m * N + c) = pack8(o);
+  }
+}
+
+tp_status reduce_rmsnorm(const float* const* partials, int R, const void* residual, void* y,
+                         const void* gamma, void* yn, int64_t M, int64_t N, float eps,
+                         hipStream_t s) {
+  PartialPtrs P = {};
+  for (int r = 0; r < R; ++r) P.p[r] = partials[r];
+  hipLaunchKernelGGL(reduce_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, s, P, R,
+                     static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(y),
+                     static_cast<const uint16_t*>(gamma), static_cast<uint16_t*>(yn), N, eps);
+  TPL_LAUNCH_CHECK("reduce_rmsnorm");
   return TP_OK;
 }
 

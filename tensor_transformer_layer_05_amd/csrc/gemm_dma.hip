@@ -52,14 +52,21 @@ struct DmaTile {
 
 __device__ __forceinline__ int dswz(int row, int kc) { return kc ^ ((row >> 1) & 7); }
 
-template <class C, bool OUT_F32, bool VEC_OUT>
+// EPI: 0 = plain product; 1 = SwiGLU on a paired tile (W rows [0, I) gate,
+// [I, 2I) up; the tile's first BN/2 W rows are gate rows n0.., the rest the
+// matching up rows; output [M, I]); 2 = GELU on each output.  The fused
+// epilogues round the products to bf16 first, exactly as the unfused path
+// stores them before the activation kernel reads them.
+template <class C, bool OUT_F32, bool VEC_OUT, int EPI>
 __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
     int M, int N, int K) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
+  // SwiGLU: N is the intermediate size I, each tile covers BN/2 outputs.
+  constexpr int OUT_BN = EPI == 1 ? C::BN / 2 : C::BN;
 
   const int tiles_m = (M + C::BM - 1) / C::BM;
-  const int tiles_n = (N + C::BN - 1) / C::BN;
+  const int tiles_n = (N + OUT_BN - 1) / OUT_BN;
   const int ntile = tiles_m * tiles_n;
   const int pid = xcd_remap(blockIdx.x, ntile);
   constexpr int GROUP_M = 8;
@@ -68,18 +75,24 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   const int gsize = min(tiles_m - first_m, GROUP_M);
   const int tm = first_m + (pid % in_group) % gsize;
   const int tn = (pid % in_group) / gsize;
-  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int m0 = tm * C::BM, n0 = tn * OUT_BN;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
 
   // Buffer resources based at the tile's first row, bounded to its valid rows.
-  const uint32_t xrows = (uint32_t)min(C::BM, M - m0), wrows = (uint32_t)min(C::BN, N - n0);
+  // SwiGLU: the waves loading W-tile rows [BN/2, BN) read the up rows I + n0..
+  // (the split is wave-uniform: a wave's loads cover WL*8 consecutive rows).
+  const uint32_t xrows = (uint32_t)min(C::BM, M - m0);
+  const bool up_rows = EPI == 1 && wave * C::WL * 8 >= C::BN / 2;
+  const uint32_t wrows = (uint32_t)min(OUT_BN, N - n0);
+  const int wbase = up_rows ? N + n0 : n0;
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(X + (int64_t)m0 * K), 0, xrows * (uint32_t)K * 2u, 0x00020000);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (int64_t)n0 * K), 0, wrows * (uint32_t)K * 2u, 0x00020000);
+      (void*)(W + (int64_t)wbase * K), 0, wrows * (uint32_t)K * 2u, 0x00020000);
+  const int wrow_shift = up_rows ? C::BN / 2 : 0;   // W-tile row -> row of the resource
 
   // Load i of this wave fills LDS rows (wave*L + i)*8 .. +7; lane -> row lane/8,
   // LDS chunk lane%8, which holds global chunk dswz(row, lane%8).
@@ -96,7 +109,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   for (int i = 0; i < C::WL; ++i) {
     const int row = (wave * C::WL + i) * 8 + lrow;
     wk[i] = 8 * dswz(row, lpos);
-    woff[i] = (uint32_t)(row * K + wk[i]) * 2u;
+    woff[i] = (uint32_t)((row - wrow_shift) * K + wk[i]) * 2u;
   }
   auto load_x = [&](int k0, int stage) {
     TPL_LDS uint16_t* base = (TPL_LDS uint16_t*)lds + stage * C::STAGE;
@@ -190,6 +203,56 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
 
   // Epilogue.  acc[i][j] lane holds token m = wm*TM + 32j + (lane&31) and
   // features n = wn*TN + 32i + 8*(r/4) + 4*(lane/32) + r%4, r = 0..15.
+  if constexpr (EPI == 1) {
+    // Up-row waves (wn >= WN/2) park their accumulators in LDS; the gate-row
+    // wave with the same lane layout (wn - WN/2) combines them.
+    constexpr int PER_WAVE = C::FA * C::FB * 16 * 64;   // floats
+    float* xch = reinterpret_cast<float*>(lds);
+    static_assert((C::NW / 2) * PER_WAVE * 4 <= 2 * C::STAGE * 2, "exchange fits in the stages");
+    __syncthreads();
+    const int pair = wm * (C::WN / 2) + (wn % (C::WN / 2));
+    if (wn >= C::WN / 2) {
+#pragma unroll
+      for (int i = 0; i < C::FA; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            xch[pair * PER_WAVE + ((i * C::FB + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (wn < C::WN / 2) {
+#pragma unroll
+      for (int i = 0; i < C::FA; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::FB; ++j) {
+          const int m = m0 + wm * C::TM + j * 32 + frow;
+          if (m >= M) continue;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn * C::TN + i * 32 + 8 * q + 4 * fh;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float g = bf2f((uint16_t)f2bf_bits(acc[i][j][4 * q + e]));
+              const float u = bf2f((uint16_t)f2bf_bits(
+                  xch[pair * PER_WAVE + ((i * C::FB + j) * 16 + 4 * q + e) * 64 + lane]));
+              v[e] = act_fn<TP_ACT_SWIGLU>(g, u);
+            }
+            if (VEC_OUT && n + 3 < N) {
+              *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(Y) + (int64_t)m * N + n) =
+                  u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (n + e < N) reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n + e] = (uint16_t)f2bf_bits(v[e]);
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < C::FA; ++i) {
 #pragma unroll
@@ -199,8 +262,12 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + wn * C::TN + i * 32 + 8 * q + 4 * fh;
-        const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                            acc[i][j][4 * q + 3]};
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                      acc[i][j][4 * q + 3]};
+        if constexpr (EPI == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = act_fn<TP_ACT_GELU>(bf2f((uint16_t)f2bf_bits(v[e])), 0.f);
+        }
         if (VEC_OUT && n + 3 < N) {
           if constexpr (OUT_F32) {
             const f32x4 o = {v[0], v[1], v[2], v[3]};
@@ -228,19 +295,25 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
 using Dma256 = DmaTile<256, 256, 2, 4>;   // 8 waves, one workgroup per CU
 using Dma128 = DmaTile<128, 128, 2, 2>;   // 4 waves, two workgroups per CU
 
-template <class C>
+template <class C, int EPI>
 static tp_status launch_dma(const void* x, const void* w, void* y, int M, int N, int K,
                             bool out_f32, bool vec_out, hipStream_t s) {
-  const int ntile = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  constexpr int OUT_BN = EPI == 1 ? C::BN / 2 : C::BN;
+  const int ntile = ((M + C::BM - 1) / C::BM) * ((N + OUT_BN - 1) / OUT_BN);
   dim3 grid(ntile), block(C::NT);
   auto X = static_cast<const uint16_t*>(x);
   auto Wp = static_cast<const uint16_t*>(w);
-  if (out_f32) {
-    if (vec_out) hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, true, true>), grid, block, 0, s, X, Wp, y, M, N, K);
-    else hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, true, false>), grid, block, 0, s, X, Wp, y, M, N, K);
+  if constexpr (EPI == 0) {
+    if (out_f32) {
+      if (vec_out) hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, true, true, 0>), grid, block, 0, s, X, Wp, y, M, N, K);
+      else hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, true, false, 0>), grid, block, 0, s, X, Wp, y, M, N, K);
+    } else {
+      if (vec_out) hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, false, true, 0>), grid, block, 0, s, X, Wp, y, M, N, K);
+      else hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, false, false, 0>), grid, block, 0, s, X, Wp, y, M, N, K);
+    }
   } else {
-    if (vec_out) hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, false, true>), grid, block, 0, s, X, Wp, y, M, N, K);
-    else hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, false, false>), grid, block, 0, s, X, Wp, y, M, N, K);
+    if (vec_out) hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, false, true, EPI>), grid, block, 0, s, X, Wp, y, M, N, K);
+    else hipLaunchKernelGGL((gemm_bf16_dma_kernel<C, false, false, EPI>), grid, block, 0, s, X, Wp, y, M, N, K);
   }
   TPL_LAUNCH_CHECK("gemm_bf16_dma");
   return TP_OK;
@@ -260,8 +333,24 @@ int gemm_dma_pick_tile(int M, int N) {
 tp_status gemm_bf16_dma(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                         bool out_f32, bool vec_out, hipStream_t s, int force_tile) {
   const int pick = force_tile >= 0 ? force_tile : gemm_dma_pick_tile((int)M, (int)N);
-  if (pick == 0) return launch_dma<Dma256>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
-  return launch_dma<Dma128>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
+  if (pick == 0) return launch_dma<Dma256, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
+  return launch_dma<Dma128, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
+}
+
+// Column-parallel linear with the rank-local activation fused into the
+// epilogue, bf16 output [M, I]: act = TP_ACT_SWIGLU (w is [2I, K], gate rows
+// then up rows) or TP_ACT_GELU (w is [I, K]).  Same requirements as above.
+tp_status gemm_bf16_dma_act(const void* x, const void* w, void* h, int64_t M, int64_t I, int64_t K,
+                            int act, bool vec_out, hipStream_t s) {
+  if (act == TP_ACT_SWIGLU) {
+    // a paired 256-wide tile yields 128 outputs: pick the tile on the doubled width
+    const int pick = gemm_dma_pick_tile((int)M, (int)(2 * I));
+    if (pick == 0) return launch_dma<Dma256, 1>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
+    return launch_dma<Dma128, 1>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
+  }
+  const int pick = gemm_dma_pick_tile((int)M, (int)I);
+  if (pick == 0) return launch_dma<Dma256, 2>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
+  return launch_dma<Dma128, 2>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
 }
 
 }  // namespace tpl

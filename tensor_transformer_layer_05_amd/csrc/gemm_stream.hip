@@ -31,21 +31,33 @@ __device__ __forceinline__ u32x4 bload(const __amdgpu_buffer_rsrc_t r, uint32_t 
 
 }  // namespace
 
-template <int WAVES, int MT, int RT, bool OUT_F32>
+// EPI: 0 = plain product; 1 = SwiGLU (RT = 2: row tile 0 = gate rows n0..,
+// tile 1 = the matching up rows N + n0.. of a [2N, K] weight; output [M, N]);
+// 2 = GELU on each output.  Fused epilogues round the sums to bf16 before the
+// activation, exactly as the unfused path stores them.
+template <int WAVES, int MT, int RT, bool OUT_F32, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
     int M, int N, int K, int kw) {
   __shared__ float red[WAVES * RT * MT * 256];
+  static_assert(EPI != 1 || RT == 2, "SwiGLU pairs a gate and an up row tile");
+  constexpr int OUT_ROWS = EPI == 1 ? 16 : 16 * RT;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * 16 * RT;
+  const int n0 = blockIdx.x * OUT_ROWS;
   const int g = lane >> 4;         // k-group of this lane inside a 32-k step
   const int i16 = lane & 15;       // weight row / token inside a 16-tile
 
-  const int wrows = min(16 * RT, N - n0);
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (int64_t)n0 * K), 0, (uint32_t)wrows * (uint32_t)K * 2u, 0x00020000);
+  // one resource per row tile, based at its first row and bounded to its valid rows
+  __amdgpu_buffer_rsrc_t wr[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int base = EPI == 1 ? (r == 0 ? n0 : N + n0) : n0 + 16 * r;
+    const int rows = EPI == 1 ? min(16, N - n0) : max(0, min(16, N - n0 - 16 * r));
+    wr[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)base * K), 0,
+                                              (uint32_t)rows * (uint32_t)K * 2u, 0x00020000);
+  }
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)X, 0, (uint32_t)M * (uint32_t)K * 2u, 0x00020000);
 
@@ -55,7 +67,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
 
   uint32_t woff[RT], xoff[MT];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) woff[r] = (uint32_t)((r * 16 + i16) * K) * 2u;
+  for (int r = 0; r < RT; ++r) woff[r] = (uint32_t)(i16 * K) * 2u;
 #pragma unroll
   for (int t = 0; t < MT; ++t) xoff[t] = (uint32_t)((t * 16 + i16) * K) * 2u;
 
@@ -73,7 +85,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
       const bool ok = k < ke;
       const uint32_t kbytes = (uint32_t)k * 2u;
 #pragma unroll
-      for (int r = 0; r < RT; ++r) wv[r][j] = bload(wr, ok ? woff[r] + kbytes : kOob);
+      for (int r = 0; r < RT; ++r) wv[r][j] = bload(wr[r], ok ? woff[r] + kbytes : kOob);
 #pragma unroll
       for (int t = 0; t < MT; ++t) xv[t][j] = bload(xr, ok ? xoff[t] + kbytes : kOob);
     }
@@ -120,6 +132,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
   __syncthreads();
 
   constexpr int PER = RT * MT * 256;
+  if constexpr (EPI == 1) {
+    for (int v = threadIdx.x; v < MT * 256; v += WAVES * 64) {
+      float sg = 0.f, su = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) { sg += red[w * PER + v]; su += red[w * PER + MT * 256 + v]; }
+      const int t = v / 256, l = (v >> 2) & 63, e = v & 3;
+      const int m = t * 16 + (l & 15);
+      const int n = n0 + (l >> 4) * 4 + e;
+      if (m < M && n < N)
+        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] = (uint16_t)f2bf_bits(
+            act_fn<TP_ACT_SWIGLU>(bf2f((uint16_t)f2bf_bits(sg)), bf2f((uint16_t)f2bf_bits(su))));
+    }
+    return;
+  }
   for (int v = threadIdx.x; v < PER; v += WAVES * 64) {
     float s = 0.f;
 #pragma unroll
@@ -128,7 +154,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
     const int m = t * 16 + (l & 15);
     const int n = n0 + rt * 16 + (l >> 4) * 4 + e;
     if (m < M && n < N) {
-      if constexpr (OUT_F32)
+      if constexpr (EPI == 2)
+        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] =
+            (uint16_t)f2bf_bits(act_fn<TP_ACT_GELU>(bf2f((uint16_t)f2bf_bits(s)), 0.f));
+      else if constexpr (OUT_F32)
         reinterpret_cast<float*>(Y)[(int64_t)m * N + n] = s;
       else
         reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] = (uint16_t)f2bf_bits(s);
@@ -136,22 +165,45 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
   }
 }
 
-template <int WAVES, int MT, int RT>
+template <int WAVES, int MT, int RT, int EPI = 0>
 static void launch_stream(const void* x, const void* w, void* y, int M, int N, int K, int kw,
                           bool out_f32, hipStream_t s) {
-  dim3 grid((N + 16 * RT - 1) / (16 * RT)), block(WAVES * 64);
+  constexpr int OUT_ROWS = EPI == 1 ? 16 : 16 * RT;
+  dim3 grid((N + OUT_ROWS - 1) / OUT_ROWS), block(WAVES * 64);
   auto X = static_cast<const uint16_t*>(x);
   auto Wp = static_cast<const uint16_t*>(w);
-  if (out_f32)
-    hipLaunchKernelGGL((gemm_stream_kernel<WAVES, MT, RT, true>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
-  else
-    hipLaunchKernelGGL((gemm_stream_kernel<WAVES, MT, RT, false>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+  if constexpr (EPI == 0) {
+    if (out_f32)
+      hipLaunchKernelGGL((gemm_stream_kernel<WAVES, MT, RT, true, 0>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+    else
+      hipLaunchKernelGGL((gemm_stream_kernel<WAVES, MT, RT, false, 0>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+  } else {
+    hipLaunchKernelGGL((gemm_stream_kernel<WAVES, MT, RT, false, EPI>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+  }
 }
 
-// Requires 1 <= M <= 64 (M > 32 goes to the LDS-ring kernel), K % 8 == 0, 16-byte aligned X and W, M*K and
-// 32*K elements addressable with 32-bit byte offsets.
 tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M, int64_t N,
                                int64_t K, bool out_f32, hipStream_t s);
+
+// Waves per workgroup of the decode linear on an [N, K] weight: split K so
+// that every wave streams >= 256 k; 16 waves (1024 threads, <= 128 VGPRs
+// each) only for the lightest register footprints and when there are few row
+// tiles to spread over the chip.  The fused-activation variant takes the same
+// split (hence the same float sums) as the plain linear on the full weight.
+static int stream_row_tiles(int mt, int64_t N) { return (mt >= 2 && N >= 16 * 2 * 224) ? 2 : 1; }
+
+static int stream_waves(int mt, int64_t N, int64_t K) {
+  const int rt = stream_row_tiles(mt, N);
+  const int64_t nblk = (N + 16 * rt - 1) / (16 * rt);
+  int waves = (nblk < 384 && mt * rt <= 2) ? 16 : 8;
+  while (waves > 4 && K / waves < 256) waves >>= 1;
+  return waves;
+}
+
+static int stream_kw(int64_t K, int waves) {
+  int kw = (int)((K + waves - 1) / waves);
+  return (kw + 31) & ~31;
+}
 
 tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                            bool out_f32, hipStream_t s) {
@@ -161,15 +213,9 @@ tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int
   if (mt >= 3) return gemm_bf16_stream_dma(x, w, y, M, N, K, out_f32, s);
   // Two row tiles per wave when there are several token tiles (each X
   // fragment then feeds two MFMAs) and enough row tiles to fill the chip.
-  const int rt = (mt >= 2 && N >= 16 * 2 * 224) ? 2 : 1;
-  const int64_t nblk = (N + 16 * rt - 1) / (16 * rt);
-  // Waves per workgroup: split K so that every wave streams >= 256 k; 16
-  // waves (1024 threads, <= 128 VGPRs each) only for the lightest register
-  // footprints and when there are few row tiles to spread over the chip.
-  int waves = (nblk < 384 && mt * rt <= 2) ? 16 : 8;
-  while (waves > 4 && K / waves < 256) waves >>= 1;
-  int kw = (int)((K + waves - 1) / waves);
-  kw = (kw + 31) & ~31;
+  const int rt = stream_row_tiles(mt, N);
+  const int waves = stream_waves(mt, N, K);
+  const int kw = stream_kw(K, waves);
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
 #define TPL_STREAM(WV, MTV, RTV) launch_stream<WV, MTV, RTV>(x, w, y, Mi, Ni, Ki, kw, out_f32, s)
 #define TPL_STREAM_MT(WV, RTV)                  \
@@ -187,6 +233,40 @@ tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int
 #undef TPL_STREAM_MT
 #undef TPL_STREAM
   TPL_LAUNCH_CHECK("gemm_bf16_stream");
+  return TP_OK;
+}
+
+tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
+                                   int64_t K, int act, hipStream_t s);
+
+// Decode linear with the rank-local activation fused (bf16 output [M, I]):
+// act = TP_ACT_SWIGLU (w is [2I, K], gate rows then up rows) or TP_ACT_GELU
+// (w is [I, K]).  Same requirements as gemm_bf16_stream; the K split is the
+// one gemm_bf16_stream takes on the same weight, so the results equal the
+// plain linear followed by the activation bit for bit.
+tp_status gemm_bf16_stream_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
+                               int64_t K, int act, hipStream_t s) {
+  const int mt = (int)((M + 15) / 16);
+  if (mt >= 3) return gemm_bf16_stream_dma_act(x, w, h, M, I, K, act, s);
+  const int waves = stream_waves(mt, act == TP_ACT_SWIGLU ? 2 * I : I, K);
+  const int kw = stream_kw(K, waves);
+  const int Mi = (int)M, Ii = (int)I, Ki = (int)K;
+#define TPL_SACT(WV, MTV)                                                                      \
+  do {                                                                                         \
+    if (act == TP_ACT_SWIGLU) launch_stream<WV, MTV, 2, 1>(x, w, h, Mi, Ii, Ki, kw, false, s); \
+    else launch_stream<WV, MTV, 1, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);                     \
+  } while (0)
+#define TPL_SACT_MT(WV)                 \
+  do {                                  \
+    if (mt == 1) TPL_SACT(WV, 1);       \
+    else TPL_SACT(WV, 2);               \
+  } while (0)
+  if (waves == 16) TPL_SACT_MT(16);
+  else if (waves == 8) TPL_SACT_MT(8);
+  else TPL_SACT_MT(4);
+#undef TPL_SACT_MT
+#undef TPL_SACT
+  TPL_LAUNCH_CHECK("gemm_bf16_stream_act");
   return TP_OK;
 }
 

@@ -39,10 +39,15 @@ __device__ __forceinline__ u32x4 sbload(const __amdgpu_buffer_rsrc_t r, uint32_t
 
 }  // namespace
 
-template <int WAVES, int MT, int RT, int S, bool OUT_F32>
+// EPI as in gemm_stream_kernel: 0 plain, 1 SwiGLU (RT = 2: gate tile + the
+// matching up tile of a [2N, K] weight, output [M, N]), 2 GELU.
+template <int WAVES, int MT, int RT, int S, bool OUT_F32, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
     int M, int N, int K, int kw) {
+  static_assert(EPI != 1 || RT == 2, "SwiGLU pairs a gate and an up row tile");
+  static_assert(RT == 1 || RT == 2, "one or two row tiles");
+  constexpr int OUT_ROWS = EPI == 1 ? 16 : 16 * RT;
   constexpr int ROWS = 16 * RT;
   constexpr int STAGE = ROWS * 128;                   // bf16 elements per stage (256 B rows)
   constexpr int RING = S * STAGE;                      // per wave
@@ -52,13 +57,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * ROWS;
+  const int n0 = blockIdx.x * OUT_ROWS;
   const int g = lane >> 4;         // k-group of this lane inside a 32-k step
   const int i16 = lane & 15;       // weight row / token inside a 16-tile
 
-  const int wrows = min(ROWS, N - n0);
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (int64_t)n0 * K), 0, (uint32_t)wrows * (uint32_t)K * 2u, 0x00020000);
+  // one resource per row tile, based at its first row and bounded to its valid rows
+  __amdgpu_buffer_rsrc_t wr[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int base = EPI == 1 ? (r == 0 ? n0 : N + n0) : n0 + 16 * r;
+    const int rows = EPI == 1 ? min(16, N - n0) : max(0, min(16, N - n0 - 16 * r));
+    wr[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)base * K), 0,
+                                              (uint32_t)rows * (uint32_t)K * 2u, 0x00020000);
+  }
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)X, 0, (uint32_t)M * (uint32_t)K * 2u, 0x00020000);
 
@@ -76,10 +87,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
     TPL_LDS uint16_t* dst = ring + (c % S) * STAGE;
 #pragma unroll
     for (int d = 0; d < ROWS / 4; ++d) {
-      const int row = 4 * d + drow;
+      const int row = 4 * d + drow;                      // row tile d / 4, row (row % 16) in it
       const int k = k0 + 8 * (dpos ^ (row & 15));
-      const uint32_t off = k < ke ? (uint32_t)(row * K + k) * 2u : kSOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (TPL_LDS void*)(dst + d * 4 * 128), 16, off, 0, 0, 0);
+      const uint32_t off = k < ke ? (uint32_t)((row & 15) * K + k) * 2u : kSOob;
+      const __amdgpu_buffer_rsrc_t rs = d < 4 ? wr[0] : wr[RT - 1];   // row tile d / 4 (RT <= 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TPL_LDS void*)(dst + d * 4 * 128), 16, off, 0, 0, 0);
     }
   };
 
@@ -166,6 +178,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
   __syncthreads();
 
   constexpr int PER = RT * MT * 256;
+  if constexpr (EPI == 1) {
+    for (int v = threadIdx.x; v < MT * 256; v += WAVES * 64) {
+      float sg = 0.f, su = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) { sg += red[w * PER + v]; su += red[w * PER + MT * 256 + v]; }
+      const int t = v / 256, l = (v >> 2) & 63, e = v & 3;
+      const int m = t * 16 + (l & 15);
+      const int n = n0 + (l >> 4) * 4 + e;
+      if (m < M && n < N)
+        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] = (uint16_t)f2bf_bits(
+            act_fn<TP_ACT_SWIGLU>(bf2f((uint16_t)f2bf_bits(sg)), bf2f((uint16_t)f2bf_bits(su))));
+    }
+    return;
+  }
   for (int v = threadIdx.x; v < PER; v += WAVES * 64) {
     float s = 0.f;
 #pragma unroll
@@ -174,7 +200,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
     const int m = t * 16 + (l & 15);
     const int n = n0 + rt * 16 + (l >> 4) * 4 + e;
     if (m < M && n < N) {
-      if constexpr (OUT_F32)
+      if constexpr (EPI == 2)
+        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] =
+            (uint16_t)f2bf_bits(act_fn<TP_ACT_GELU>(bf2f((uint16_t)f2bf_bits(s)), 0.f));
+      else if constexpr (OUT_F32)
         reinterpret_cast<float*>(Y)[(int64_t)m * N + n] = s;
       else
         reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] = (uint16_t)f2bf_bits(s);
@@ -182,16 +211,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
   }
 }
 
-template <int WAVES, int MT, int RT, int S>
+template <int WAVES, int MT, int RT, int S, int EPI = 0>
 static void launch_stream_dma(const void* x, const void* w, void* y, int M, int N, int K, int kw,
                               bool out_f32, hipStream_t s) {
-  dim3 grid((N + 16 * RT - 1) / (16 * RT)), block(WAVES * 64);
+  constexpr int OUT_ROWS = EPI == 1 ? 16 : 16 * RT;
+  dim3 grid((N + OUT_ROWS - 1) / OUT_ROWS), block(WAVES * 64);
   auto X = static_cast<const uint16_t*>(x);
   auto Wp = static_cast<const uint16_t*>(w);
-  if (out_f32)
-    hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, true>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
-  else
-    hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, false>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+  if constexpr (EPI == 0) {
+    if (out_f32)
+      hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, true, 0>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+    else
+      hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, false, 0>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+  } else {
+    hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, false, EPI>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+  }
 }
 
 // Requires 33 <= M <= 64, K % 8 == 0, 16-byte aligned X and W, M*K and
@@ -206,6 +240,24 @@ tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M,
   if (M > 48) launch_stream_dma<WV, 4, 2, 8>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
   else launch_stream_dma<WV, 3, 2, 8>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
   TPL_LAUNCH_CHECK("gemm_bf16_stream_dma");
+  return TP_OK;
+}
+
+// The same kernel with the rank-local activation fused (bf16 output [M, I]).
+tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
+                                   int64_t K, int act, hipStream_t s) {
+  constexpr int WV = 2;
+  int kw = (int)((K + WV - 1) / WV);
+  kw = (kw + 127) & ~127;
+  const int Mi = (int)M, Ii = (int)I, Ki = (int)K;
+  if (act == TP_ACT_SWIGLU) {
+    if (M > 48) launch_stream_dma<WV, 4, 2, 8, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    else launch_stream_dma<WV, 3, 2, 8, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
+  } else {
+    if (M > 48) launch_stream_dma<WV, 4, 2, 8, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    else launch_stream_dma<WV, 3, 2, 8, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
+  }
+  TPL_LAUNCH_CHECK("gemm_bf16_stream_dma_act");
   return TP_OK;
 }
 

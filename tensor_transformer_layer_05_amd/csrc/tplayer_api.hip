@@ -12,6 +12,13 @@ tp_status gemm_bf16_mfma(const void* x, const void* w, void* y, int64_t M, int64
                          bool out_f32, bool aligned, hipStream_t s, int force_tile);
 tp_status gemm_bf16_dma(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                         bool out_f32, bool vec_out, hipStream_t s, int force_tile);
+tp_status gemm_bf16_dma_act(const void* x, const void* w, void* h, int64_t M, int64_t I, int64_t K,
+                            int act, bool vec_out, hipStream_t s);
+tp_status gemm_bf16_stream_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
+                               int64_t K, int act, hipStream_t s);
+tp_status reduce_rmsnorm(const float* const* partials, int R, const void* residual, void* y,
+                         const void* gamma, void* yn, int64_t M, int64_t N, float eps,
+                         hipStream_t s);
 tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                            bool out_f32, hipStream_t s);
 tp_status gemm_f32(const float* x, const float* w, float* y, int64_t M, int64_t N, int64_t K,
@@ -90,6 +97,27 @@ tp_status tp_column_linear(const void* x, const void* w, void* y, int64_t M, int
 tp_status tp_row_linear_partial(const void* x, const void* w, float* partial, int64_t M, int64_t K,
                                 int64_t N, tp_dtype dt, void* stream) {
   return linear_common(x, w, partial, M, K, N, dt, stream, /*out_f32=*/true);
+}
+
+tp_status tp_column_linear_act(const void* x, const void* w, void* h, int64_t M, int64_t K,
+                               int64_t I, tp_act act, tp_dtype dt, void* stream) {
+  if (act == TP_ACT_NONE) return tp_column_linear(x, w, h, M, K, I, dt, stream);
+  if (!x || !w || !h) return TP_ERR_NULL;
+  if (act != TP_ACT_SWIGLU && act != TP_ACT_GELU) return TP_ERR_DTYPE;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (M <= 0 || K <= 0 || I <= 0) return TP_ERR_SHAPE;
+  if (M > kIntMax || K > kIntMax || I > kIntMax) return TP_ERR_UNSUPPORTED;
+  if (dt != TP_BF16) return TP_ERR_UNSUPPORTED;
+  if (!aligned(x, 2) || !aligned(w, 2) || !aligned(h, 2)) return TP_ERR_ALIGN;
+  // The fused kernels stream 16-byte vectors of both operands.
+  if (K % 8 != 0 || !aligned(x, 16) || !aligned(w, 16)) return TP_ERR_UNSUPPORTED;
+  const int64_t wrows = act == TP_ACT_SWIGLU ? 2 * I : I;
+  if (wrows * K * 2 >= (int64_t{1} << 32)) return TP_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  if (M <= 64 && K < (int64_t{1} << 24)) return tpl::gemm_bf16_stream_act(x, w, h, M, I, K, (int)act, s);
+  if (K >= (int64_t{1} << 21)) return TP_ERR_UNSUPPORTED;
+  const bool vec_out = (I % 4 == 0) && aligned(h, 8);
+  return tpl::gemm_bf16_dma_act(x, w, h, M, I, K, (int)act, vec_out, s);
 }
 
 tp_status tp_swiglu_local(const void* gate, const void* up, void* h, int64_t M, int64_t I,
@@ -179,6 +207,33 @@ tp_status tp_reduce_partials(const float* const* partials, int64_t R, const void
   }
   return tpl::reduce_partials(partials, (int)R, residual, y, M * N, out_dt == TP_BF16, vec,
                               as_stream(stream));
+}
+
+tp_status tp_reduce_partials_rmsnorm(const float* const* partials, int64_t R, const void* residual,
+                                     void* y, const void* gamma, void* yn, int64_t M, int64_t N,
+                                     float eps, tp_dtype dt, void* stream) {
+  if (!partials || !y || !gamma || !yn) return TP_ERR_NULL;
+  if (R < 1 || R > 16) return TP_ERR_SHAPE;
+  for (int64_t r = 0; r < R; ++r)
+    if (!partials[r]) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (M <= 0 || N <= 0 || !(eps >= 0.f) || !isfinite(eps)) return TP_ERR_SHAPE;
+  if (M > kIntMax) return TP_ERR_UNSUPPORTED;
+  const size_t es = esize(dt);
+  if (!aligned(y, es) || !aligned(yn, es) || !aligned(gamma, es) || (residual && !aligned(residual, es)))
+    return TP_ERR_ALIGN;
+  bool fused = dt == TP_BF16 && N % 8 == 0 && aligned(y, 16) && aligned(yn, 16) && aligned(gamma, 16) &&
+               (!residual || aligned(residual, 16));
+  for (int64_t r = 0; r < R; ++r) {
+    if (!aligned(partials[r], 4)) return TP_ERR_ALIGN;
+    fused = fused && aligned(partials[r], 16);
+  }
+  if (fused)
+    return tpl::reduce_rmsnorm(partials, (int)R, residual, y, gamma, yn, M, N, eps, as_stream(stream));
+  // other layouts: the two unfused calls (same results)
+  const tp_status st = tp_reduce_partials(partials, R, residual, y, M, N, dt, stream);
+  if (st != TP_OK) return st;
+  return tp_rmsnorm(y, gamma, yn, M, N, eps, dt, stream);
 }
 
 tp_status tp_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t N, float eps,

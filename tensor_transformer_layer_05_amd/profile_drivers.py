@@ -5,8 +5,10 @@
 
 ``gemm_traffic``: one plain 256 MiB device-to-device copy (a calibration
 dispatch of known size: 256 MiB read, 256 MiB written), then one launch of the
-prefill gate|up column-parallel GEMM (M=4096, K=8192, N=28672, bf16).  Run it
-under ``rocprofv3 --pmc FETCH_SIZE`` and, separately, ``--pmc WRITE_SIZE``.
+prefill gate|up projection with SwiGLU in its epilogue (M=4096, K=8192,
+2I=28672, output [4096, 14336], bf16), then one launch of the plain gate|up
+GEMM on the same operands (output [4096, 28672]).  Run it under
+``rocprofv3 --pmc FETCH_SIZE`` and, separately, ``--pmc WRITE_SIZE``.
 """
 from __future__ import annotations
 
@@ -14,7 +16,7 @@ import sys
 
 import torch
 
-from . import column_linear, lib
+from . import column_linear, column_linear_act, lib
 
 
 def gemm_traffic() -> None:
@@ -25,9 +27,12 @@ def gemm_traffic() -> None:
     M, K, N = 4096, 8192, 28672
     x = torch.randn(M, K, device="cuda").to(torch.bfloat16)
     w = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
+    h = torch.empty(M, N // 2, device="cuda", dtype=torch.bfloat16)
     y = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
     torch.cuda.synchronize()
     b.copy_(a)
+    torch.cuda.synchronize()
+    column_linear_act(x, w, "swiglu", out=h)
     torch.cuda.synchronize()
     column_linear(x, w, out=y)
     torch.cuda.synchronize()

@@ -9,9 +9,9 @@ parallel" / "MLP 里的 tensor parallel"; P2 sections 二 and 2.1):
     o = attention over the rank's heads               local
     P_attn_r = o Wo_r                                 row-parallel partial
     h = x + sum_r P_attn_r                            all-reduce arithmetic
-    hn = RMSNorm(h)
+    hn = RMSNorm(h)                                   (fused with the sum)
     g|u = hn Wgu_r                                    column-parallel
-    a = SiLU(g) * u   (or GELU(g))                    local
+    a = SiLU(g) * u   (or GELU(g))                    local (fused into g|u)
     P_mlp_r = a Wd_r                                  row-parallel partial
     y = h + sum_r P_mlp_r                             all-reduce arithmetic
 
@@ -27,18 +27,23 @@ from __future__ import annotations
 
 import torch
 
-from . import (column_linear, local_attention, kv_append, reduce_partials, rmsnorm,
-               row_linear_partial, swiglu_local)
+from . import (column_linear, column_linear_act, local_attention, kv_append, reduce_partials,
+               reduce_partials_rmsnorm, rmsnorm, row_linear_partial, swiglu_local)
 
 
 class MlpShard:
     """gate|up (or fc1) column-parallel, local activation, down (or fc2)
     row-parallel partial for one rank.  ``w_in`` is ``[2*I_l, H]`` (gate rows
     then up rows) for SwiGLU or ``[I_l, H]`` for GELU/none; ``w_out`` is
-    ``[H, I_l]``."""
+    ``[H, I_l]``.  With ``fused`` (the default) a bf16 shard takes the
+    activation in the projection's epilogue (``column_linear_act``); the
+    result is the same bit for bit."""
 
-    def __init__(self, w_in: torch.Tensor, w_out: torch.Tensor, act: str, max_tokens: int):
+    def __init__(self, w_in: torch.Tensor, w_out: torch.Tensor, act: str, max_tokens: int,
+                 fused: bool = True):
         self.w_in, self.w_out, self.act = w_in, w_out, act
+        self.fused = (fused and act in ("swiglu", "gelu") and w_in.dtype == torch.bfloat16
+                      and w_in.shape[1] % 8 == 0 and w_in.data_ptr() % 16 == 0)
         self.I = w_out.shape[1]
         self.H = w_out.shape[0]
         n_in = w_in.shape[0]
@@ -50,9 +55,13 @@ class MlpShard:
 
     def partial(self, x: torch.Tensor, out: torch.Tensor):
         M = x.shape[0]
+        a = self.a[:M]
+        if self.fused and x.is_contiguous() and x.data_ptr() % 16 == 0:
+            column_linear_act(x, self.w_in, self.act, out=a)
+            row_linear_partial(a, self.w_out, out=out)
+            return out
         gu = self.gu[:M]
         column_linear(x, self.w_in, out=gu)
-        a = self.a[:M]
         if self.act == "swiglu":
             swiglu_local(gu[:, :self.I], gu[:, self.I:], "swiglu", out=a)
         else:
@@ -126,10 +135,10 @@ class LayerShard:
     """One rank's share of a pre-norm decoder layer (prefill of one sequence)."""
 
     def __init__(self, g1, g2, wqkv, wo, wgu, wd, n_q, n_kv, head_dim, eps, max_tokens,
-                 act="swiglu"):
-        self.g1, self.g2, self.eps = g1, g2, eps
+                 act="swiglu", fused=True):
+        self.g1, self.g2, self.eps, self.fused = g1, g2, eps, fused
         self.attn = AttnShard(wqkv, wo, n_q, n_kv, head_dim, max_tokens)
-        self.mlp = MlpShard(wgu, wd, act, max_tokens)
+        self.mlp = MlpShard(wgu, wd, act, max_tokens, fused=fused)
         H = wo.shape[0]
         dev, dt = wqkv.device, wqkv.dtype
         self.xn = torch.empty((max_tokens, H), dtype=dt, device=dev)
@@ -153,7 +162,13 @@ class LayerShard:
         S = x.shape[0]
         self.attn_partial(x, attn_parts[rank])
         h = self.h[:S]
-        reduce_partials(attn_parts, residual=x, out=h)
-        self.mlp_partial(h, mlp_parts[rank])
+        if self.fused:
+            # the all-reduce's sum and the MLP's pre-norm in one pass
+            reduce_partials_rmsnorm(attn_parts, self.g2, residual=x, eps=self.eps, out=h,
+                                    out_norm=self.hn[:S])
+            self.mlp.partial(self.hn[:S], mlp_parts[rank])
+        else:
+            reduce_partials(attn_parts, residual=x, out=h)
+            self.mlp_partial(h, mlp_parts[rank])
         reduce_partials(mlp_parts, residual=h, out=y)
         return y

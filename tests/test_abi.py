@@ -39,7 +39,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("tp_column_linear", "tp_swiglu_local", "tp_local_attention", "tp_row_linear_partial",
-              "tp_reduce_partials", "tp_rmsnorm", "tp_kv_append", "tp_status_string"):
+              "tp_reduce_partials", "tp_rmsnorm", "tp_kv_append", "tp_status_string",
+              "tp_column_linear_act", "tp_reduce_partials_rmsnorm"):
         assert n in names
 
 
@@ -155,6 +156,35 @@ def test_rmsnorm_and_append_validation(lib):
     assert f(P, P, 128, P, P, cs, 2, 2, 128, 0, 1, S) == SHAPE     # row stride < Hkv*D
     assert f(P, P, 256, P, P, cs, 2, 2, 128, -1, 1, S) == SHAPE
     assert f(P, P, 256, P, P, cs, 2, 2, 128, 0, 0, S) == UNSUPPORTED
+
+
+@no_gpu
+def test_fused_entry_validation(lib):
+    f = lib.tp_column_linear_act
+    assert f(None, P, P, 4, 8, 8, 1, 1, S) == NULL
+    assert f(P, P, None, 4, 8, 8, 2, 1, S) == NULL
+    assert f(P, P, P, 4, 8, 8, 9, 1, S) == DTYPE             # bad activation
+    assert f(P, P, P, 4, 8, 8, 1, 5, S) == DTYPE             # bad dtype
+    assert f(P, P, P, 0, 8, 8, 1, 1, S) == SHAPE
+    assert f(P, P, P, 4, 8, 0, 1, 1, S) == SHAPE
+    assert f(P, P, P, 4, 8, 8, 1, 0, S) == UNSUPPORTED       # fused activations are bf16 only
+    assert f(P, P, P, 4, 12, 8, 1, 1, S) == UNSUPPORTED      # K % 8 != 0
+    assert f(P + 2, P, P, 4, 8, 8, 1, 1, S) == UNSUPPORTED   # x not 16-byte aligned
+    assert f(P + 1, P, P, 4, 8, 8, 1, 1, S) == ALIGN
+    assert f(P, P, P, 4, 1 << 20, 1 << 11, 1, 1, S) == UNSUPPORTED   # weight past 32-bit offsets
+    g = lib.tp_reduce_partials_rmsnorm
+    arr = (ctypes.c_void_p * 2)(P, P)
+    assert g(None, 2, None, P, P, P, 4, 8, 1e-5, 1, S) == NULL
+    assert g(arr, 2, None, P, None, P, 4, 8, 1e-5, 1, S) == NULL
+    assert g(arr, 2, None, P, P, None, 4, 8, 1e-5, 1, S) == NULL
+    assert g(arr, 0, None, P, P, P, 4, 8, 1e-5, 1, S) == SHAPE
+    assert g(arr, 17, None, P, P, P, 4, 8, 1e-5, 1, S) == SHAPE
+    assert g(arr, 2, None, P, P, P, 4, 8, -1.0, 1, S) == SHAPE
+    assert g(arr, 2, None, P, P, P, 0, 8, 1e-5, 1, S) == SHAPE
+    assert g(arr, 2, None, P, P, P, 4, 8, 1e-5, 4, S) == DTYPE
+    assert g(arr, 2, None, P + 1, P, P, 4, 8, 1e-5, 1, S) == ALIGN
+    odd = (ctypes.c_void_p * 2)(P, P + 2)
+    assert g(odd, 2, None, P, P, P, 4, 8, 1e-5, 1, S) == ALIGN
 
 
 # ---------------------------------------------------------------------------

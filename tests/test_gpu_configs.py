@@ -61,8 +61,13 @@ def test_decode_mlp_tp8_rank0(M):
     wu = I.normal(c.seed, "wu", (il, H), c.w_std, rank=0)
     wd = I.normal(c.seed, "wd", (H, il), c.w_std, rank=0)
     sh = MlpShard(torch.cat([wg.dev, wu.dev], 0).to(DEV), wd.dev.to(DEV), "swiglu", 64)
+    assert sh.fused
     p = torch.empty((M, H), dtype=torch.float32, device=DEV)
     sh.partial(x.dev.to(DEV), p)
+    p_unfused = torch.empty_like(p)
+    sh.fused = False
+    sh.partial(x.dev.to(DEV), p_unfused)
+    assert torch.equal(p, p_unfused), "fused gate|up + SwiGLU differs from the unfused calls"
     ref = O.mlp_rank_partial(x.ref, wg.ref, wd.ref, "swiglu", 0, 1, w_up=wu.ref)
     assert_normwise(p, ref, 1e-2, f"rank-0 partial M={M}")
     # storage-faithful oracle (bf16 intermediates where the kernels store them)
@@ -167,6 +172,13 @@ def test_prefill_layer_tp2_equals_unsharded():
     # the benchmark's step for rank 0, with rank 1's partials already in place
     shards[0].step(X, pa, pm, 0, y)
     torch.cuda.synchronize()
+    # the fused calls (sum + pre-norm, gate|up + SwiGLU) give the unfused bits
+    y_unfused = torch.empty_like(y)
+    h_fused = shards[0].h[:S].clone()
+    shards[0].fused = shards[0].mlp.fused = False
+    shards[0].step(X, pa, pm, 0, y_unfused)
+    assert torch.equal(h_fused, shards[0].h[:S]), "fused sum + RMSNorm changed h"
+    assert torch.equal(y, y_unfused), "fused step differs from the unfused step"
     rows = sample_rows(S, 48, 104)
     cat0 = lambda n: np.concatenate([ws[r][n].ref for r in range(R)], 0)
     cat1 = lambda n: np.concatenate([ws[r][n].ref for r in range(R)], 1)
