@@ -12,7 +12,8 @@ are computed once before timing.  Inputs are seeded synthetic tensors already
 resident in HBM.  Prints ONE JSON line.
 
 Secondary figures (same line, key "decode"): the decode MLP shard at TP=8
-(M = 1, 8, 64) and the decode attention shard at TP=4, timed over 4 rotating
+(M = 1, 8, 64), the decode attention shard at TP=4 and the same attention at
+TP=16 with replicated KV heads, timed over 4 rotating
 copies of the weights/caches so that the 256 MB Infinity Cache cannot hold
 the working set between steps (also as HIP-graph replays, "graph_ms").
 """
@@ -337,7 +338,41 @@ def decode_figures(steps=30, warmup=5, copies=4):
     fl = 2.0 * B * H * (hq + 2 * hkv) * D + 4.0 * B * hq * L * D + 2.0 * B * hq * D * H
     out["attn_tp4_B32_L2048"] = {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
                                  "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS, "graph_ms": gms}
+    out["attn_tp16_rep_B32_L2048"] = _replicated_attn_figure(steps, warmup, copies)
     return out
+
+
+def _replicated_attn_figure(steps, warmup, copies):
+    """Rank 0's decode attention shard when KV heads are replicated (32 q / 8
+    KV heads at TP 16: 2 q heads and one KV head per rank)."""
+    c = I.config("decode_attn_tp16_rep")
+    H, R, D, B, L = c.hidden, c.tp, c.head_dim, c.batch, c.kv_len
+    hq = c.n_q // R
+    heads = tpl.kv_heads_of_rank(c.n_q, c.n_kv, 0, R)
+    x = I.normal(c.seed, "x", (B, H)).dev.to(DEV)
+    wq = I.normal(c.seed, "wq", (c.n_q * D, H), c.w_std).dev
+    wk = I.normal(c.seed, "wk", (c.n_kv * D, H), c.w_std).dev
+    wv = I.normal(c.seed, "wv", (c.n_kv * D, H), c.w_std).dev
+    wo = I.normal(c.seed, "wo", (H, c.n_q * D), c.w_std).dev
+    wqkv = tpl.shard_qkv(wq, wk, wv, 0, R, D)
+    wo0 = tpl.shard_row(wo, 0, R)
+    kc = I.normal(c.seed, "kcache", (B, c.n_kv, L, D)).dev[:, heads[0]:heads[0] + 1].contiguous()
+    vc = I.normal(c.seed, "vcache", (B, c.n_kv, L, D)).dev[:, heads[0]:heads[0] + 1].contiguous()
+    sets = [(AttnShard(wqkv.to(DEV), wo0.to(DEV), hq, len(heads), D, B), kc.to(DEV), vc.to(DEV),
+             torch.empty((B, H), dtype=torch.float32, device=DEV)) for _ in range(copies)]
+
+    def step(j):
+        a, k_, v_, P = sets[j]
+        a.decode_partial(x, k_.transpose(1, 2), v_.transpose(1, 2), L - 1, P)
+
+    fns = [(lambda j=j: step(j)) for j in range(copies)]
+    gms = _graph_ms(fns, steps, warmup)
+    ms = _median_ms(lambda i: fns[i % copies](), steps, warmup)
+    byts = (wqkv.numel() + wo0.numel() + kc.numel() + vc.numel()) * 2 + B * H * 2 + B * H * 4
+    fl = 2.0 * B * H * wqkv.shape[0] + 4.0 * B * hq * L * D + 2.0 * B * hq * D * H
+    return {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
+            "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS, "graph_ms": gms,
+            "kv_cache_bytes_per_rank": tpl.kv_cache_bytes_per_rank(c.n_q, c.n_kv, R, B, L, D)}
 
 
 # ---------------------------------------------------------------------------

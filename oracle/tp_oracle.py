@@ -25,7 +25,8 @@ Conventions (readings where the pages leave a choice open):
   * A fused local QKV weight stacks the rank's q heads, then its k heads, then
     its v heads, each head ``D`` consecutive output features.
   * GQA: global q head j reads KV head ``j // (Hq/Hkv)``; with contiguous
-    sharding local q head h reads local KV head ``h // (Hq_l/Hkv_l)``.
+    sharding local q head h reads local KV head ``h // (Hq_l/Hkv_l)``.  With
+    fewer KV heads than ranks each rank keeps one replicated KV head.
   * Attention scale ``1/sqrt(D)``; causal masking aligned at the end of the key
     span (key t is visible to query position p iff t <= p); softmax with the
     row maximum subtracted.
@@ -46,6 +47,7 @@ __all__ = [
     "round_bf16", "linear", "column_shard", "row_shard", "input_shard",
     "column_linear", "row_linear_partial", "reduce_partials", "concat_columns",
     "silu", "gelu", "local_activation", "rmsnorm", "attention", "qkv_shard",
+    "kv_heads_of_rank", "kv_cache_bytes_per_rank",
     "mlp_unsharded", "mlp_rank_partial", "attention_block_unsharded",
     "attention_rank_partial", "layer_unsharded", "layer_sharded",
 ]
@@ -215,18 +217,52 @@ def attention(q, k, v, causal: bool, scale: float | None = None, q_pos=None):
     return out
 
 
+def kv_heads_of_rank(n_q: int, n_kv: int, r: int, R: int):
+    """The KV heads rank r holds, as a list of global KV head ids.
+
+    The q heads are split into R contiguous blocks (P1 "Attention 里的 tensor
+    parallel").  When the KV heads divide by R they are split the same way.
+    When there are fewer KV heads than ranks (P3 "权重变小，不代表所有显存都按
+    比例变小": 32 q / 8 KV heads at TP 16), KV heads cannot be split further:
+    each rank keeps the one KV head its q heads read, j // (Hq/Hkv) for its
+    q heads j, so every KV head is replicated on R / Hkv ranks.  This needs
+    R % Hkv == 0, so that a rank's q heads all fall in one KV group."""
+    if n_q % R:
+        raise ValueError("q heads must divide by the TP size")
+    if n_q % n_kv:
+        raise ValueError("q heads must be a multiple of KV heads")
+    if n_kv % R == 0:
+        c = n_kv // R
+        return list(range(r * c, (r + 1) * c))
+    if R % n_kv:
+        raise ValueError("KV heads must divide by the TP size or the TP size by the KV heads")
+    hq = n_q // R
+    group = n_q // n_kv
+    heads = sorted({j // group for j in range(r * hq, (r + 1) * hq)})
+    assert len(heads) == 1
+    return heads
+
+
+def kv_cache_bytes_per_rank(n_q: int, n_kv: int, R: int, batch: int, kv_len: int,
+                            head_dim: int, elem_bytes: int = 2) -> int:
+    """Bytes of K and V cache one rank keeps for ``batch`` sequences of
+    ``kv_len`` keys (P3: the KV cache is stored per the actual head layout, so
+    it stops shrinking once every rank holds a single replicated KV head)."""
+    return 2 * batch * kv_len * len(kv_heads_of_rank(n_q, n_kv, 0, R)) * head_dim * elem_bytes
+
+
 def qkv_shard(wq, wk, wv, r: int, R: int, head_dim: int):
     """Rank r's fused QKV weight ``[(Hq_l + 2*Hkv_l)*D, H]``: its block of q
-    heads, then its block of KV heads for k, then for v."""
+    heads, then its KV heads for k, then for v (a replicated KV head when
+    there are fewer KV heads than ranks; see ``kv_heads_of_rank``)."""
     wq, wk, wv = (np.asarray(a) for a in (wq, wk, wv))
     for a in (wq, wk, wv):
         if a.shape[0] % head_dim != 0:
             raise ValueError("projection rows must be whole heads")
     n_q, n_kv = wq.shape[0] // head_dim, wk.shape[0] // head_dim
-    if n_q % R or n_kv % R:
-        raise ValueError("q and KV heads must divide by the TP size")
-    return np.concatenate([column_shard(wq, r, R), column_shard(wk, r, R),
-                           column_shard(wv, r, R)], axis=0)
+    heads = kv_heads_of_rank(n_q, n_kv, r, R)
+    kv_rows = np.concatenate([np.arange(j * head_dim, (j + 1) * head_dim) for j in heads])
+    return np.concatenate([column_shard(wq, r, R), wk[kv_rows], wv[kv_rows]], axis=0)
 
 
 # ---------------------------------------------------------------------------
@@ -284,7 +320,7 @@ def attention_rank_partial(x, wq, wk, wv, wo, head_dim: int, r: int, R: int,
     (row-parallel) giving a partial of the hidden output."""
     S = x.shape[0]
     n_q, n_kv = wq.shape[0] // head_dim, wk.shape[0] // head_dim
-    hq, hkv = n_q // R, n_kv // R
+    hq, hkv = n_q // R, len(kv_heads_of_rank(n_q, n_kv, r, R))
     wqkv = qkv_shard(wq, wk, wv, r, R, head_dim)
     dq, dkv = hq * head_dim, hkv * head_dim
     kv = store(column_linear(x, wqkv[dq:, :]))

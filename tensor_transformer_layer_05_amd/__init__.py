@@ -25,7 +25,7 @@ __all__ = [
     "column_linear", "column_linear_act", "row_linear_partial", "swiglu_local",
     "local_attention", "local_attention_workspace", "kv_append", "reduce_partials",
     "reduce_partials_rmsnorm", "rmsnorm",
-    "shard_column", "shard_row", "shard_qkv",
+    "shard_column", "shard_row", "shard_qkv", "kv_heads_of_rank", "kv_cache_bytes_per_rank",
     "F32", "BF16", "ACT_NONE", "ACT_SWIGLU", "ACT_GELU",
 ]
 
@@ -375,12 +375,38 @@ def shard_row(w: torch.Tensor, r: int, R: int) -> torch.Tensor:
     return w.narrow(1, s, b).contiguous()
 
 
+def kv_heads_of_rank(n_q: int, n_kv: int, r: int, R: int) -> list:
+    """Global ids of the KV heads rank r holds.  KV heads are split in
+    contiguous blocks when they divide by R; with fewer KV heads than ranks
+    (GQA at a large TP size) each rank holds the single KV head its q heads
+    read, replicated on R / n_kv ranks (requires R % n_kv == 0)."""
+    if R <= 0 or not (0 <= r < R):
+        raise ValueError(f"rank {r} out of range for TP size {R}")
+    if n_q % R or n_q % n_kv:
+        raise ValueError("q heads must divide by the TP size and by the KV heads")
+    if n_kv % R == 0:
+        c = n_kv // R
+        return list(range(r * c, (r + 1) * c))
+    if R % n_kv:
+        raise ValueError("KV heads must divide by the TP size or the TP size by the KV heads")
+    return [(r * (n_q // R)) // (n_q // n_kv)]
+
+
+def kv_cache_bytes_per_rank(n_q: int, n_kv: int, R: int, batch: int, kv_len: int,
+                            head_dim: int, elem_bytes: int = 2) -> int:
+    """K and V cache bytes one rank keeps (replicated KV heads count on every
+    rank that holds them)."""
+    return 2 * batch * kv_len * len(kv_heads_of_rank(n_q, n_kv, 0, R)) * head_dim * elem_bytes
+
+
 def shard_qkv(wq: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor, r: int, R: int,
               head_dim: int) -> torch.Tensor:
-    """Rank r's fused ``[q heads | k heads | v heads]`` weight."""
+    """Rank r's fused ``[q heads | k heads | v heads]`` weight (its KV heads
+    per ``kv_heads_of_rank``)."""
     for t in (wq, wk, wv):
         if t.shape[0] % head_dim:
             raise ValueError("projection rows must be whole heads")
-    if (wq.shape[0] // head_dim) % R or (wk.shape[0] // head_dim) % R:
-        raise ValueError("q and KV heads must divide by the TP size")
-    return torch.cat([shard_column(wq, r, R), shard_column(wk, r, R), shard_column(wv, r, R)], 0)
+    heads = kv_heads_of_rank(wq.shape[0] // head_dim, wk.shape[0] // head_dim, r, R)
+    j0, c = heads[0], len(heads)
+    return torch.cat([shard_column(wq, r, R), wk.narrow(0, j0 * head_dim, c * head_dim),
+                      wv.narrow(0, j0 * head_dim, c * head_dim)], 0).contiguous()

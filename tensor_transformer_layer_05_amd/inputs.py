@@ -119,6 +119,11 @@ CONFIGS = {
     "prefill_layer_tp2": Config(name="prefill_layer_tp2", seed=104, tp=2, hidden=8192,
                                 tokens=(4096,), inter=28672, n_q=64, n_kv=8,
                                 head_dim=128, act="swiglu", rmsnorm=True),
+    # The same attention at TP=16: fewer KV heads than ranks, so each rank holds
+    # 2 q heads and one KV head replicated on 2 ranks.
+    "decode_attn_tp16_rep": Config(name="decode_attn_tp16_rep", seed=106, tp=16, hidden=4096,
+                                   tokens=(1,), n_q=32, n_kv=8, head_dim=128, kv_len=2048,
+                                   batch=32),
     # GPT-style GELU MLP at TP=8, 4x expansion, all 8 ranks + in-HBM reduce.
     "gelu_mlp_tp8": Config(name="gelu_mlp_tp8", seed=105, tp=8, hidden=12288,
                            tokens=(2048,), inter=49152, act="gelu"),

@@ -206,8 +206,18 @@ def test_shard_helpers_match_oracle_slices():
     for r in range(2):
         assert np.array_equal(tpl.shard_qkv(wq, wk, wv, r, 2, 4).numpy(),
                               O.qkv_shard(wq.numpy(), wk.numpy(), wv.numpy(), r, 2, 4))
+    # 2 KV heads over 4 ranks: each KV head replicated on 2 ranks
+    for R in (4, 8):
+        for r in range(R):
+            assert tpl.kv_heads_of_rank(8, 2, r, R) == O.kv_heads_of_rank(8, 2, r, R)
+            assert np.array_equal(tpl.shard_qkv(wq, wk, wv, r, R, 4).numpy(),
+                                  O.qkv_shard(wq.numpy(), wk.numpy(), wv.numpy(), r, R, 4))
+    assert tpl.kv_cache_bytes_per_rank(32, 8, 16, 2, 64, 128) == O.kv_cache_bytes_per_rank(
+        32, 8, 16, 2, 64, 128)
     with pytest.raises(ValueError):
-        tpl.shard_qkv(wq, wk, wv, 0, 4, 4)     # 2 KV heads over 4 ranks
+        tpl.shard_qkv(wq, wk, wv, 0, 3, 4)     # 8 q heads over 3 ranks
+    with pytest.raises(ValueError):
+        tpl.kv_heads_of_rank(12, 4, 0, 6)      # 4 KV heads over 6 ranks
 
 
 def test_binding_rejects_cpu_tensors():

@@ -127,6 +127,51 @@ def test_decode_attn_tp4_rank0():
     assert_normwise(V[:, :, L - 1], vn, 1e-2, "appended v")
 
 
+def test_decode_attn_tp16_replicated_kv_all_ranks():
+    """32 q / 8 KV heads at TP 16: every rank holds 2 q heads and one KV head
+    replicated on 2 ranks; the 16 decode partials sum to the unsharded block
+    and replicated ranks append identical K/V."""
+    c = I.config("decode_attn_tp16_rep")
+    H, R, D, B, L = c.hidden, c.tp, c.head_dim, c.batch, c.kv_len
+    log(f"config decode_attn_tp16_rep all {R} ranks B={B} L={L}")
+    x = I.normal(c.seed, "x", (B, H))
+    wq = I.normal(c.seed, "wq", (c.n_q * D, H), c.w_std)
+    wk = I.normal(c.seed, "wk", (c.n_kv * D, H), c.w_std)
+    wv = I.normal(c.seed, "wv", (c.n_kv * D, H), c.w_std)
+    wo = I.normal(c.seed, "wo", (H, c.n_q * D), c.w_std)
+    kc = I.normal(c.seed, "kcache", (B, c.n_kv, L, D))
+    vc = I.normal(c.seed, "vcache", (B, c.n_kv, L, D))
+    X = x.dev.to(DEV)
+    parts, appended = [], []
+    for r in range(R):
+        heads = tpl.kv_heads_of_rank(c.n_q, c.n_kv, r, R)
+        assert heads == [r // 2]
+        wqkv = tpl.shard_qkv(wq.dev, wk.dev, wv.dev, r, R, D).to(DEV)
+        sh = AttnShard(wqkv, tpl.shard_row(wo.dev, r, R).to(DEV), c.n_q // R, 1, D, B)
+        K = kc.dev[:, heads[0]:heads[0] + 1].contiguous().to(DEV)
+        V = vc.dev[:, heads[0]:heads[0] + 1].contiguous().to(DEV)
+        p = torch.empty((B, H), dtype=torch.float32, device=DEV)
+        sh.decode_partial(X, K.transpose(1, 2), V.transpose(1, 2), L - 1, p)
+        parts.append(p)
+        appended.append((K[:, 0, L - 1].cpu(), V[:, 0, L - 1].cpu()))
+        del sh, K, V
+    for r in range(0, R, 2):
+        assert torch.equal(appended[r][0], appended[r + 1][0]), f"ranks {r},{r+1}: appended k differs"
+        assert torch.equal(appended[r][1], appended[r + 1][1]), f"ranks {r},{r+1}: appended v differs"
+    y = tpl.reduce_partials(parts)
+    q = O.linear(x.ref, wq.ref).reshape(B, 1, c.n_q, D)
+    kn = O.linear(x.ref, wk.ref).reshape(B, c.n_kv, D)
+    vn = O.linear(x.ref, wv.ref).reshape(B, c.n_kv, D)
+    k = kc.ref.copy(); v = vc.ref.copy()
+    k[:, :, L - 1] = kn; v[:, :, L - 1] = vn
+    o = O.attention(q, k.transpose(0, 2, 1, 3), v.transpose(0, 2, 1, 3), causal=True)
+    ref = O.linear(o.reshape(B, c.n_q * D), wo.ref)
+    assert_normwise(y, ref, 1e-2, "16-rank sum vs unsharded decode attention block")
+    # rank 0's partial alone against the oracle's rank partial
+    ref0 = O.row_linear_partial(o[:, 0, :2].reshape(B, 2 * D), O.row_shard(wo.ref, 0, R))
+    assert_normwise(parts[0], ref0, 1e-2, "rank 0 partial")
+
+
 def _layer_weights(c, R):
     H, D = c.hidden, c.head_dim
     hq, hkv, il = c.n_q // R, c.n_kv // R, c.inter // R

@@ -353,6 +353,54 @@ def test_layer_attention_block_matches_bruteforce():
 
 
 # ---------------------------------------------------------------------------
+# GQA with fewer KV heads than ranks (P3 "权重变小，不代表所有显存都按比例变小":
+# 32 q / 8 KV heads; from TP 8 to TP 16 the q heads keep halving per rank but
+# the KV heads per rank do not; vLLM's QKVParallelLinear replicates them)
+# ---------------------------------------------------------------------------
+
+def check_gqa_replication():
+    # the page's structural example
+    per = {R: len(O.kv_heads_of_rank(32, 8, 0, R)) for R in (1, 2, 4, 8, 16, 32)}
+    assert per == {1: 8, 2: 4, 4: 2, 8: 1, 16: 1, 32: 1}
+    b8 = O.kv_cache_bytes_per_rank(32, 8, 8, 4, 1024, 128)
+    assert b8 == 2 * 4 * 1024 * 1 * 128 * 2
+    assert O.kv_cache_bytes_per_rank(32, 8, 16, 4, 1024, 128) == b8        # no longer halves
+    assert O.kv_cache_bytes_per_rank(32, 8, 4, 4, 1024, 128) == 2 * b8
+    # TP 16: ranks 2k and 2k+1 hold KV head k; every KV head is held; each
+    # rank's q heads (2 of them) read the KV head it holds
+    for R, rep in ((16, 2), (32, 4)):
+        held = [O.kv_heads_of_rank(32, 8, r, R) for r in range(R)]
+        assert all(len(h) == 1 for h in held)
+        assert [h[0] for h in held] == [r // rep for r in range(R)]
+        hq = 32 // R
+        for r in range(R):
+            assert {j // 4 for j in range(r * hq, (r + 1) * hq)} == set(held[r])
+    # sharded == unsharded with replicated KV heads (the Σ of rank partials
+    # is the unsharded block only if every rank reads the right KV head)
+    rng = np.random.default_rng(31)
+    H, D, n_q, n_kv = 16, 4, 8, 2
+    wq = rng.standard_normal((n_q * D, H)); wk = rng.standard_normal((n_kv * D, H))
+    wv = rng.standard_normal((n_kv * D, H)); wo = rng.standard_normal((H, n_q * D))
+    x = rng.standard_normal((5, H))
+    ref = O.attention_block_unsharded(x, wq, wk, wv, wo, D)
+    for R in (1, 2, 4, 8):
+        parts = [O.attention_rank_partial(x, wq, wk, wv, wo, D, r, R) for r in range(R)]
+        assert np.allclose(O.reduce_partials(parts), ref, rtol=1e-12, atol=1e-12)
+    # the replicated slice is the KV head's rows of wk / wv
+    w = O.qkv_shard(wq, wk, wv, 5, 8, D)
+    assert w.shape == ((1 + 2) * D, H)
+    assert np.array_equal(w[:D], wq[5 * D:6 * D])
+    assert np.array_equal(w[D:2 * D], wk[D:2 * D]) and np.array_equal(w[2 * D:], wv[D:2 * D])   # q head 5 -> KV head 5 // 4
+    for bad in ((8, 3, 4), (8, 4, 6), (6, 2, 4)):
+        with pytest.raises(ValueError):
+            O.kv_heads_of_rank(bad[0], bad[1], 0, bad[2])
+
+
+def test_gqa_replication():
+    check_gqa_replication()
+
+
+# ---------------------------------------------------------------------------
 # bf16 rounding used by the storage-faithful mode
 # ---------------------------------------------------------------------------
 
@@ -448,7 +496,18 @@ def _mut_qkv_order(wq, wk, wv, r, R, head_dim):
     return _orig_qkv_shard(wq, wv, wk, r, R, head_dim)
 
 
+_orig_kv_heads = O.kv_heads_of_rank
+
+
+def _mut_kv_heads_modulo(n_q, n_kv, r, R):
+    # replicated ranks take KV head r % Hkv instead of the head their q heads read
+    if n_kv % R == 0:
+        return _orig_kv_heads(n_q, n_kv, r, R)
+    return [r % n_kv]
+
+
 MUTATIONS = [
+    ("kv_heads_of_rank", _mut_kv_heads_modulo),
     ("linear", _mut_linear_transposed),
     ("row_shard", _mut_row_shard_wrong_axis),
     ("reduce_partials", _mut_reduce_drops_residual),
@@ -465,7 +524,7 @@ MUTATIONS = [
 
 ALL_CHECKS = [check_worked_example, check_linear_bruteforce, check_sharding_invariants,
               check_toy_mlp_bitexact, check_activations, check_rmsnorm, check_attention,
-              check_layer_sharded_equals_unsharded]
+              check_layer_sharded_equals_unsharded, check_gqa_replication]
 
 
 @pytest.mark.parametrize("name,fn", MUTATIONS, ids=[f"{n}:{f.__name__}" for n, f in MUTATIONS])
