@@ -12,8 +12,9 @@ are computed once before timing.  Inputs are seeded synthetic tensors already
 resident in HBM.  Prints ONE JSON line.
 
 Secondary figures (same line, key "decode"): the decode MLP shard at TP=8
-(M = 1, 8, 64), the decode attention shard at TP=4 and the same attention at
-TP=16 with replicated KV heads, timed over 4 rotating
+(M = 1, 8, 64), the decode attention shard at TP=4, the same attention at
+TP=16 with replicated KV heads and the vocab-parallel lm_head shard with its
+greedy argmax (TP=8), timed over rotating
 copies of the weights/caches so that the 256 MB Infinity Cache cannot hold
 the working set between steps (also as HIP-graph replays, "graph_ms").
 """
@@ -339,6 +340,27 @@ def decode_figures(steps=30, warmup=5, copies=4):
     out["attn_tp4_B32_L2048"] = {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
                                  "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS, "graph_ms": gms}
     out["attn_tp16_rep_B32_L2048"] = _replicated_attn_figure(steps, warmup, copies)
+    out.update(_lm_head_figures(steps, warmup))
+    return out
+
+
+def _lm_head_figures(steps, warmup, copies=2):
+    """Rank 0's vocab-parallel lm_head shard with its local greedy argmax
+    (128256-token vocab at TP 8: 16032 x 8192 bf16 rows, 263 MB per copy)."""
+    from tensor_transformer_layer_05_amd.shard import VocabShard
+    c = I.config("lm_head_tp8")
+    H, R, V = c.hidden, c.tp, c.extra["vocab"]
+    b = V // R
+    w = I.normal(c.seed, "w", (b, H), c.w_std, rank=0).dev
+    shards = [VocabShard(w.to(DEV), 0, max(c.tokens)) for _ in range(copies)]
+    out = {}
+    for M in c.tokens:
+        h = I.normal(c.seed, "h", (M, H)).dev.to(DEV)
+        ms = _median_ms(lambda i: shards[i % copies].local_greedy(h), steps, warmup)
+        byts = b * H * 2 + M * H * 2 + M * b * 4 * 2 + M * 12
+        fl = 2.0 * M * H * b
+        out[f"lm_head_tp8_M{M}"] = {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
+                                    "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS}
     return out
 
 

@@ -207,6 +207,36 @@ tp_status tp_reduce_partials_rmsnorm(const float* const* partials, int64_t R,
 tp_status tp_rmsnorm(const void* x, const void* gamma, void* y,
                      int64_t M, int64_t N, float eps, tp_dtype dt, void* stream);
 
+/*
+ * Greedy token choice of a vocab-parallel lm_head (P1 "lm_head 怎么处理": the
+ * lm_head is split by vocab rows, column-parallel; under greedy decoding each
+ * rank takes the largest logit of its vocab block and an all-gather /
+ * all-reduce of those pairs finds the global one).
+ *
+ * Local step, per token row m of the rank's logits:
+ *     (max_val[m], max_idx[m]) = max over j of (logits[m, j], vocab_offset + j)
+ * under the order: NaN counts as -inf; a larger value wins; equal values go to
+ * the lower vocab id (max_val is -inf when the row holds no number).
+ *   logits  : [M, V_r] float32 device, contiguous (e.g. the rank's fp32 logits
+ *             from tp_row_linear_partial(h, W_vocab_r, ...))
+ *   max_val : [M] float32 device;  max_idx : [M] int64 device (global vocab ids)
+ *   vocab_offset: first vocab id of the rank's block (r * V / R for contiguous
+ *   blocks).  M, V_r <= 2^31 - 1 (TP_ERR_UNSUPPORTED otherwise).
+ */
+tp_status tp_vocab_argmax_local(const float* logits, int64_t M, int64_t V_r, int64_t vocab_offset,
+                                float* max_val, int64_t* max_idx, void* stream);
+
+/*
+ * The exchange's arithmetic on one GPU: combine the R ranks' local pairs in
+ * rank order with the same order as above (ties -> lowest vocab id), giving
+ * the argmax over the full vocab.
+ *   vals : host array of R device pointers to [M] float32
+ *   idxs : host array of R device pointers to [M] int64
+ *   out_val : [M] float32, out_idx : [M] int64 (device);  1 <= R <= 64
+ */
+tp_status tp_vocab_argmax_reduce(const float* const* vals, const int64_t* const* idxs, int64_t R,
+                                 int64_t M, float* out_val, int64_t* out_idx, void* stream);
+
 /* Static text for a status code. */
 const char* tp_status_string(tp_status s);
 

@@ -47,7 +47,8 @@ __all__ = [
     "round_bf16", "linear", "column_shard", "row_shard", "input_shard",
     "column_linear", "row_linear_partial", "reduce_partials", "concat_columns",
     "silu", "gelu", "local_activation", "rmsnorm", "attention", "qkv_shard",
-    "kv_heads_of_rank", "kv_cache_bytes_per_rank",
+    "kv_heads_of_rank", "kv_cache_bytes_per_rank", "vocab_argmax_local", "vocab_argmax_reduce",
+    "greedy_token", "greedy_token_sharded",
     "mlp_unsharded", "mlp_rank_partial", "attention_block_unsharded",
     "attention_rank_partial", "layer_unsharded", "layer_sharded",
 ]
@@ -263,6 +264,50 @@ def qkv_shard(wq, wk, wv, r: int, R: int, head_dim: int):
     heads = kv_heads_of_rank(n_q, n_kv, r, R)
     kv_rows = np.concatenate([np.arange(j * head_dim, (j + 1) * head_dim) for j in heads])
     return np.concatenate([column_shard(wq, r, R), wk[kv_rows], wv[kv_rows]], axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Vocab-parallel lm_head, greedy decoding (P1 "lm_head 怎么处理": the lm_head
+# is split by vocab, column-parallel; each rank takes its largest logit and an
+# all-gather / all-reduce picks the global one)
+# ---------------------------------------------------------------------------
+
+def vocab_argmax_local(logits, vocab_offset: int = 0):
+    """Per row: the largest logit of the rank's vocab block and its global
+    vocab id.  Reading where the page is silent: a NaN logit counts as -inf,
+    and equal logits go to the lowest vocab id (numpy's argmax returns the
+    first maximum)."""
+    z = np.asarray(logits, np.float64)
+    z = np.where(np.isnan(z), -np.inf, z)
+    j = np.argmax(z, axis=-1)
+    return np.take_along_axis(z, j[..., None], axis=-1)[..., 0], j.astype(np.int64) + vocab_offset
+
+
+def vocab_argmax_reduce(vals, ids):
+    """The exchange: the ranks' (value, id) pairs, combined rank by rank; a
+    larger value wins, an equal value keeps the lower id."""
+    best_v = np.array(vals[0], np.float64)
+    best_i = np.array(ids[0], np.int64)
+    for v, i in zip(vals[1:], ids[1:]):
+        v = np.asarray(v, np.float64); i = np.asarray(i, np.int64)
+        take = (v > best_v) | ((v == best_v) & (i < best_i))
+        best_v = np.where(take, v, best_v)
+        best_i = np.where(take, i, best_i)
+    return best_v, best_i
+
+
+def greedy_token(h, w_vocab):
+    """Unsharded greedy choice: argmax over the full vocab of ``h W^T``."""
+    return vocab_argmax_local(linear(h, w_vocab), 0)
+
+
+def greedy_token_sharded(h, w_vocab, R: int):
+    """The same choice made the vocab-parallel way: rank r's logits over its
+    contiguous vocab block, its local argmax, then the combine over ranks."""
+    V = np.asarray(w_vocab).shape[0]
+    pairs = [vocab_argmax_local(column_linear(h, column_shard(w_vocab, r, R)), r * (V // R))
+             for r in range(R)]
+    return vocab_argmax_reduce([p[0] for p in pairs], [p[1] for p in pairs])
 
 
 # ---------------------------------------------------------------------------

@@ -10,7 +10,8 @@ fallback -- if the library is missing the calls raise.
 Entry points (same names as the C ABI, without the ``tp_`` prefix):
 ``column_linear``, ``column_linear_act``, ``row_linear_partial``,
 ``swiglu_local``, ``local_attention``, ``kv_append``, ``reduce_partials``,
-``reduce_partials_rmsnorm``, ``rmsnorm``.
+``reduce_partials_rmsnorm``, ``rmsnorm``, ``vocab_argmax_local``,
+``vocab_argmax_reduce``.
 Weights use the nn.Linear layout ``[out_features, in_features]``.
 """
 from __future__ import annotations
@@ -24,7 +25,7 @@ __all__ = [
     "lib", "library_path", "TPError",
     "column_linear", "column_linear_act", "row_linear_partial", "swiglu_local",
     "local_attention", "local_attention_workspace", "kv_append", "reduce_partials",
-    "reduce_partials_rmsnorm", "rmsnorm",
+    "reduce_partials_rmsnorm", "rmsnorm", "vocab_argmax_local", "vocab_argmax_reduce",
     "shard_column", "shard_row", "shard_qkv", "kv_heads_of_rank", "kv_cache_bytes_per_rank",
     "F32", "BF16", "ACT_NONE", "ACT_SWIGLU", "ACT_GELU",
 ]
@@ -60,6 +61,9 @@ _SIGS = {
     "tp_reduce_partials_rmsnorm": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, _vp, _vp, _vp, _vp,
                                                   _i64, _i64, ctypes.c_float, ctypes.c_int, _vp]),
     "tp_rmsnorm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, ctypes.c_float, ctypes.c_int, _vp]),
+    "tp_vocab_argmax_local": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "tp_vocab_argmax_reduce": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64, _i64,
+                                              _vp, _vp, _vp]),
     "tp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tp_last_error": (ctypes.c_char_p, []),
     "tp_version": (ctypes.c_char_p, []),
@@ -104,16 +108,16 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _dev(t: torch.Tensor, name: str):
+def _dev(t: torch.Tensor, name: str, dtypes=_DT):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a CUDA (HIP) tensor")
-    if t.dtype not in _DT:
+    if t.dtype not in dtypes:
         raise ValueError(f"{name}: unsupported dtype {t.dtype}")
     return t
 
 
-def _contig(t: torch.Tensor, name: str):
-    _dev(t, name)
+def _contig(t: torch.Tensor, name: str, dtypes=_DT):
+    _dev(t, name, dtypes)
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
@@ -348,6 +352,41 @@ def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, out: torch.
     _check("tp_rmsnorm", lib().tp_rmsnorm(x.data_ptr(), gamma.data_ptr(), out.data_ptr(), M, N,
                                           float(eps), _DT[x.dtype], _stream(x)))
     return out
+
+
+def vocab_argmax_local(logits: torch.Tensor, vocab_offset: int = 0):
+    """Per row of a rank's fp32 logits ``[M, V_r]``: the largest logit and its
+    global vocab id (NaN counts as -inf; ties go to the lower id).
+    Returns ``(values [M] float32, ids [M] int64)``."""
+    _contig(logits, "logits")
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be a 2-D float32 tensor")
+    M, V = logits.shape
+    mv = torch.empty(M, dtype=torch.float32, device=logits.device)
+    mi = torch.empty(M, dtype=torch.int64, device=logits.device)
+    _check("tp_vocab_argmax_local", lib().tp_vocab_argmax_local(
+        logits.data_ptr(), M, V, int(vocab_offset), mv.data_ptr(), mi.data_ptr(), _stream(logits)))
+    return mv, mi
+
+
+def vocab_argmax_reduce(vals, idxs):
+    """Combine the ranks' ``(values, ids)`` in rank order: the argmax over the
+    full vocab.  Returns ``(values [M], ids [M])``."""
+    vals, idxs = list(vals), list(idxs)
+    if not vals or len(vals) != len(idxs):
+        raise ValueError("need one (values, ids) pair per rank")
+    M = vals[0].shape[0]
+    for v, i in zip(vals, idxs):
+        _contig(v, "values"); _contig(i, "ids", (torch.int64,))
+        if v.dtype != torch.float32 or i.dtype != torch.int64 or v.shape != (M,) or i.shape != (M,):
+            raise ValueError("values must be [M] float32 and ids [M] int64")
+    ov = torch.empty(M, dtype=torch.float32, device=vals[0].device)
+    oi = torch.empty(M, dtype=torch.int64, device=vals[0].device)
+    va = (ctypes.c_void_p * len(vals))(*[v.data_ptr() for v in vals])
+    ia = (ctypes.c_void_p * len(idxs))(*[i.data_ptr() for i in idxs])
+    _check("tp_vocab_argmax_reduce", lib().tp_vocab_argmax_reduce(
+        va, ia, len(vals), M, ov.data_ptr(), oi.data_ptr(), _stream(vals[0])))
+    return ov, oi
 
 
 # ---------------------------------------------------------------------------

@@ -16,6 +16,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kNumXcd = 8;    // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr int kMaxArgmaxRanks = 64;   // ranks combined by one vocab argmax reduce call
 
 // ---- bf16 <-> fp32 ---------------------------------------------------------
 

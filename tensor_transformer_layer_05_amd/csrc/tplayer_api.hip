@@ -52,6 +52,10 @@ void set_hip_error(const char* where, hipError_t e) {
   snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
 }
 
+tp_status vocab_argmax_local(const float* logits, int64_t M, int64_t V, int64_t offset, float* mv,
+                             int64_t* mi, bool vec, hipStream_t s);
+tp_status vocab_argmax_reduce(const float* const* vals, const int64_t* const* idxs, int R, int64_t M,
+                              float* ov, int64_t* oi, hipStream_t s);
 }  // namespace tpl
 
 namespace {
@@ -234,6 +238,28 @@ tp_status tp_reduce_partials_rmsnorm(const float* const* partials, int64_t R, co
   const tp_status st = tp_reduce_partials(partials, R, residual, y, M, N, dt, stream);
   if (st != TP_OK) return st;
   return tp_rmsnorm(y, gamma, yn, M, N, eps, dt, stream);
+}
+
+tp_status tp_vocab_argmax_local(const float* logits, int64_t M, int64_t V_r, int64_t vocab_offset,
+                                float* max_val, int64_t* max_idx, void* stream) {
+  if (!logits || !max_val || !max_idx) return TP_ERR_NULL;
+  if (M <= 0 || V_r <= 0 || vocab_offset < 0) return TP_ERR_SHAPE;
+  if (M > kIntMax || V_r > kIntMax) return TP_ERR_UNSUPPORTED;
+  if (!aligned(logits, 4) || !aligned(max_val, 4) || !aligned(max_idx, 8)) return TP_ERR_ALIGN;
+  const bool vec = V_r % 4 == 0 && aligned(logits, 16);
+  return tpl::vocab_argmax_local(logits, M, V_r, vocab_offset, max_val, max_idx, vec, as_stream(stream));
+}
+
+tp_status tp_vocab_argmax_reduce(const float* const* vals, const int64_t* const* idxs, int64_t R,
+                                 int64_t M, float* out_val, int64_t* out_idx, void* stream) {
+  if (!vals || !idxs || !out_val || !out_idx) return TP_ERR_NULL;
+  if (R < 1 || R > tpl::kMaxArgmaxRanks || M <= 0) return TP_ERR_SHAPE;
+  for (int64_t r = 0; r < R; ++r) {
+    if (!vals[r] || !idxs[r]) return TP_ERR_NULL;
+    if (!aligned(vals[r], 4) || !aligned(idxs[r], 8)) return TP_ERR_ALIGN;
+  }
+  if (!aligned(out_val, 4) || !aligned(out_idx, 8)) return TP_ERR_ALIGN;
+  return tpl::vocab_argmax_reduce(vals, idxs, (int)R, M, out_val, out_idx, as_stream(stream));
 }
 
 tp_status tp_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t N, float eps,

@@ -124,6 +124,10 @@ CONFIGS = {
     "decode_attn_tp16_rep": Config(name="decode_attn_tp16_rep", seed=106, tp=16, hidden=4096,
                                    tokens=(1,), n_q=32, n_kv=8, head_dim=128, kv_len=2048,
                                    batch=32),
+    # Vocab-parallel lm_head at TP=8 (128256-token vocab, 16032 rows per rank),
+    # greedy choice of the next token for 1 and 8 sequences.
+    "lm_head_tp8": Config(name="lm_head_tp8", seed=107, tp=8, hidden=8192, tokens=(1, 8),
+                          extra={"vocab": 128256}),
     # GPT-style GELU MLP at TP=8, 4x expansion, all 8 ranks + in-HBM reduce.
     "gelu_mlp_tp8": Config(name="gelu_mlp_tp8", seed=105, tp=8, hidden=12288,
                            tokens=(2048,), inter=49152, act="gelu"),

@@ -28,7 +28,8 @@ from __future__ import annotations
 import torch
 
 from . import (column_linear, column_linear_act, local_attention, kv_append, reduce_partials,
-               reduce_partials_rmsnorm, rmsnorm, row_linear_partial, swiglu_local)
+               reduce_partials_rmsnorm, rmsnorm, row_linear_partial, swiglu_local,
+               vocab_argmax_local, vocab_argmax_reduce)
 
 
 class MlpShard:
@@ -172,3 +173,24 @@ class LayerShard:
             self.mlp_partial(h, mlp_parts[rank])
         reduce_partials(mlp_parts, residual=h, out=y)
         return y
+
+
+class VocabShard:
+    """One rank's block of a vocab-parallel lm_head (P1 "lm_head 怎么处理"):
+    ``w`` is the rank's ``[V_r, H]`` rows of the ``[V, H]`` lm_head, starting at
+    vocab id ``offset``.  ``local_greedy`` gives the rank's float32 logits and
+    its (largest logit, global id) per token; ``greedy`` combines all ranks'
+    pairs (the all-gather's arithmetic) into the next token ids."""
+
+    def __init__(self, w: torch.Tensor, offset: int, max_tokens: int):
+        self.w, self.offset = w, offset
+        self.logits = torch.empty((max_tokens, w.shape[0]), dtype=torch.float32, device=w.device)
+
+    def local_greedy(self, h: torch.Tensor):
+        z = self.logits[:h.shape[0]]
+        row_linear_partial(h, self.w, out=z)     # fp32 output of h @ w.T
+        return vocab_argmax_local(z, self.offset)
+
+    @staticmethod
+    def greedy(pairs):
+        return vocab_argmax_reduce([p[0] for p in pairs], [p[1] for p in pairs])

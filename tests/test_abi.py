@@ -187,6 +187,28 @@ def test_fused_entry_validation(lib):
     assert g(odd, 2, None, P, P, P, 4, 8, 1e-5, 1, S) == ALIGN
 
 
+@no_gpu
+def test_argmax_validation(lib):
+    f = lib.tp_vocab_argmax_local
+    assert f(None, 4, 100, 0, P, P, S) == NULL
+    assert f(P, 4, 100, 0, None, P, S) == NULL
+    assert f(P, 0, 100, 0, P, P, S) == SHAPE
+    assert f(P, 4, 0, 0, P, P, S) == SHAPE
+    assert f(P, 4, 100, -1, P, P, S) == SHAPE
+    assert f(P, 4, 1 << 31, 0, P, P, S) == UNSUPPORTED
+    assert f(P + 2, 4, 100, 0, P, P, S) == ALIGN
+    assert f(P, 4, 100, 0, P, P + 4, S) == ALIGN              # int64 ids need 8-byte alignment
+    g = lib.tp_vocab_argmax_reduce
+    va = (ctypes.c_void_p * 2)(P, P)
+    assert g(None, va, 2, 4, P, P, S) == NULL
+    assert g(va, va, 0, 4, P, P, S) == SHAPE
+    assert g(va, va, 65, 4, P, P, S) == SHAPE
+    assert g(va, va, 2, 0, P, P, S) == SHAPE
+    assert g(va, (ctypes.c_void_p * 2)(P, None), 2, 4, P, P, S) == NULL
+    assert g(va, (ctypes.c_void_p * 2)(P, P + 4), 2, 4, P, P, S) == ALIGN
+    assert g(va, va, 2, 4, P, P + 4, S) == ALIGN
+
+
 # ---------------------------------------------------------------------------
 # host-side shard slicing of the binding (CPU tensors; pure indexing)
 # ---------------------------------------------------------------------------

@@ -401,6 +401,62 @@ def test_gqa_replication():
 
 
 # ---------------------------------------------------------------------------
+# Vocab-parallel greedy argmax (P1 "lm_head 怎么处理")
+# ---------------------------------------------------------------------------
+
+def _loop_argmax(row, offset):
+    best_v, best_i = -math.inf, None
+    for j, z in enumerate(row):
+        z = -math.inf if math.isnan(z) else z
+        if best_i is None or z > best_v:
+            best_v, best_i = z, j
+    return best_v, best_i + offset
+
+
+def check_vocab_argmax():
+    rng = np.random.default_rng(41)
+    z = rng.standard_normal((6, 37))
+    z[1, 30] = z[1, 5] = z[1].max() + 1.0              # tie: the lower id wins
+    z[2, :] = np.nan; z[2, 11] = -np.inf                # no number but -inf at 11
+    z[3, :] = np.nan                                    # nothing: id 0, value -inf
+    z[4, 0] = np.nan; z[4, 9] = 50.0                    # NaN never wins
+    z[5, 3] = -0.0; z[5, :] = np.minimum(z[5, :], -1.0); z[5, 3] = -0.0; z[5, 8] = 0.0   # -0 == +0
+    v, i = O.vocab_argmax_local(z, 100)
+    for m in range(6):
+        lv, li = _loop_argmax(z[m], 100)
+        assert v[m] == lv and i[m] == li, (m, v[m], i[m], lv, li)
+    assert i[1] == 105 and i[2] == 100 and i[3] == 100 and i[4] == 109 and i[5] == 103
+    # sharding the vocab and combining the ranks' pairs gives the full argmax,
+    # including maxima tied across ranks (the lower rank's block wins)
+    V = 48
+    z = rng.standard_normal((5, V))
+    z[0, 7] = z[0, 40] = 9.0
+    z[1, 13] = z[1, 12] = 9.0
+    z[2, 47] = 9.0
+    for R in (1, 2, 3, 4, 8, 16):
+        b = V // R
+        pairs = [O.vocab_argmax_local(z[:, r * b:(r + 1) * b], r * b) for r in range(R)]
+        gv, gi = O.vocab_argmax_reduce([p[0] for p in pairs], [p[1] for p in pairs])
+        fv, fi = O.vocab_argmax_local(z, 0)
+        assert np.array_equal(gi, fi) and np.array_equal(gv, fv)
+        assert gi[0] == 7 and gi[1] == 12 and gi[2] == 47
+    # end to end through the lm_head: integer-valued h and W with duplicated
+    # vocab rows (equal logits in different ranks' blocks)
+    h = rng.integers(-3, 4, (4, 16)).astype(np.float64)
+    w = rng.integers(-3, 4, (32, 16)).astype(np.float64)
+    w[25] = w[3] = 3.0 * np.sign(h[0] + 0.5)            # the same, largest logit for row 0
+    for R in (1, 2, 4, 8):
+        sv, si = O.greedy_token_sharded(h, w, R)
+        fv, fi = O.greedy_token(h, w)
+        assert np.array_equal(si, fi) and np.array_equal(sv, fv)
+    assert fi[0] == 3
+
+
+def test_vocab_argmax():
+    check_vocab_argmax()
+
+
+# ---------------------------------------------------------------------------
 # bf16 rounding used by the storage-faithful mode
 # ---------------------------------------------------------------------------
 
@@ -506,8 +562,33 @@ def _mut_kv_heads_modulo(n_q, n_kv, r, R):
     return [r % n_kv]
 
 
+def _mut_argmax_last(logits, vocab_offset=0):
+    z = np.asarray(logits, np.float64)
+    z = np.where(np.isnan(z), -np.inf, z)
+    n = z.shape[-1]
+    j = n - 1 - np.argmax(z[..., ::-1], axis=-1)          # last maximum instead of the first
+    return np.take_along_axis(z, j[..., None], axis=-1)[..., 0], j.astype(np.int64) + vocab_offset
+
+
+def _mut_argmax_nan_wins(logits, vocab_offset=0):
+    z = np.asarray(logits, np.float64)
+    j = np.argmax(z, axis=-1)                             # numpy's argmax picks a NaN
+    return np.take_along_axis(z, j[..., None], axis=-1)[..., 0], j.astype(np.int64) + vocab_offset
+
+
+def _mut_reduce_later_rank(vals, ids):
+    best_v = np.array(vals[0], np.float64); best_i = np.array(ids[0], np.int64)
+    for v, i in zip(vals[1:], ids[1:]):
+        take = np.asarray(v) >= best_v
+        best_v = np.where(take, v, best_v); best_i = np.where(take, i, best_i)
+    return best_v, best_i
+
+
 MUTATIONS = [
     ("kv_heads_of_rank", _mut_kv_heads_modulo),
+    ("vocab_argmax_local", _mut_argmax_last),
+    ("vocab_argmax_local", _mut_argmax_nan_wins),
+    ("vocab_argmax_reduce", _mut_reduce_later_rank),
     ("linear", _mut_linear_transposed),
     ("row_shard", _mut_row_shard_wrong_axis),
     ("reduce_partials", _mut_reduce_drops_residual),
@@ -524,7 +605,7 @@ MUTATIONS = [
 
 ALL_CHECKS = [check_worked_example, check_linear_bruteforce, check_sharding_invariants,
               check_toy_mlp_bitexact, check_activations, check_rmsnorm, check_attention,
-              check_layer_sharded_equals_unsharded, check_gqa_replication]
+              check_layer_sharded_equals_unsharded, check_gqa_replication, check_vocab_argmax]
 
 
 @pytest.mark.parametrize("name,fn", MUTATIONS, ids=[f"{n}:{f.__name__}" for n, f in MUTATIONS])
