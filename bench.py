@@ -12,8 +12,8 @@ are computed once before timing.  Inputs are seeded synthetic tensors already
 resident in HBM.  Prints ONE JSON line.
 
 Secondary figures (same line, key "decode"): the decode MLP shard at TP=8
-(M = 1, 8, 64), the decode attention shard at TP=4, the same attention at
-TP=16 with replicated KV heads and the vocab-parallel lm_head shard with its
+(M = 1, 8, 64), the decode attention shard at TP=4 (contiguous and paged
+cache), the same attention at TP=16 with replicated KV heads and the vocab-parallel lm_head shard with its
 greedy argmax (TP=8), timed over rotating
 copies of the weights/caches so that the 256 MB Infinity Cache cannot hold
 the working set between steps (also as HIP-graph replays, "graph_ms").
@@ -340,6 +340,7 @@ def decode_figures(steps=30, warmup=5, copies=4):
     out["attn_tp4_B32_L2048"] = {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
                                  "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS, "graph_ms": gms}
     out["attn_tp16_rep_B32_L2048"] = _replicated_attn_figure(steps, warmup, copies)
+    out["attn_tp4_paged_B32_L2048"] = _paged_attn_figure(steps, warmup, copies)
     out.update(_lm_head_figures(steps, warmup))
     return out
 
@@ -362,6 +363,38 @@ def _lm_head_figures(steps, warmup, copies=2):
         out[f"lm_head_tp8_M{M}"] = {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
                                     "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS}
     return out
+
+
+def _paged_attn_figure(steps, warmup, copies, bs=16):
+    """Rank 0's decode attention shard of config decode_attn_tp4 with a paged
+    cache: block size 16, physical blocks shuffled, every sequence at the full
+    2048 keys (the contiguous figure's byte count)."""
+    c = I.config("decode_attn_tp4")
+    H, R, D, B, L = c.hidden, c.tp, c.head_dim, c.batch, c.kv_len
+    hq, hkv = c.n_q // R, c.n_kv // R
+    nblk = L // bs
+    x = I.normal(c.seed, "x", (B, H)).dev.to(DEV)
+    wqkv = I.normal(c.seed, "wqkv", ((hq + 2 * hkv) * D, H), c.w_std).dev
+    wo = I.normal(c.seed, "wo", (H, hq * D), c.w_std).dev
+    kc = I.normal(c.seed, "kcache", (B * nblk, bs, hkv, D)).dev
+    vc = I.normal(c.seed, "vcache", (B * nblk, bs, hkv, D)).dev
+    table = torch.from_numpy(np.random.default_rng(c.seed).permutation(B * nblk).astype(np.int32))
+    table = table.reshape(B, nblk).to(DEV)
+    lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    sets = [(AttnShard(wqkv.to(DEV), wo.to(DEV), hq, hkv, D, B), kc.to(DEV), vc.to(DEV),
+             torch.empty((B, H), dtype=torch.float32, device=DEV)) for _ in range(copies)]
+
+    def step(j):
+        a, k_, v_, P = sets[j]
+        a.decode_partial_paged(x, k_, v_, table, lens, L, P)
+
+    fns = [(lambda j=j: step(j)) for j in range(copies)]
+    gms = _graph_ms(fns, steps, warmup)
+    ms = _median_ms(lambda i: fns[i % copies](), steps, warmup)
+    byts = (wqkv.numel() + wo.numel() + kc.numel() + vc.numel()) * 2 + B * H * 2 + B * H * 4
+    fl = 2.0 * B * H * (hq + 2 * hkv) * D + 4.0 * B * hq * L * D + 2.0 * B * hq * D * H
+    return {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
+            "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS, "graph_ms": gms}
 
 
 def _replicated_attn_figure(steps, warmup, copies):

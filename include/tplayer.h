@@ -208,6 +208,53 @@ tp_status tp_rmsnorm(const void* x, const void* gamma, void* y,
                      int64_t M, int64_t N, float eps, tp_dtype dt, void* stream);
 
 /*
+ * Decode attention over the rank's local heads with a paged KV cache (P1
+ * "Tensor parallel 对 KV cache 的影响": every rank keeps a KV pool holding only
+ * its own heads; the block table is the same on all ranks because blocks are
+ * allotted along the token axis; each rank reads the same logical blocks'
+ * physical blocks, its heads only).  One query token per sequence:
+ *     o[b,h,:] = softmax_t(scale * q[b,h,:] . K_b[t,h/G,:]) V_b[t,h/G,:],  t < L_b
+ * where L_b = context_lens[b] and key t of sequence b is slot t % block_size
+ * of physical block block_table[b * table_stride + t / block_size]:
+ *   q : element (b,h,d) at q[b*qs[0] + h*qs[1] + d]          bf16
+ *   k_pool, v_pool : element (blk,slot,j,d) at pool[blk*ps[0] + slot*ps[1] + j*ps[2] + d]
+ *   o : element (b,h,d) at o[b*os[0] + h*os[1] + d]          bf16
+ *   block_table : int32 [B, table_stride] device; context_lens : int32 [B] device
+ *   1 <= context_lens[b] <= max_context_len (values outside are clamped into
+ *   that range); table entries outside [0, num_blocks) read as zero K/V.
+ *   table_stride >= ceil(max_context_len / block_size) (TP_ERR_SHAPE).
+ *   dt must be TP_BF16, D = 128, block_size a multiple of 16, G = Hq/Hkv <= 32
+ *   (TP_ERR_UNSUPPORTED otherwise).
+ *   workspace: device scratch of tp_paged_attention_workspace(...) bytes (NULL
+ *   when 0), caller-owned, used only during the call; overlapping calls must
+ *   not share one.
+ */
+tp_status tp_paged_attention_decode(const void* q, const int64_t qs[2], const void* k_pool,
+                                    const void* v_pool, const int64_t ps[3], int64_t num_blocks,
+                                    const int32_t* block_table, int64_t table_stride,
+                                    const int32_t* context_lens, int64_t max_context_len,
+                                    int64_t block_size, void* o, const int64_t os[2], int64_t B,
+                                    int64_t Hq, int64_t Hkv, int64_t D, float scale, tp_dtype dt,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+size_t tp_paged_attention_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_context_len,
+                                    int64_t block_size);
+
+/*
+ * Store the current decode token's k and v of every sequence b in its paged
+ * slot, position context_lens[b] - 1 (the same P1 section: the rank's pool
+ * holds only its heads):
+ *   k_new, v_new : element (b,j,d) at k_new[b*new_stride + j*D + d]   bf16
+ *   pools, block_table, context_lens as in tp_paged_attention_decode.
+ * Sequences whose position or table entry is out of range are skipped.
+ */
+tp_status tp_paged_kv_append(const void* k_new, const void* v_new, int64_t new_stride, void* k_pool,
+                             void* v_pool, const int64_t ps[3], int64_t num_blocks,
+                             const int32_t* block_table, int64_t table_stride,
+                             const int32_t* context_lens, int64_t B, int64_t Hkv, int64_t D,
+                             int64_t block_size, tp_dtype dt, void* stream);
+
+/*
  * Greedy token choice of a vocab-parallel lm_head (P1 "lm_head 怎么处理": the
  * lm_head is split by vocab rows, column-parallel; under greedy decoding each
  * rank takes the largest logit of its vocab block and an all-gather /

@@ -48,7 +48,8 @@ __all__ = [
     "column_linear", "row_linear_partial", "reduce_partials", "concat_columns",
     "silu", "gelu", "local_activation", "rmsnorm", "attention", "qkv_shard",
     "kv_heads_of_rank", "kv_cache_bytes_per_rank", "vocab_argmax_local", "vocab_argmax_reduce",
-    "greedy_token", "greedy_token_sharded",
+    "greedy_token", "greedy_token_sharded", "paged_gather", "paged_decode_attention",
+    "paged_append",
     "mlp_unsharded", "mlp_rank_partial", "attention_block_unsharded",
     "attention_rank_partial", "layer_unsharded", "layer_sharded",
 ]
@@ -264,6 +265,46 @@ def qkv_shard(wq, wk, wv, r: int, R: int, head_dim: int):
     heads = kv_heads_of_rank(n_q, n_kv, r, R)
     kv_rows = np.concatenate([np.arange(j * head_dim, (j + 1) * head_dim) for j in heads])
     return np.concatenate([column_shard(wq, r, R), wk[kv_rows], wv[kv_rows]], axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Paged KV cache (P1 "Tensor parallel 对 KV cache 的影响": each rank's KV pool
+# holds only its own heads; the block table is the same on every rank)
+# ---------------------------------------------------------------------------
+
+def paged_gather(pool, table_row, length: int, block_size: int):
+    """The first ``length`` key rows of one sequence, ``[length, Hkv, D]``:
+    key t is slot ``t % block_size`` of physical block
+    ``table_row[t // block_size]`` of ``pool [num_blocks, block_size, Hkv, D]``."""
+    pool = np.asarray(pool, np.float64)
+    rows = [pool[int(table_row[t // block_size]), t % block_size] for t in range(length)]
+    return np.stack(rows, axis=0)
+
+
+def paged_decode_attention(q, k_pool, v_pool, table, lens, block_size: int, scale=None):
+    """Decode attention (one query token per sequence, seeing all its keys)
+    over a paged cache.  q ``[B, Hq, D]`` -> o ``[B, Hq, D]``."""
+    q = np.asarray(q, np.float64)
+    B, Hq, D = q.shape
+    out = np.zeros_like(q)
+    for b in range(B):
+        L = int(lens[b])
+        k = paged_gather(k_pool, table[b], L, block_size)
+        v = paged_gather(v_pool, table[b], L, block_size)
+        out[b] = attention(q[b][None, None], k[None], v[None], causal=True, scale=scale)[0, 0]
+    return out
+
+
+def paged_append(k_pool, v_pool, k_new, v_new, table, lens, block_size: int):
+    """Copies of the pools with each sequence's new k/v ``[B, Hkv, D]`` stored
+    at position ``lens[b] - 1``."""
+    kp = np.array(k_pool, np.float64); vp = np.array(v_pool, np.float64)
+    for b in range(len(lens)):
+        t = int(lens[b]) - 1
+        blk = int(table[b][t // block_size])
+        kp[blk, t % block_size] = k_new[b]
+        vp[blk, t % block_size] = v_new[b]
+    return kp, vp
 
 
 # ---------------------------------------------------------------------------

@@ -10,8 +10,8 @@ fallback -- if the library is missing the calls raise.
 Entry points (same names as the C ABI, without the ``tp_`` prefix):
 ``column_linear``, ``column_linear_act``, ``row_linear_partial``,
 ``swiglu_local``, ``local_attention``, ``kv_append``, ``reduce_partials``,
-``reduce_partials_rmsnorm``, ``rmsnorm``, ``vocab_argmax_local``,
-``vocab_argmax_reduce``.
+``reduce_partials_rmsnorm``, ``rmsnorm``, ``paged_attention_decode``,
+``paged_kv_append``, ``vocab_argmax_local``, ``vocab_argmax_reduce``.
 Weights use the nn.Linear layout ``[out_features, in_features]``.
 """
 from __future__ import annotations
@@ -26,6 +26,7 @@ __all__ = [
     "column_linear", "column_linear_act", "row_linear_partial", "swiglu_local",
     "local_attention", "local_attention_workspace", "kv_append", "reduce_partials",
     "reduce_partials_rmsnorm", "rmsnorm", "vocab_argmax_local", "vocab_argmax_reduce",
+    "paged_attention_decode", "paged_attention_workspace", "paged_kv_append",
     "shard_column", "shard_row", "shard_qkv", "kv_heads_of_rank", "kv_cache_bytes_per_rank",
     "F32", "BF16", "ACT_NONE", "ACT_SWIGLU", "ACT_GELU",
 ]
@@ -61,6 +62,13 @@ _SIGS = {
     "tp_reduce_partials_rmsnorm": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, _vp, _vp, _vp, _vp,
                                                   _i64, _i64, ctypes.c_float, ctypes.c_int, _vp]),
     "tp_rmsnorm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, ctypes.c_float, ctypes.c_int, _vp]),
+    "tp_paged_attention_decode": (ctypes.c_int, [_vp, _i64p, _vp, _vp, _i64p, _i64, _vp, _i64, _vp,
+                                                 _i64, _i64, _vp, _i64p, _i64, _i64, _i64, _i64,
+                                                 ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t,
+                                                 _vp]),
+    "tp_paged_attention_workspace": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
+    "tp_paged_kv_append": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64p, _i64, _vp, _i64, _vp,
+                                          _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
     "tp_vocab_argmax_local": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "tp_vocab_argmax_reduce": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64, _i64,
                                               _vp, _vp, _vp]),
@@ -352,6 +360,75 @@ def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, out: torch.
     _check("tp_rmsnorm", lib().tp_rmsnorm(x.data_ptr(), gamma.data_ptr(), out.data_ptr(), M, N,
                                           float(eps), _DT[x.dtype], _stream(x)))
     return out
+
+
+def _paged_common(block_table, context_lens, k_pool, v_pool):
+    _contig(block_table, "block_table", (torch.int32,))
+    _contig(context_lens, "context_lens", (torch.int32,))
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _dev(t, n)
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{n} must be [num_blocks, block_size, Hkv, D] with a contiguous last dim")
+    if k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
+        raise ValueError("k_pool and v_pool must have the same shape and strides")
+    if block_table.dim() != 2 or context_lens.shape != (block_table.shape[0],):
+        raise ValueError("block_table must be [B, max_blocks] and context_lens [B]")
+    return _arr3([k_pool.stride(0), k_pool.stride(1), k_pool.stride(2)])
+
+
+def paged_attention_workspace(B, Hq, Hkv, max_context_len, block_size) -> int:
+    return int(lib().tp_paged_attention_workspace(B, Hq, Hkv, max_context_len, block_size))
+
+
+def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                           block_table: torch.Tensor, context_lens: torch.Tensor,
+                           max_context_len: int, scale: float | None = None,
+                           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Decode attention over a paged KV cache.  q ``[B, Hq, D]`` (last dim
+    contiguous); pools ``[num_blocks, block_size, Hkv, D]``; block_table
+    ``[B, max_blocks]`` int32; context_lens ``[B]`` int32 (keys per sequence,
+    the current token included).  Returns o ``[B, Hq, D]``."""
+    _dev(q, "q")
+    if q.dim() != 3 or q.stride(2) != 1:
+        raise ValueError("q must be [B, Hq, D] with a contiguous last dimension")
+    ps = _paged_common(block_table, context_lens, k_pool, v_pool)
+    B, Hq, D = q.shape
+    nb, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have one row per sequence")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    if out.dim() != 3 or out.stride(2) != 1:
+        raise ValueError("out must be [B, Hq, D] with a contiguous last dimension")
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    need = paged_attention_workspace(B, Hq, Hkv, max_context_len, bs)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    qs = (ctypes.c_int64 * 2)(q.stride(0), q.stride(1))
+    os_ = (ctypes.c_int64 * 2)(out.stride(0), out.stride(1))
+    _check("tp_paged_attention_decode", lib().tp_paged_attention_decode(
+        q.data_ptr(), qs, k_pool.data_ptr(), v_pool.data_ptr(), ps, nb, block_table.data_ptr(),
+        block_table.stride(0), context_lens.data_ptr(), int(max_context_len), bs, out.data_ptr(), os_,
+        B, Hq, Hkv, D, float(scale), _DT[q.dtype], workspace.data_ptr() if need else None, need,
+        _stream(q)))
+    return out
+
+
+def paged_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
+                    v_pool: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor):
+    """Store each sequence's current k/v (``[B, Hkv, D]`` views with a shared
+    row stride) at position ``context_lens[b] - 1`` of the paged pools."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, n)
+    ps = _paged_common(block_table, context_lens, k_pool, v_pool)
+    B, H, D = k_new.shape
+    if k_new.stride(2) != 1 or k_new.stride(1) != D or v_new.stride() != k_new.stride():
+        raise ValueError("k_new/v_new must be [B, Hkv, D] rows of one stride")
+    _check("tp_paged_kv_append", lib().tp_paged_kv_append(
+        k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_pool.data_ptr(), v_pool.data_ptr(), ps,
+        k_pool.shape[0], block_table.data_ptr(), block_table.stride(0), context_lens.data_ptr(), B, H,
+        D, k_pool.shape[1], _DT[k_new.dtype], _stream(k_new)))
 
 
 def vocab_argmax_local(logits: torch.Tensor, vocab_offset: int = 0):

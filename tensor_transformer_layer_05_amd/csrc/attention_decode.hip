@@ -23,6 +23,17 @@
 // are in flight while the current one is computed, with an online softmax
 // across tiles.  There is no barrier in the loop; the waves' (max, sum, O^T)
 // are merged through LDS at the end.
+//
+// Paged variant (page P1 "Tensor parallel 对 KV cache 的影响": the block table
+// is the same on every rank, each rank's physical blocks hold only its own KV
+// heads): key t of sequence b sits in physical block table[b][t / bs], slot
+// t % bs, of the rank's K and V pools.  A workgroup first copies the table
+// entries of its key chunk to LDS; each 1 KB load (4 key rows) then lies in one
+// block (bs is a multiple of 16), so its buffer resource is based at that
+// block and bounded to it.  Sequences have their own lengths; entries outside
+// [0, num_blocks) read as zero instead of faulting.
+#include <algorithm>
+
 #include "common.h"
 
 namespace tpl {
@@ -31,13 +42,19 @@ constexpr int kDecD = 128;           // head dimension handled
 constexpr int kDecTile = 32;         // keys per tile
 constexpr int kDecMaxG = 32;         // query heads per KV head (MFMA columns)
 
+constexpr int kPagedMaxBlocks = 512;   // table entries one workgroup stages in LDS
+
 struct DecArgs {
   const uint16_t* q; int64_t qs0, qs2;          // (b, h) strides (s = 0)
+  // contiguous: element (b, t, j, d) at k[b*ks0 + t*ks1 + j*ks2 + d];
+  // paged:      element (block, slot, j, d) at k[block*ks0 + slot*ks1 + j*ks2 + d]
   const uint16_t* k; const uint16_t* v; int64_t ks0, ks1, ks2;
   uint16_t* o; int64_t os0, os2;
   float* ws;                                    // partials, or nullptr if one chunk
   int Skv, Hq, Hkv, G, nsplit, chunk;           // chunk: keys per workgroup (multiple of 4*32)
   float scale_log2;                             // softmax scale * log2(e)
+  // paged only
+  const int* table; int64_t tstride; const int* lens; int bs; int64_t nblocks;
 };
 
 namespace {
@@ -54,22 +71,34 @@ __device__ __forceinline__ float dec_pair_sum(float x) {
 }
 }  // namespace
 
+template <bool PAGED>
 __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   constexpr int TE = kDecTile * kDecD;                 // bf16 elements of one K (or V) tile
   constexpr int WRING = 2 * 2 * TE;                    // per wave: 2 stages x (K, V)
   __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * WRING];   // 128 KB
   __shared__ float wstat[4][kDecMaxG][2];
+  __shared__ int tbl[PAGED ? kPagedMaxBlocks : 1];
 
   const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, hl = lane >> 5;
   const int G = a.G;
+  // keys of this sequence (paged: its own length, clamped into [1, Skv])
+  const int L = PAGED ? min(max(a.lens[b], 1), a.Skv) : a.Skv;
   const int wkeys = a.chunk / 4;                       // keys per wave (multiple of 32)
   const int tw = split * a.chunk + wave * wkeys;       // first key of this wave
-  const int nt = max(0, min(wkeys, a.Skv - tw) + kDecTile - 1) / kDecTile;   // tiles with keys
+  const int nt = max(0, min(wkeys, L - tw) + kDecTile - 1) / kDecTile;   // tiles with keys
 
-  const uint32_t nrec = (uint32_t)(((int64_t)(a.Skv - 1) * a.ks1 + kDecD) * 2);
+  const int blk0 = PAGED ? split * a.chunk / a.bs : 0;   // first table entry of the chunk
+  if constexpr (PAGED) {
+    const int nb = min((split * a.chunk + a.chunk - 1) / a.bs, (L - 1) / a.bs) - blk0 + 1;
+    for (int e = tid; e < nb; e += 256) tbl[e] = a.table[(int64_t)b * a.tstride + blk0 + e];
+    __syncthreads();
+  }
+
+  const uint32_t nrec = PAGED ? (uint32_t)(((int64_t)(a.bs - 1) * a.ks1 + kDecD) * 2)
+                              : (uint32_t)(((int64_t)(L - 1) * a.ks1 + kDecD) * 2);
   const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.k + b * a.ks0 + j * a.ks2), 0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
@@ -84,13 +113,31 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     for (int u = 0; u < kDecTile / 4; ++u) {
       const int row = 4 * u + lr;
       const int t = tw + i * kDecTile + row;
-      const bool ok = t < a.Skv && i < nt;
-      const uint32_t rb = (uint32_t)((int64_t)t * a.ks1 * 2);
+      const bool ok = t < L && i < nt;
       const int kc = lp ^ (row & 15), vc = lp ^ (4 * (row & 3));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TPL_DLDS void*)(kd + u * 4 * kDecD), 16,
-                                               ok ? rb + (uint32_t)kc * 16u : 0x80000000u, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TPL_DLDS void*)(vd + u * 4 * kDecD), 16,
-                                               ok ? rb + (uint32_t)vc * 16u : 0x80000000u, 0, 0, 0);
+      if constexpr (PAGED) {
+        // rows t0 .. t0+3 of this load share one block (bs % 16 == 0)
+        const int t0 = tw + i * kDecTile + 4 * u;
+        int pb = (t0 < L && i < nt) ? tbl[t0 / a.bs - blk0] : -1;
+        pb = __builtin_amdgcn_readfirstlane(pb);
+        const bool bok = pb >= 0 && pb < a.nblocks;
+        const int64_t base = (bok ? pb * a.ks0 : 0) + j * a.ks2;
+        const __amdgpu_buffer_rsrc_t kb = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.k + base), 0, bok ? nrec : 0u, 0x00020000);
+        const __amdgpu_buffer_rsrc_t vb = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.v + base), 0, bok ? nrec : 0u, 0x00020000);
+        const uint32_t rb = (uint32_t)((int64_t)(t % a.bs) * a.ks1 * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kb, (TPL_DLDS void*)(kd + u * 4 * kDecD), 16,
+                                                 ok ? rb + (uint32_t)kc * 16u : 0x80000000u, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vb, (TPL_DLDS void*)(vd + u * 4 * kDecD), 16,
+                                                 ok ? rb + (uint32_t)vc * 16u : 0x80000000u, 0, 0, 0);
+      } else {
+        const uint32_t rb = (uint32_t)((int64_t)t * a.ks1 * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TPL_DLDS void*)(kd + u * 4 * kDecD), 16,
+                                                 ok ? rb + (uint32_t)kc * 16u : 0x80000000u, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TPL_DLDS void*)(vd + u * 4 * kDecD), 16,
+                                                 ok ? rb + (uint32_t)vc * 16u : 0x80000000u, 0, 0, 0);
+      }
     }
   };
   issue(0);
@@ -137,7 +184,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = tw + i * kDecTile + 8 * (r >> 2) + 4 * hl + (r & 3);
-      const float x = t < a.Skv ? st[r] * a.scale_log2 : -INFINITY;
+      const float x = t < L ? st[r] * a.scale_log2 : -INFINITY;
       st[r] = x;
       mx = fmaxf(mx, x);
     }
@@ -301,9 +348,90 @@ tp_status attn_decode(const void* q, const int64_t qs[3], const void* k, const v
   a.nsplit = attn_decode_nsplit(B, Hkv, Skv);
   a.ws = a.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_decode_kernel, dim3(a.nsplit, a.Hkv, B), dim3(256), 0, s, a);
+  a.table = nullptr; a.tstride = 0; a.lens = nullptr; a.bs = 0; a.nblocks = 0;
+  hipLaunchKernelGGL(attn_decode_kernel<false>, dim3(a.nsplit, a.Hkv, B), dim3(256), 0, s, a);
   if (a.ws) hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.Hq, B), dim3(128), 0, s, a, (int)B);
   TPL_LAUNCH_CHECK("attn_decode");
+  return TP_OK;
+}
+
+// Paged decode: chunks also bounded so that one chunk's table entries fit the
+// workgroup's LDS copy.
+static int paged_chunk(int64_t B, int64_t Hkv, int64_t max_len, int64_t bs) {
+  int chunk = dec_chunk(B, Hkv, max_len);
+  const int64_t cap = (int64_t)(kPagedMaxBlocks - 1) * bs / (4 * kDecTile) * (4 * kDecTile);
+  if (chunk > cap) chunk = (int)cap;
+  return chunk;
+}
+
+int attn_paged_nsplit(int64_t B, int64_t Hkv, int64_t max_len, int64_t bs) {
+  const int64_t chunk = paged_chunk(B, Hkv, max_len, bs);
+  return (int)((max_len + chunk - 1) / chunk);
+}
+
+size_t attn_paged_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_len, int64_t bs) {
+  const int ns = attn_paged_nsplit(B, Hkv, max_len, bs);
+  if (ns == 1) return 0;
+  return (size_t)(B * Hq * ns) * (2 + kDecD) * sizeof(float);
+}
+
+tp_status attn_decode_paged(const void* q, const int64_t qs[2], const void* kp, const void* vp,
+                            const int64_t ps[3], int64_t nblocks, const int* table, int64_t tstride,
+                            const int* lens, int64_t max_len, int64_t bs, void* o,
+                            const int64_t os[2], int64_t B, int64_t Hq, int64_t Hkv, float scale,
+                            void* ws, hipStream_t s) {
+  DecArgs a;
+  a.q = static_cast<const uint16_t*>(q); a.qs0 = qs[0]; a.qs2 = qs[1];
+  a.k = static_cast<const uint16_t*>(kp); a.v = static_cast<const uint16_t*>(vp);
+  a.ks0 = ps[0]; a.ks1 = ps[1]; a.ks2 = ps[2];
+  a.o = static_cast<uint16_t*>(o); a.os0 = os[0]; a.os2 = os[1];
+  a.Skv = (int)max_len; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / Hkv);
+  if (a.G > kDecMaxG) return TP_ERR_UNSUPPORTED;
+  a.chunk = paged_chunk(B, Hkv, max_len, bs);
+  a.nsplit = attn_paged_nsplit(B, Hkv, max_len, bs);
+  a.ws = a.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.table = table; a.tstride = tstride; a.lens = lens; a.bs = (int)bs; a.nblocks = nblocks;
+  hipLaunchKernelGGL(attn_decode_kernel<true>, dim3(a.nsplit, a.Hkv, B), dim3(256), 0, s, a);
+  if (a.ws) hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.Hq, B), dim3(128), 0, s, a, (int)B);
+  TPL_LAUNCH_CHECK("attn_decode_paged");
+  return TP_OK;
+}
+
+// Write the current token's k and v of every sequence into its slot
+// (lens[b] - 1) of the paged pools; sequences whose slot or block is out of
+// range are skipped.
+__global__ __launch_bounds__(256) void paged_kv_append_kernel(
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn, int64_t new_stride,
+    uint16_t* __restrict__ kp, uint16_t* __restrict__ vp, int64_t ps0, int64_t ps1, int64_t ps2,
+    int64_t nblocks, const int* __restrict__ table, int64_t tstride, int64_t maxblk,
+    const int* __restrict__ lens, int64_t B, int64_t H, int64_t D, int64_t bs) {
+  const int64_t total = B * H * D;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t d = e % D, j = (e / D) % H, b = e / (D * H);
+    const int64_t pos = (int64_t)lens[b] - 1;
+    if (pos < 0 || pos / bs >= maxblk) continue;
+    const int64_t pb = table[b * tstride + pos / bs];
+    if (pb < 0 || pb >= nblocks) continue;
+    const int64_t src = b * new_stride + j * D + d;
+    const int64_t dst = pb * ps0 + (pos % bs) * ps1 + j * ps2 + d;
+    kp[dst] = kn[src];
+    vp[dst] = vn[src];
+  }
+}
+
+tp_status paged_kv_append(const void* kn, const void* vn, int64_t new_stride, void* kp, void* vp,
+                          const int64_t ps[3], int64_t nblocks, const int* table, int64_t tstride,
+                          int64_t maxblk, const int* lens, int64_t B, int64_t H, int64_t D, int64_t bs,
+                          hipStream_t s) {
+  const int64_t total = B * H * D;
+  const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(paged_kv_append_kernel, dim3(grid), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(kn), static_cast<const uint16_t*>(vn), new_stride,
+                     static_cast<uint16_t*>(kp), static_cast<uint16_t*>(vp), ps[0], ps[1], ps[2],
+                     nblocks, table, tstride, maxblk, lens, B, H, D, bs);
+  TPL_LAUNCH_CHECK("paged_kv_append");
   return TP_OK;
 }
 

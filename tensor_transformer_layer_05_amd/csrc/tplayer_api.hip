@@ -54,6 +54,17 @@ void set_hip_error(const char* where, hipError_t e) {
 
 tp_status vocab_argmax_local(const float* logits, int64_t M, int64_t V, int64_t offset, float* mv,
                              int64_t* mi, bool vec, hipStream_t s);
+int attn_paged_nsplit(int64_t B, int64_t Hkv, int64_t max_len, int64_t bs);
+size_t attn_paged_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_len, int64_t bs);
+tp_status attn_decode_paged(const void* q, const int64_t qs[2], const void* kp, const void* vp,
+                            const int64_t ps[3], int64_t nblocks, const int* table, int64_t tstride,
+                            const int* lens, int64_t max_len, int64_t bs, void* o,
+                            const int64_t os[2], int64_t B, int64_t Hq, int64_t Hkv, float scale,
+                            void* ws, hipStream_t s);
+tp_status paged_kv_append(const void* kn, const void* vn, int64_t new_stride, void* kp, void* vp,
+                          const int64_t ps[3], int64_t nblocks, const int* table, int64_t tstride,
+                          int64_t maxblk, const int* lens, int64_t B, int64_t H, int64_t D, int64_t bs,
+                          hipStream_t s);
 tp_status vocab_argmax_reduce(const float* const* vals, const int64_t* const* idxs, int R, int64_t M,
                               float* ov, int64_t* oi, hipStream_t s);
 }  // namespace tpl
@@ -238,6 +249,73 @@ tp_status tp_reduce_partials_rmsnorm(const float* const* partials, int64_t R, co
   const tp_status st = tp_reduce_partials(partials, R, residual, y, M, N, dt, stream);
   if (st != TP_OK) return st;
   return tp_rmsnorm(y, gamma, yn, M, N, eps, dt, stream);
+}
+
+size_t tp_paged_attention_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_context_len,
+                                    int64_t block_size) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || max_context_len <= 0 || block_size < 16 ||
+      block_size % 16)
+    return 0;
+  return tpl::attn_paged_workspace(B, Hq, Hkv, max_context_len, block_size);
+}
+
+tp_status tp_paged_attention_decode(const void* q, const int64_t qs[2], const void* k_pool,
+                                    const void* v_pool, const int64_t ps[3], int64_t num_blocks,
+                                    const int32_t* block_table, int64_t table_stride,
+                                    const int32_t* context_lens, int64_t max_context_len,
+                                    int64_t block_size, void* o, const int64_t os[2], int64_t B,
+                                    int64_t Hq, int64_t Hkv, int64_t D, float scale, tp_dtype dt,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !qs || !k_pool || !v_pool || !ps || !block_table || !context_lens || !o || !os)
+    return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv || num_blocks <= 0 || max_context_len <= 0)
+    return TP_ERR_SHAPE;
+  if (!isfinite(scale)) return TP_ERR_SHAPE;
+  if (block_size <= 0 || table_stride < (max_context_len + block_size - 1) / block_size) return TP_ERR_SHAPE;
+  if (dt != TP_BF16 || D != 128 || block_size < 16 || block_size % 16) return TP_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 32 || B > 65535 || Hkv > 65535 || max_context_len > kIntMax) return TP_ERR_UNSUPPORTED;
+  if (num_blocks > kIntMax) return TP_ERR_UNSUPPORTED;
+  for (int i = 0; i < 3; ++i) {
+    if (ps[i] < 0) return TP_ERR_SHAPE;
+    if (ps[i] % 8) return TP_ERR_ALIGN;
+  }
+  for (int i = 0; i < 2; ++i) {
+    if (qs[i] < 0 || os[i] < 0) return TP_ERR_SHAPE;
+    if (qs[i] % 8 || os[i] % 4) return TP_ERR_ALIGN;
+  }
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(o, 8) ||
+      !aligned(block_table, 4) || !aligned(context_lens, 4))
+    return TP_ERR_ALIGN;
+  // one block's rows must be addressable with 31-bit byte offsets
+  if (((block_size - 1) * ps[1] + D) * 2 >= (int64_t{1} << 31)) return TP_ERR_UNSUPPORTED;
+  const size_t need = tpl::attn_paged_workspace(B, Hq, Hkv, max_context_len, block_size);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 4)) return TP_ERR_ALIGN;
+  return tpl::attn_decode_paged(q, qs, k_pool, v_pool, ps, num_blocks, block_table, table_stride,
+                                context_lens, max_context_len, block_size, o, os, B, Hq, Hkv, scale,
+                                workspace, as_stream(stream));
+}
+
+tp_status tp_paged_kv_append(const void* k_new, const void* v_new, int64_t new_stride, void* k_pool,
+                             void* v_pool, const int64_t ps[3], int64_t num_blocks,
+                             const int32_t* block_table, int64_t table_stride,
+                             const int32_t* context_lens, int64_t B, int64_t Hkv, int64_t D,
+                             int64_t block_size, tp_dtype dt, void* stream) {
+  if (!k_new || !v_new || !k_pool || !v_pool || !ps || !block_table || !context_lens) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (B <= 0 || Hkv <= 0 || D <= 0 || num_blocks <= 0 || table_stride <= 0 || block_size <= 0)
+    return TP_ERR_SHAPE;
+  if (new_stride < Hkv * D) return TP_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i)
+    if (ps[i] < 0) return TP_ERR_SHAPE;
+  if (dt != TP_BF16) return TP_ERR_UNSUPPORTED;
+  if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(k_pool, 2) || !aligned(v_pool, 2) ||
+      !aligned(block_table, 4) || !aligned(context_lens, 4))
+    return TP_ERR_ALIGN;
+  return tpl::paged_kv_append(k_new, v_new, new_stride, k_pool, v_pool, ps, num_blocks, block_table,
+                              table_stride, table_stride, context_lens, B, Hkv, D, block_size,
+                              as_stream(stream));
 }
 
 tp_status tp_vocab_argmax_local(const float* logits, int64_t M, int64_t V_r, int64_t vocab_offset,

@@ -29,7 +29,7 @@ import torch
 
 from . import (column_linear, column_linear_act, local_attention, kv_append, reduce_partials,
                reduce_partials_rmsnorm, rmsnorm, row_linear_partial, swiglu_local,
-               vocab_argmax_local, vocab_argmax_reduce)
+               vocab_argmax_local, vocab_argmax_reduce, paged_attention_decode, paged_kv_append)
 
 
 class MlpShard:
@@ -121,6 +121,28 @@ class AttnShard:
         o = self.o[:B]
         local_attention(q, kc, vc, causal=True, out=o.view(B, 1, self.n_q, self.D),
                         workspace=self._workspace(B, pos + 1, x.device))
+        row_linear_partial(o, self.wo, out=out)
+        return out
+
+    def decode_partial_paged(self, x: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                             block_table: torch.Tensor, context_lens: torch.Tensor,
+                             max_context_len: int, out: torch.Tensor):
+        """One new token per sequence with a paged cache: pools
+        ``[num_blocks, block_size, Hkv_l, D]`` holding this rank's KV heads,
+        the block table shared by all ranks; ``context_lens[b]`` counts the
+        new token, which is stored at position ``context_lens[b] - 1``."""
+        B = x.shape[0]
+        qkv = self.qkv[:B]
+        column_linear(x, self.wqkv, out=qkv)
+        q, k, v = self._views(qkv, B, 1)
+        paged_kv_append(k[:, 0], v[:, 0], k_pool, v_pool, block_table, context_lens)
+        o = self.o[:B]
+        from . import paged_attention_workspace
+        need = paged_attention_workspace(B, self.n_q, self.n_kv, max_context_len, k_pool.shape[1])
+        if need and (self.ws is None or self.ws.numel() < need):
+            self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        paged_attention_decode(q[:, 0], k_pool, v_pool, block_table, context_lens, max_context_len,
+                               out=o.view(B, self.n_q, self.D), workspace=self.ws)
         row_linear_partial(o, self.wo, out=out)
         return out
 

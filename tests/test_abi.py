@@ -187,6 +187,47 @@ def test_fused_entry_validation(lib):
     assert g(odd, 2, None, P, P, P, 4, 8, 1e-5, 1, S) == ALIGN
 
 
+def _s2(*v):
+    return (ctypes.c_int64 * 2)(*v)
+
+
+@no_gpu
+def test_paged_validation(lib):
+    f = lib.tp_paged_attention_decode
+    ps = _s3(16 * 2 * 128, 2 * 128, 128)
+
+    def call(q=P, k=P, v=P, ps=ps, nb=64, tbl=P, ts=8, lens=P, maxl=100, bs=16, o=P, B=2, Hq=8,
+             Hkv=2, D=128, scale=0.088, dt=1, ws=None, wsb=0):
+        return f(q, _s2(1024, 128), k, v, ps, nb, tbl, ts, lens, maxl, bs, o, _s2(1024, 128), B, Hq,
+                 Hkv, D, scale, dt, ws, wsb, S)
+
+    assert call(tbl=None) == NULL
+    assert call(lens=None) == NULL
+    assert call(Hq=6, Hkv=4) == SHAPE
+    assert call(nb=0) == SHAPE
+    assert call(maxl=0) == SHAPE
+    assert call(ts=6) == SHAPE                    # ceil(100 / 16) = 7 entries per row needed
+    assert call(bs=24) == UNSUPPORTED             # block size not a multiple of 16
+    assert call(bs=8, ts=13) == UNSUPPORTED
+    assert call(D=64) == UNSUPPORTED
+    assert call(dt=0) == UNSUPPORTED
+    assert call(dt=7) == DTYPE
+    assert call(Hq=66, Hkv=1) == UNSUPPORTED      # G > 32
+    assert call(ps=_s3(16 * 2 * 128, 2 * 128, 100)) == ALIGN
+    assert call(tbl=P + 2) == ALIGN
+    assert call(k=P + 8) == ALIGN
+    need = lib.tp_paged_attention_workspace(1, 8, 2, 4096, 16)
+    assert need > 0
+    assert call(B=1, maxl=4096, ts=256) == WORKSPACE
+    assert lib.tp_paged_attention_workspace(1, 8, 2, 4096, 24) == 0
+    g = lib.tp_paged_kv_append
+    assert g(None, P, 256, P, P, ps, 64, P, 8, P, 2, 2, 128, 16, 1, S) == NULL
+    assert g(P, P, 128, P, P, ps, 64, P, 8, P, 2, 2, 128, 16, 1, S) == SHAPE   # row stride < Hkv*D
+    assert g(P, P, 256, P, P, ps, 0, P, 8, P, 2, 2, 128, 16, 1, S) == SHAPE
+    assert g(P, P, 256, P, P, ps, 64, P, 8, P, 2, 2, 128, 16, 0, S) == UNSUPPORTED
+    assert g(P, P, 256, P, P, ps, 64, P + 2, 8, P, 2, 2, 128, 16, 1, S) == ALIGN
+
+
 @no_gpu
 def test_argmax_validation(lib):
     f = lib.tp_vocab_argmax_local

@@ -401,6 +401,60 @@ def test_gqa_replication():
 
 
 # ---------------------------------------------------------------------------
+# Paged KV cache (P1 "Tensor parallel 对 KV cache 的影响")
+# ---------------------------------------------------------------------------
+
+def check_paged_attention():
+    rng = np.random.default_rng(43)
+    B, Hq, Hkv, D, bs, L = 3, 4, 2, 8, 4, 10
+    nblk = (L + bs - 1) // bs
+    kc = rng.standard_normal((B, L, Hkv, D)); vc = rng.standard_normal((B, L, Hkv, D))
+    q = rng.standard_normal((B, Hq, D))
+    lens = [10, 1, 7]
+    ref = np.stack([O.attention(q[b][None, None], kc[b:b + 1, :lens[b]], vc[b:b + 1, :lens[b]],
+                                causal=True)[0, 0] for b in range(B)])
+    # identity layout: sequence b owns blocks b*nblk .. b*nblk + nblk - 1
+    pad = nblk * bs
+    kp = np.zeros((B * nblk, bs, Hkv, D)); vp = np.zeros_like(kp)
+    for b in range(B):
+        kk = np.zeros((pad, Hkv, D)); vv = np.zeros((pad, Hkv, D))
+        kk[:L] = kc[b]; vv[:L] = vc[b]
+        kp[b * nblk:(b + 1) * nblk] = kk.reshape(nblk, bs, Hkv, D)
+        vp[b * nblk:(b + 1) * nblk] = vv.reshape(nblk, bs, Hkv, D)
+    table = [[b * nblk + i for i in range(nblk)] for b in range(B)]
+    assert np.allclose(O.paged_decode_attention(q, kp, vp, table, lens, bs), ref, rtol=1e-13, atol=1e-14)
+    # shuffled physical blocks (and spare blocks of garbage) give the same result
+    perm = rng.permutation(B * nblk + 5)
+    kp2 = np.full((B * nblk + 5, bs, Hkv, D), np.nan); vp2 = np.full_like(kp2, np.nan)
+    table2 = [[int(perm[b * nblk + i]) for i in range(nblk)] for b in range(B)]
+    for b in range(B):
+        for i in range(nblk):
+            kp2[table2[b][i]] = kp[table[b][i]]; vp2[table2[b][i]] = vp[table[b][i]]
+    assert np.allclose(O.paged_decode_attention(q, kp2, vp2, table2, lens, bs), ref, rtol=1e-13,
+                       atol=1e-14)
+    # heads split over ranks, one block table: each rank's pool holds its KV
+    # heads; the ranks' outputs over their q heads make up the whole
+    for R in (1, 2):
+        parts = []
+        for r in range(R):
+            hk = O.kv_heads_of_rank(Hq, Hkv, r, R)
+            hq = list(range(r * Hq // R, (r + 1) * Hq // R))
+            parts.append(O.paged_decode_attention(q[:, hq], kp2[:, :, hk], vp2[:, :, hk], table2, lens, bs))
+        assert np.allclose(np.concatenate(parts, axis=1), ref, rtol=1e-13, atol=1e-14)
+    # append then attend: the new token is the last key
+    kn = rng.standard_normal((B, Hkv, D)); vn = rng.standard_normal((B, Hkv, D))
+    lens3 = [11, 2, 8]
+    table3 = [[*row, int(perm[-1 - b])] for b, row in enumerate(table2)]   # a 4th block each
+    kp3, vp3 = O.paged_append(kp2, vp2, kn, vn, table3, lens3, bs)
+    assert np.array_equal(kp3[table3[0][2], 2], kn[0]) and np.array_equal(vp3[table3[1][0], 1], vn[1])
+    assert np.array_equal(kp3[table3[2][1], 3], kn[2])
+
+
+def test_paged_attention():
+    check_paged_attention()
+
+
+# ---------------------------------------------------------------------------
 # Vocab-parallel greedy argmax (P1 "lm_head 怎么处理")
 # ---------------------------------------------------------------------------
 
@@ -584,7 +638,15 @@ def _mut_reduce_later_rank(vals, ids):
     return best_v, best_i
 
 
+def _mut_paged_swapped(pool, table_row, length, block_size):
+    pool = np.asarray(pool, np.float64)
+    n = len(table_row)
+    rows = [pool[int(table_row[t % n]), (t // n) % block_size] for t in range(length)]
+    return np.stack(rows, axis=0)
+
+
 MUTATIONS = [
+    ("paged_gather", _mut_paged_swapped),
     ("kv_heads_of_rank", _mut_kv_heads_modulo),
     ("vocab_argmax_local", _mut_argmax_last),
     ("vocab_argmax_local", _mut_argmax_nan_wins),
@@ -605,7 +667,8 @@ MUTATIONS = [
 
 ALL_CHECKS = [check_worked_example, check_linear_bruteforce, check_sharding_invariants,
               check_toy_mlp_bitexact, check_activations, check_rmsnorm, check_attention,
-              check_layer_sharded_equals_unsharded, check_gqa_replication, check_vocab_argmax]
+              check_layer_sharded_equals_unsharded, check_gqa_replication, check_vocab_argmax,
+              check_paged_attention]
 
 
 @pytest.mark.parametrize("name,fn", MUTATIONS, ids=[f"{n}:{f.__name__}" for n, f in MUTATIONS])
