@@ -25,8 +25,9 @@
 //    first two sub-steps, and the last sub-step's MFMAs are split around the
 //    barrier so that the next step's first fragment reads overlap them.
 //  * 256x256 tiles run 8 waves (2 per SIMD, 128x64 per wave, accumulators in
-//    128 VGPRs); 128x128 tiles run 4 waves with 2 workgroups per CU, for grids
-//    too small to fill 256 CUs with 256x256 tiles.
+//    128 VGPRs); 128x128 tiles run 4 waves with 2 workgroups per CU, and
+//    256x320 tiles 8 waves of 64x160, for grids that 256x256 tiles would
+//    leave with a mostly empty last round.
 //  * Workgroup ids are remapped so that consecutive tile ids share an XCD
 //    (one L2 per XCD), walking groups of 8 M-tiles.
 #include "common.h"
@@ -47,7 +48,7 @@ struct DmaTile {
   static constexpr int XL = BM / 8 / NW, WL = BN / 8 / NW;  // 1 KB loads per wave per step
   static constexpr int STAGE = (BM + BN) * BK;              // bf16 elements per LDS stage
   static_assert(XL * NW * 8 == BM && WL * NW * 8 == BN, "load split");
-  static_assert(FA >= 2 && FA % 2 == 0, "the last sub-step splits the A fragments in two");
+  static_assert(FA >= 2, "the last sub-step splits the A fragments in two");
 };
 
 __device__ __forceinline__ int dswz(int row, int kc) { return kc ^ ((row >> 1) & 7); }
@@ -294,6 +295,10 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
 
 using Dma256 = DmaTile<256, 256, 2, 4>;   // 8 waves, one workgroup per CU
 using Dma128 = DmaTile<128, 128, 2, 2>;   // 4 waves, two workgroups per CU
+// 256x320: 8 waves of 64x160 (144 KB of LDS for two stages).  For N where
+// 256x256 tiles leave a mostly empty last round, e.g. the fused QKV at
+// N = 5120: 16 x 16 tiles fill 256 CUs exactly once.
+using Dma320 = DmaTile<256, 320, 4, 2>;
 
 template <class C, int EPI>
 static tp_status launch_dma(const void* x, const void* w, void* y, int M, int N, int K,
@@ -319,21 +324,26 @@ static tp_status launch_dma(const void* x, const void* w, void* y, int M, int N,
   return TP_OK;
 }
 
-// 0 = 256x256 (8 waves), 1 = 128x128 (4 waves).  Estimated time = full-chip
-// rounds x round time; a round of 128x128 tiles (two per CU) does half the
-// work of a 256x256 round at ~85% of its efficiency (measured on gate|up- and
-// qkv-shaped problems).
-int gemm_dma_pick_tile(int M, int N) {
+// 0 = 256x256 (8 waves), 1 = 128x128 (4 waves), 2 = 256x320 (8 waves).
+// Estimated time = full-chip rounds x round time in units of a 256x256 round:
+// a round of 128x128 tiles (two per CU) does half that work at ~85% of its
+// efficiency, a round of 256x320 tiles does 1.25x the work at the same
+// efficiency (measured on gate|up-, qkv- and o_proj-shaped problems).
+// `wide` allows the 256x320 tile (its epilogue has no room for the SwiGLU
+// exchange).
+int gemm_dma_pick_tile(int M, int N, bool wide) {
   const double t256 = ceil((double)((M + 255) / 256) * ((N + 255) / 256) / 256.0);
   const double t128 = ceil((double)((M + 127) / 128) * ((N + 127) / 128) / 512.0) * 0.5 / 0.85;
+  const double t320 = wide ? ceil((double)((M + 255) / 256) * ((N + 319) / 320) / 256.0) * 1.25 : 1e30;
+  if (t320 < t256 && t320 < t128) return 2;
   return t128 < t256 ? 1 : 0;
 }
 
-// Requires K % 8 == 0, 16-byte aligned X and W, and 256*K*2 < 2^31.
 tp_status gemm_bf16_dma(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                         bool out_f32, bool vec_out, hipStream_t s, int force_tile) {
-  const int pick = force_tile >= 0 ? force_tile : gemm_dma_pick_tile((int)M, (int)N);
+  const int pick = force_tile >= 0 ? force_tile : gemm_dma_pick_tile((int)M, (int)N, true);
   if (pick == 0) return launch_dma<Dma256, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
+  if (pick == 2) return launch_dma<Dma320, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
   return launch_dma<Dma128, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
 }
 
@@ -344,12 +354,13 @@ tp_status gemm_bf16_dma_act(const void* x, const void* w, void* h, int64_t M, in
                             int act, bool vec_out, hipStream_t s) {
   if (act == TP_ACT_SWIGLU) {
     // a paired 256-wide tile yields 128 outputs: pick the tile on the doubled width
-    const int pick = gemm_dma_pick_tile((int)M, (int)(2 * I));
+    const int pick = gemm_dma_pick_tile((int)M, (int)(2 * I), false);
     if (pick == 0) return launch_dma<Dma256, 1>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
     return launch_dma<Dma128, 1>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
   }
-  const int pick = gemm_dma_pick_tile((int)M, (int)I);
+  const int pick = gemm_dma_pick_tile((int)M, (int)I, true);
   if (pick == 0) return launch_dma<Dma256, 2>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
+  if (pick == 2) return launch_dma<Dma320, 2>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
   return launch_dma<Dma128, 2>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
 }
 

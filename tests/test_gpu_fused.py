@@ -45,6 +45,7 @@ ACT_SHAPES = [
     (300, 520, 1000),
     (1000, 2048, 700),
     (2048, 1024, 3584),  # 256x256 tiles
+    (4000, 520, 5100),   # GELU: 256x320 tiles
 ]
 
 
