@@ -219,9 +219,75 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x
   }
 }
 
+// Rows of at most 8 x 2048 bf16 elements: the same arithmetic in the same order
+// as rmsnorm_kernel<true, true>, with the row held in registers between the
+// two passes and every load of the row issued before the first use.
+template <int CH>
+__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ gamma,
+                                                          uint16_t* __restrict__ y, int64_t N, float eps) {
+  __shared__ float wsum[4];
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint16_t* xr = x + m * N;
+  u32x4 xv[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int64_t c = tid * 8 + k * 2048;
+    xv[k] = c < N ? *reinterpret_cast<const u32x4*>(xr + c) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    if (tid * 8 + k * 2048 < N) {
+      float f[8];
+      unpack8(xv[k], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  const float inv = rsqrtf(tot / (float)N + eps);
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int64_t c = tid * 8 + k * 2048;
+    if (c < N) {
+      float f[8], gm[8], o[8];
+      unpack8(xv[k], f);
+      unpack8(*reinterpret_cast<const u32x4*>(gamma + c), gm);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = f[i] * inv * gm[i];
+      *reinterpret_cast<u32x4*>(y + m * N + c) = pack8(o);
+    }
+  }
+}
+
 tp_status rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t N, float eps,
                   bool bf16, bool vec, hipStream_t s) {
   dim3 grid((unsigned)M), block(256);
+  const int ch = (int)((N + 2047) / 2048);
+  if (bf16 && vec && ch <= 8) {
+    auto X = static_cast<const uint16_t*>(x);
+    auto G = static_cast<const uint16_t*>(gamma);
+    auto Y = static_cast<uint16_t*>(y);
+#define TPL_RMS(C) hipLaunchKernelGGL((rmsnorm_reg_kernel<C>), grid, block, 0, s, X, G, Y, N, eps)
+    switch (ch) {
+      case 1: TPL_RMS(1); break;
+      case 2: TPL_RMS(2); break;
+      case 3: TPL_RMS(3); break;
+      case 4: TPL_RMS(4); break;
+      case 5: TPL_RMS(5); break;
+      case 6: TPL_RMS(6); break;
+      case 7: TPL_RMS(7); break;
+      default: TPL_RMS(8); break;
+    }
+#undef TPL_RMS
+    TPL_LAUNCH_CHECK("rmsnorm");
+    return TP_OK;
+  }
   if (bf16) {
     if (vec) hipLaunchKernelGGL((rmsnorm_kernel<true, true>), grid, block, 0, s, x, gamma, y, N, eps);
     else hipLaunchKernelGGL((rmsnorm_kernel<true, false>), grid, block, 0, s, x, gamma, y, N, eps);
@@ -288,11 +354,117 @@ __global__ __launch_bounds__(256) void reduce_rmsnorm_kernel(PartialPtrs P, int 
   }
 }
 
+// Rows of at most 8 x 2048 elements: reduce_rmsnorm_kernel's arithmetic in the
+// same order, with each rank's loads for the whole row issued together and h
+// kept in registers for the second pass.
+template <int CH>
+__global__ __launch_bounds__(256) void reduce_rmsnorm_reg_kernel(PartialPtrs P, int R,
+                                                                 const uint16_t* residual,
+                                                                 uint16_t* y,   // may alias residual
+                                                                 const uint16_t* __restrict__ gamma,
+                                                                 uint16_t* __restrict__ yn, int64_t N,
+                                                                 float eps) {
+  __shared__ float wsum[4];
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x;
+  f32x4 acc[CH][2];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int64_t c = tid * 8 + k * 2048;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      acc[k][half] = c < N ? *reinterpret_cast<const f32x4*>(P.p[0] + m * N + c + 4 * half)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int r = 1; r < R; ++r) {
+    f32x4 v[CH][2];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int64_t c = tid * 8 + k * 2048;
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        v[k][half] = c < N ? *reinterpret_cast<const f32x4*>(P.p[r] + m * N + c + 4 * half)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      acc[k][0] += v[k][0];
+      acc[k][1] += v[k][1];
+    }
+  }
+  u32x4 hb[CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int64_t c = tid * 8 + k * 2048;
+    if (c < N) {
+      const int64_t o = m * N + c;
+      float h[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        f32x4 a = acc[k][half];
+        if (residual) {
+          const u32x2 rv = *reinterpret_cast<const u32x2*>(residual + o + 4 * half);
+          a[0] += bf_lo(rv[0]); a[1] += bf_hi(rv[0]);
+          a[2] += bf_lo(rv[1]); a[3] += bf_hi(rv[1]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[4 * half + i] = a[i];
+      }
+      hb[k] = pack8(h);
+      *reinterpret_cast<u32x4*>(y + o) = hb[k];
+      float f[8];
+      unpack8(hb[k], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  const float inv = rsqrtf(tot / (float)N + eps);
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int64_t c = tid * 8 + k * 2048;
+    if (c < N) {
+      float f[8], gm[8], o[8];
+      unpack8(hb[k], f);
+      unpack8(*reinterpret_cast<const u32x4*>(gamma + c), gm);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = f[i] * inv * gm[i];
+      *reinterpret_cast<u32x4*>(yn + m * N + c) = pack8(o);
+    }
+  }
+}
+
 tp_status reduce_rmsnorm(const float* const* partials, int R, const void* residual, void* y,
                          const void* gamma, void* yn, int64_t M, int64_t N, float eps,
                          hipStream_t s) {
   PartialPtrs P = {};
   for (int r = 0; r < R; ++r) P.p[r] = partials[r];
+  const int ch = (int)((N + 2047) / 2048);
+  if (ch <= 8) {
+    auto Rs = static_cast<const uint16_t*>(residual);
+    auto Y = static_cast<uint16_t*>(y);
+    auto G = static_cast<const uint16_t*>(gamma);
+    auto YN = static_cast<uint16_t*>(yn);
+#define TPL_RRMS(C) hipLaunchKernelGGL((reduce_rmsnorm_reg_kernel<C>), dim3((unsigned)M), dim3(256), 0, s, \
+                                       P, R, Rs, Y, G, YN, N, eps)
+    switch (ch) {
+      case 1: TPL_RRMS(1); break;
+      case 2: TPL_RRMS(2); break;
+      case 3: TPL_RRMS(3); break;
+      case 4: TPL_RRMS(4); break;
+      case 5: TPL_RRMS(5); break;
+      case 6: TPL_RRMS(6); break;
+      case 7: TPL_RRMS(7); break;
+      default: TPL_RRMS(8); break;
+    }
+#undef TPL_RRMS
+    TPL_LAUNCH_CHECK("reduce_rmsnorm");
+    return TP_OK;
+  }
   hipLaunchKernelGGL(reduce_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, s, P, R,
                      static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(y),
                      static_cast<const uint16_t*>(gamma), static_cast<uint16_t*>(yn), N, eps);

@@ -102,7 +102,7 @@ def test_column_linear_act_rejects_unsupported():
 
 
 @pytest.mark.parametrize("R", [1, 2, 8])
-@pytest.mark.parametrize("M,N", [(1, 8192), (7, 4096), (300, 1024), (3, 8), (5, 100)])
+@pytest.mark.parametrize("M,N", [(1, 8192), (7, 4096), (300, 1024), (3, 8), (5, 100), (2, 14344), (2, 20480)])
 @pytest.mark.parametrize("residual", [True, False])
 def test_reduce_partials_rmsnorm(R, M, N, residual):
     log(f"reduce_partials_rmsnorm R={R} M={M} N={N} residual={residual}")

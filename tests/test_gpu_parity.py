@@ -141,7 +141,7 @@ def test_activation(act, M, I_, dtype):
 # RMSNorm and the sum of partials
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,N", [(1, 8), (7, 8192), (300, 4096), (3, 100)])
+@pytest.mark.parametrize("M,N", [(1, 8), (7, 8192), (300, 4096), (3, 100), (2, 16392), (2, 20000)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_rmsnorm(M, N, dtype):
     log(f"rmsnorm M={M} N={N} {dtype}")
