@@ -253,3 +253,56 @@ def test_kv_append_exact():
     torch.cuda.synchronize()
     assert torch.equal(kc[:, :, 5], kn) and torch.equal(vc[:, :, 5], vn)
     assert torch.count_nonzero(kc[:, :, :5]) == 0 and torch.count_nonzero(kc[:, :, 6:]) == 0
+
+
+# ---------------------------------------------------------------------------
+# maximum sizes of each path (the limits the C ABI documents)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,N", [
+    (3, (1 << 22) + 8, 40),      # weight streaming, K far past any tile
+    (40, (1 << 20) + 8, 24),     # LDS-ring weight streaming (33..64 tokens)
+    (65, (1 << 21) - 8, 64),     # prefill tile kernel at its largest K (32-bit offsets)
+])
+def test_linear_max_k_integer_exact(M, K, N):
+    """Integers in {-1, 0, 1}: every partial sum stays below 2^24, so the
+    result is exact at any K."""
+    log(f"linear max-K int M={M} K={K} N={N}")
+    x = I.uniform_int(19, "x", (M, K), -1, 1, dtype=torch.bfloat16)
+    w = I.uniform_int(19, "w", (N, K), -1, 1, dtype=torch.bfloat16)
+    ref = O.linear(x.ref, w.ref)
+    X, W = dev(x), dev(w)
+    assert_bitexact(tpl.row_linear_partial(X, W), ref, "row partial (fp32 out)")
+    assert_bitexact(tpl.column_linear(X, W), O.round_bf16(ref), "column (bf16 out)")
+
+
+def test_attention_decode_long_span():
+    """131072 keys for one sequence: 128 key chunks combined in order."""
+    B, Skv, Hq, Hkv, D = 1, 1 << 17, 8, 2, 128
+    log(f"attention decode long span Skv={Skv}")
+    q = I.normal(20, "q", (B, 1, Hq, D))
+    kc = I.normal(20, "k", (B, Hkv, Skv, D))
+    vc = I.normal(20, "v", (B, Hkv, Skv, D))
+    kref = kc.ref.transpose(0, 2, 1, 3)
+    vref = vc.ref.transpose(0, 2, 1, 3)
+    ref = O.attention(q.ref, kref, vref, causal=True)
+    o = tpl.local_attention(dev(q), dev(kc).transpose(1, 2), dev(vc).transpose(1, 2), causal=True)
+    assert_within(o, ref, _attn_bound(ref, vref), "decode attention, long span")
+    assert_normwise(o, ref, 1e-2, "decode attention, long span")
+
+
+def test_attention_prefill_long_sequence_sampled_rows():
+    """A 16384-token causal prefill; the oracle checks 64 sampled query rows
+    (each against all its keys)."""
+    B, S, Hq, Hkv, D = 1, 16384, 2, 1, 128
+    log(f"attention prefill long S={S}")
+    q = I.normal(21, "q", (B, S, Hq, D))
+    k = I.normal(21, "k", (B, S, Hkv, D))
+    v = I.normal(21, "v", (B, S, Hkv, D))
+    o = tpl.local_attention(dev(q), dev(k), dev(v), causal=True)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, S - 1],
+                                     np.random.default_rng(21).choice(S, 59, replace=False)]))
+    ref = O.attention(q.ref[:, rows], k.ref, v.ref, causal=True, q_pos=rows)
+    got = f64(o)[:, rows]
+    assert_within(got, ref, _attn_bound(ref, v.ref), "prefill attention, sampled rows")
+    assert_normwise(got, ref, 1e-2, "prefill attention, sampled rows")
