@@ -287,13 +287,20 @@ def _graph_ms(steps_fns, steps, warmup):
     return _median_ms(lambda i: graphs[i % n].replay(), steps, warmup)
 
 
+def _decode_entry(ms_eager, ms_graph, byts, fl):
+    """Figures of one decode shard: both issue modes, and the rates of the
+    faster one (a serving loop would use whichever is faster)."""
+    ms = min(ms_eager, ms_graph)
+    return {"ms": ms, "issue": "graph" if ms_graph < ms_eager else "eager",
+            "eager_ms": ms_eager, "graph_ms": ms_graph,
+            "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9, "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS}
+
+
 def decode_figures(steps=30, warmup=5, copies=4):
     """Decode shards timed over ``copies`` rotating copies of the weights and
-    caches (together larger than the 256 MB Infinity Cache).  ``ms`` is the
-    step issued call by call (the host runs ahead of the GPU); ``graph_ms``
-    is the same step replayed from a captured HIP graph, reported for
-    comparison (on this stack a graph launch costs more than the three to
-    five queued kernel launches it replaces)."""
+    caches (together larger than the 256 MB Infinity Cache).  ``eager_ms`` is
+    the step issued call by call, ``graph_ms`` the same step replayed from a
+    captured HIP graph; ``ms`` and the rates use the faster of the two."""
     out = {}
     c = I.config("decode_mlp_tp8")
     H, il = c.hidden, c.inter // c.tp
@@ -312,8 +319,7 @@ def decode_figures(steps=30, warmup=5, copies=4):
         # weights once, x read, act(g)*u written and read back, fp32 partial written
         byts = wbytes + M * H * 2 + M * il * 2 * 2 + M * H * 4
         fl = 2.0 * M * (H * 2 * il + il * H)
-        out[f"mlp_tp8_M{M}"] = {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
-                                "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS, "graph_ms": gms}
+        out[f"mlp_tp8_M{M}"] = _decode_entry(ms, gms, byts, fl)
     del mlps
     c = I.config("decode_attn_tp4")
     H, R, D, B, L = c.hidden, c.tp, c.head_dim, c.batch, c.kv_len
@@ -337,8 +343,7 @@ def decode_figures(steps=30, warmup=5, copies=4):
     ms = _median_ms(lambda i: fns[i % copies](), steps, warmup)
     byts = (wqkv.numel() + wo.numel() + kc.numel() + vc.numel()) * 2 + B * H * 2 + B * H * 4
     fl = 2.0 * B * H * (hq + 2 * hkv) * D + 4.0 * B * hq * L * D + 2.0 * B * hq * D * H
-    out["attn_tp4_B32_L2048"] = {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
-                                 "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS, "graph_ms": gms}
+    out["attn_tp4_B32_L2048"] = _decode_entry(ms, gms, byts, fl)
     out["attn_tp16_rep_B32_L2048"] = _replicated_attn_figure(steps, warmup, copies)
     out["attn_tp4_paged_B32_L2048"] = _paged_attn_figure(steps, warmup, copies)
     out.update(_lm_head_figures(steps, warmup))
@@ -393,8 +398,7 @@ def _paged_attn_figure(steps, warmup, copies, bs=16):
     ms = _median_ms(lambda i: fns[i % copies](), steps, warmup)
     byts = (wqkv.numel() + wo.numel() + kc.numel() + vc.numel()) * 2 + B * H * 2 + B * H * 4
     fl = 2.0 * B * H * (hq + 2 * hkv) * D + 4.0 * B * hq * L * D + 2.0 * B * hq * D * H
-    return {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
-            "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS, "graph_ms": gms}
+    return _decode_entry(ms, gms, byts, fl)
 
 
 def _replicated_attn_figure(steps, warmup, copies):
@@ -425,9 +429,9 @@ def _replicated_attn_figure(steps, warmup, copies):
     ms = _median_ms(lambda i: fns[i % copies](), steps, warmup)
     byts = (wqkv.numel() + wo0.numel() + kc.numel() + vc.numel()) * 2 + B * H * 2 + B * H * 4
     fl = 2.0 * B * H * wqkv.shape[0] + 4.0 * B * hq * L * D + 2.0 * B * hq * D * H
-    return {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
-            "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS, "graph_ms": gms,
-            "kv_cache_bytes_per_rank": tpl.kv_cache_bytes_per_rank(c.n_q, c.n_kv, R, B, L, D)}
+    e = _decode_entry(ms, gms, byts, fl)
+    e["kv_cache_bytes_per_rank"] = tpl.kv_cache_bytes_per_rank(c.n_q, c.n_kv, R, B, L, D)
+    return e
 
 
 # ---------------------------------------------------------------------------

@@ -1,4 +1,4 @@
-// Small-M (decode, M <= 64 tokens) bf16 linear: weight streaming.
+// Decode bf16 linear for 1..16 tokens: weight streaming.
 //
 //   Y[m, n] = sum_k X[m, k] * W[n, k]
 //
@@ -185,17 +185,14 @@ static void launch_stream(const void* x, const void* w, void* y, int M, int N, i
 tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M, int64_t N,
                                int64_t K, bool out_f32, hipStream_t s);
 
-// Waves per workgroup of the decode linear on an [N, K] weight: split K so
-// that every wave streams >= 256 k; 16 waves (1024 threads, <= 128 VGPRs
-// each) only for the lightest register footprints and when there are few row
-// tiles to spread over the chip.  The fused-activation variant takes the same
-// split (hence the same float sums) as the plain linear on the full weight.
-static int stream_row_tiles(int mt, int64_t N) { return (mt >= 2 && N >= 16 * 2 * 224) ? 2 : 1; }
-
-static int stream_waves(int mt, int64_t N, int64_t K) {
-  const int rt = stream_row_tiles(mt, N);
-  const int64_t nblk = (N + 16 * rt - 1) / (16 * rt);
-  int waves = (nblk < 384 && mt * rt <= 2) ? 16 : 8;
+// Waves per workgroup of the one-token-tile decode linear on an [N, K]
+// weight: split K so that every wave streams >= 256 k; 16 waves (1024
+// threads) when there are few row tiles to spread over the chip.  The
+// fused-activation variant takes the same split (hence the same float sums)
+// as the plain linear on the full weight.
+static int stream_waves(int64_t N, int64_t K) {
+  const int64_t nblk = (N + 15) / 16;
+  int waves = nblk < 384 ? 16 : 8;
   while (waves > 4 && K / waves < 256) waves >>= 1;
   return waves;
 }
@@ -208,30 +205,15 @@ static int stream_kw(int64_t K, int waves) {
 tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                            bool out_f32, hipStream_t s) {
   const int mt = (int)((M + 15) / 16);
-  // Three or four token tiles: the LDS-ring kernel (coalesced weight stream,
-  // two row tiles per wave) is faster; measured on 64-token decode shards.
-  if (mt >= 3) return gemm_bf16_stream_dma(x, w, y, M, N, K, out_f32, s);
-  // Two row tiles per wave when there are several token tiles (each X
-  // fragment then feeds two MFMAs) and enough row tiles to fill the chip.
-  const int rt = stream_row_tiles(mt, N);
-  const int waves = stream_waves(mt, N, K);
+  // Two to four token tiles: the kernel that streams weights and tokens
+  // through LDS (whole-line loads for both operands).
+  if (mt >= 2) return gemm_bf16_stream_dma(x, w, y, M, N, K, out_f32, s);
+  const int waves = stream_waves(N, K);
   const int kw = stream_kw(K, waves);
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
-#define TPL_STREAM(WV, MTV, RTV) launch_stream<WV, MTV, RTV>(x, w, y, Mi, Ni, Ki, kw, out_f32, s)
-#define TPL_STREAM_MT(WV, RTV)                  \
-  if (mt == 1) TPL_STREAM(WV, 1, RTV);          \
-  else TPL_STREAM(WV, 2, RTV);
-  if (waves == 16) {
-    if (rt == 1 && mt == 1) TPL_STREAM(16, 1, 1);
-    else if (rt == 1) TPL_STREAM(16, 2, 1);
-    else TPL_STREAM(16, 1, 2);
-  } else if (rt == 1) {
-    if (waves == 8) { TPL_STREAM_MT(8, 1); } else { TPL_STREAM_MT(4, 1); }
-  } else {
-    if (waves == 8) { TPL_STREAM_MT(8, 2); } else { TPL_STREAM_MT(4, 2); }
-  }
-#undef TPL_STREAM_MT
-#undef TPL_STREAM
+  if (waves == 16) launch_stream<16, 1, 1>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
+  else if (waves == 8) launch_stream<8, 1, 1>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
+  else launch_stream<4, 1, 1>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
   TPL_LAUNCH_CHECK("gemm_bf16_stream");
   return TP_OK;
 }
@@ -247,24 +229,18 @@ tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_
 tp_status gemm_bf16_stream_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
                                int64_t K, int act, hipStream_t s) {
   const int mt = (int)((M + 15) / 16);
-  if (mt >= 3) return gemm_bf16_stream_dma_act(x, w, h, M, I, K, act, s);
-  const int waves = stream_waves(mt, act == TP_ACT_SWIGLU ? 2 * I : I, K);
+  if (mt >= 2) return gemm_bf16_stream_dma_act(x, w, h, M, I, K, act, s);
+  const int waves = stream_waves(act == TP_ACT_SWIGLU ? 2 * I : I, K);
   const int kw = stream_kw(K, waves);
   const int Mi = (int)M, Ii = (int)I, Ki = (int)K;
-#define TPL_SACT(WV, MTV)                                                                      \
-  do {                                                                                         \
-    if (act == TP_ACT_SWIGLU) launch_stream<WV, MTV, 2, 1>(x, w, h, Mi, Ii, Ki, kw, false, s); \
-    else launch_stream<WV, MTV, 1, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);                     \
+#define TPL_SACT(WV)                                                                         \
+  do {                                                                                       \
+    if (act == TP_ACT_SWIGLU) launch_stream<WV, 1, 2, 1>(x, w, h, Mi, Ii, Ki, kw, false, s); \
+    else launch_stream<WV, 1, 1, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);                     \
   } while (0)
-#define TPL_SACT_MT(WV)                 \
-  do {                                  \
-    if (mt == 1) TPL_SACT(WV, 1);       \
-    else TPL_SACT(WV, 2);               \
-  } while (0)
-  if (waves == 16) TPL_SACT_MT(16);
-  else if (waves == 8) TPL_SACT_MT(8);
-  else TPL_SACT_MT(4);
-#undef TPL_SACT_MT
+  if (waves == 16) TPL_SACT(16);
+  else if (waves == 8) TPL_SACT(8);
+  else TPL_SACT(4);
 #undef TPL_SACT
   TPL_LAUNCH_CHECK("gemm_bf16_stream_act");
   return TP_OK;

@@ -1,25 +1,28 @@
-// Small-M (decode, M <= 64 tokens) bf16 linear through LDS: weight streaming.
+// Decode bf16 linear for 17..64 tokens through LDS: weight streaming.
 //
 //   Y[m, n] = sum_k X[m, k] * W[n, k]
 //
-// At decode the weight matrix is read once per call and dominates the bytes,
-// so the kernel is built around a coalesced, deeply pipelined weight stream:
+// At decode the weight matrix is read once per call and dominates the HBM
+// bytes, but with 17..64 tokens the token rows are re-read from L2 by every
+// workgroup and make up most of a workgroup's load traffic.  Loads whose 64
+// lanes each take 16 bytes of a different row (the MFMA operand layout) use
+// only half of every 128-byte line they touch, and measured per-CU load
+// throughput is then what bounds these shapes.  So both operands go through
+// LDS:
 //   * a workgroup owns RT tiles of 16 consecutive weight rows and all of K;
 //     its WAVES waves split K into contiguous 128-k-aligned ranges;
-//   * every wave streams its (16 RT) x krange weight slice through a private
-//     S-stage LDS ring with buffer_load_dwordx4 ... lds: one wave-level load
-//     writes 4 rows x 256 contiguous bytes, so each load instruction is fully
-//     coalesced (the MFMA operand layout, one row per lane, is not);
-//   * the 256-byte LDS rows keep 16-byte chunk c of row r at position
-//     c ^ (r % 16), so the A-fragment reads of v_mfma_f32_16x16x32_bf16 (16
-//     rows x one chunk per quarter-wave) hit 16 distinct bank groups;
-//   * X (the tokens, a few KB resident in L2) comes straight from global
-//     memory as the B operand, one 16-byte buffer load per lane and 32 k;
+//   * every wave streams its weight rows AND the token rows of its k range
+//     through a private S-stage LDS ring with buffer_load_dwordx4 ... lds: one
+//     wave-level load writes 4 rows x 256 contiguous bytes (two whole lines
+//     per row), for weights and tokens alike;
+//   * 256-byte LDS rows keep 16-byte chunk c of row r at c ^ (r % 16), so the
+//     fragment reads of v_mfma_f32_16x16x32_bf16 (16 rows x one chunk per
+//     quarter-wave) hit 16 distinct bank groups;
 //   * out-of-range rows, tokens and k read as zero through the buffer bounds,
 //     so the loop is branch-free and waits for exactly the chunk it uses;
-//   * no workgroup barrier inside the loop (the rings are per wave); the
-//     WAVES partial tiles are summed in LDS in wave order at the end, so the
-//     result does not depend on timing.
+//   * no workgroup barrier in the loop (the rings are per wave); the WAVES
+//     partial tiles are summed in LDS in wave order at the end, so the result
+//     depends only on WAVES and the k ranges, not on timing, RT or S.
 #include "common.h"
 
 namespace tpl {
@@ -29,18 +32,16 @@ namespace {
 constexpr uint32_t kSOob = 0x80000000u;   // offset past any buffer bound -> reads 0
 #define TPL_LDS __attribute__((address_space(3)))
 
-__device__ __forceinline__ u32x4 sbload(const __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 // s_waitcnt with only vmcnt constrained (gfx9 encoding)
 #define TPL_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
 #define TPL_LGKM0 0xC07F
 
 }  // namespace
 
-// EPI as in gemm_stream_kernel: 0 plain, 1 SwiGLU (RT = 2: gate tile + the
-// matching up tile of a [2N, K] weight, output [M, N]), 2 GELU.
+// EPI: 0 plain, 1 SwiGLU (RT = 2: row tile 0 = gate rows n0.., tile 1 = the
+// matching up rows N + n0.. of a [2N, K] weight; output [M, N]), 2 GELU.  The
+// fused epilogues round the sums to bf16 before the activation, as the
+// unfused path stores them.
 template <int WAVES, int MT, int RT, int S, bool OUT_F32, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
@@ -48,11 +49,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
   static_assert(EPI != 1 || RT == 2, "SwiGLU pairs a gate and an up row tile");
   static_assert(RT == 1 || RT == 2, "one or two row tiles");
   constexpr int OUT_ROWS = EPI == 1 ? 16 : 16 * RT;
-  constexpr int ROWS = 16 * RT;
-  constexpr int STAGE = ROWS * 128;                   // bf16 elements per stage (256 B rows)
-  constexpr int RING = S * STAGE;                      // per wave
-  constexpr int RED = WAVES * RT * MT * 256;           // floats for the final reduction
+  constexpr int WROWS = 16 * RT, XROWS = 16 * MT, ROWS = WROWS + XROWS;
+  constexpr int STAGE = ROWS * 128;                   // bf16 elements per stage (256-byte rows)
+  constexpr int RING = S * STAGE;                     // per wave
+  constexpr int DPC = ROWS / 4;                       // DMA instructions per chunk
+  constexpr int RED = WAVES * RT * MT * 256;          // floats for the final reduction
   constexpr int LDS_E = (WAVES * RING * 2 > RED * 4) ? WAVES * RING : RED * 2;
+  static_assert(S >= 3 && (S - 2) * DPC <= 63, "ring depth within the vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_E];
 
   const int lane = threadIdx.x & 63;
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
   const int g = lane >> 4;         // k-group of this lane inside a 32-k step
   const int i16 = lane & 15;       // weight row / token inside a 16-tile
 
-  // one resource per row tile, based at its first row and bounded to its valid rows
+  // one resource per weight row tile, based at its first row and bounded to its valid rows
   __amdgpu_buffer_rsrc_t wr[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
@@ -77,21 +80,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
   const int ke = min(K, kb + kw);
   const int nc = ke > kb ? (ke - kb + 127) / 128 : 0;   // 128-k chunks of this wave
 
-  // DMA lane mapping: load d of a chunk covers rows 4d .. 4d+3; lane -> row
-  // 4d + lane/16, LDS chunk position lane%16 holding logical chunk
-  // (lane%16) ^ (row % 16).
+  // DMA lane mapping: load d of a chunk covers stage rows 4d .. 4d+3 (weight
+  // rows first, then token rows); lane -> row 4d + lane/16, LDS chunk position
+  // lane%16 holding logical chunk (lane%16) ^ (row % 16).
   const int drow = lane >> 4, dpos = lane & 15;
   TPL_LDS uint16_t* ring = (TPL_LDS uint16_t*)lds + wave * RING;
   auto issue = [&](int c) {   // chunk c of this wave into stage c % S
     const int k0 = kb + c * 128;
     TPL_LDS uint16_t* dst = ring + (c % S) * STAGE;
 #pragma unroll
-    for (int d = 0; d < ROWS / 4; ++d) {
-      const int row = 4 * d + drow;                      // row tile d / 4, row (row % 16) in it
+    for (int d = 0; d < DPC; ++d) {
+      const int row = 4 * d + drow;
       const int k = k0 + 8 * (dpos ^ (row & 15));
-      const uint32_t off = k < ke ? (uint32_t)((row & 15) * K + k) * 2u : kSOob;
-      const __amdgpu_buffer_rsrc_t rs = d < 4 ? wr[0] : wr[RT - 1];   // row tile d / 4 (RT <= 2)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TPL_LDS void*)(dst + d * 4 * 128), 16, off, 0, 0, 0);
+      if (d < WROWS / 4) {       // weight rows: tile d / 4, row row % 16 in it
+        const __amdgpu_buffer_rsrc_t rs = d < 4 ? wr[0] : wr[RT - 1];
+        const uint32_t off = k < ke ? (uint32_t)((row & 15) * K + k) * 2u : kSOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TPL_LDS void*)(dst + d * 4 * 128), 16, off, 0, 0, 0);
+      } else {                   // token rows
+        const uint32_t off = k < ke ? (uint32_t)((row - WROWS) * K + k) * 2u : kSOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (TPL_LDS void*)(dst + d * 4 * 128), 16, off, 0, 0, 0);
+      }
     }
   };
 
@@ -101,43 +109,32 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint32_t xoff[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) xoff[t] = (uint32_t)((t * 16 + i16) * K) * 2u;
-  auto load_x = [&](int c, u32x4 (&xv)[MT][4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = kb + c * 128 + q * 32 + g * 8;
-      const bool ok = k < ke;
-#pragma unroll
-      for (int t = 0; t < MT; ++t) xv[t][q] = sbload(xr, ok ? xoff[t] + (uint32_t)k * 2u : kSOob);
-    }
-  };
-
-  // Memory operations complete in issue order, so each iteration issues the
-  // next chunk's X loads BEFORE the next weight DMA: waiting for X(c) then
-  // leaves the newest DMA in flight.  Chunk c is consumed once DMA(c) and
-  // X(c) have landed:
-  //   c = 0: prologue order DMA(0), X(0), DMA(1..S-2) -> (S-2) DMAs may pend;
-  //   c > 0: order ... X(c), DMA(c+S-2) -> one DMA may pend.
-  // Chunks past the end (odd count, the trailing DMAs) read as zero.
-  constexpr int DPC = ROWS / 4;   // DMA instructions per chunk
-  auto step = [&](int c, const u32x4 (&xv)[MT][4], u32x4 (&xn)[MT][4], bool first) {
-    if (first) __builtin_amdgcn_s_waitcnt(TPL_VMCNT((S - 2) * DPC));
-    else __builtin_amdgcn_s_waitcnt(TPL_VMCNT(DPC));
+  // Memory operations complete in issue order.  Before step c the chunks
+  // c .. c+S-2 are in flight (prologue: 0 .. S-2; each step adds c+S-1), so
+  // waiting until at most (S-2) chunks' loads are pending lands chunk c.  The
+  // step copies its fragments to registers, then refills the stage of chunk
+  // c-1, read by the previous step.  Chunks past the end read as zero.
+  auto step = [&](int c) {
+    __builtin_amdgcn_s_waitcnt(TPL_VMCNT((S - 2) * DPC));
     __builtin_amdgcn_sched_barrier(0);
     const uint16_t* st = lds + wave * RING + (c % S) * STAGE;
-    u32x4 wv[RT][4];
+    u32x4 wv[RT][4], xv[MT][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         const int row = r * 16 + i16;
         wv[r][q] = *reinterpret_cast<const u32x4*>(st + row * 128 + ((4 * q + g) ^ (row & 15)) * 8);
       }
-    load_x(c + 1, xn);
-    issue(c + S - 1);   // refills the stage of chunk c-1, whose reads completed last iteration
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int row = WROWS + t * 16 + i16;
+        xv[t][q] = *reinterpret_cast<const u32x4*>(st + row * 128 + ((4 * q + g) ^ (row & 15)) * 8);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(TPL_LGKM0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(c + S - 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -151,18 +148,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
   };
 
   if (nc > 0) {
-    u32x4 xa[MT][4], xb[MT][4];
-    issue(0);
-    load_x(0, xa);
 #pragma unroll
-    for (int c = 1; c < S - 1; ++c) issue(c);
+    for (int c = 0; c < S - 1; ++c) issue(c);
     __builtin_amdgcn_sched_barrier(0);
-    for (int c = 0; c < nc; c += 2) {
-      step(c, xa, xb, c == 0);
-      step(c + 1, xb, xa, false);
-    }
+    for (int c = 0; c < nc; ++c) step(c);
   }
-  // Drain the trailing (out-of-range) DMA before the LDS is reused.
+  // Drain the trailing (out-of-range) loads before the LDS is reused.
   __builtin_amdgcn_s_waitcnt(TPL_VMCNT(0));
   __syncthreads();
 
@@ -228,34 +219,48 @@ static void launch_stream_dma(const void* x, const void* w, void* y, int M, int 
   }
 }
 
-// Requires 33 <= M <= 64, K % 8 == 0, 16-byte aligned X and W, M*K and
-// 32*K elements addressable with 32-bit byte offsets.  Two waves per
-// workgroup, two row tiles per wave, an 8-stage ring (128 KB of LDS).
+// Waves per workgroup by token tiles (the K split; the fused-activation
+// variant must use the same): 3 for 17..32 tokens, 2 for 33..64.  LDS per
+// workgroup = WAVES x S x (16 RT + 16 MT) x 256 bytes <= 144 KB.
+static int stream_dma_waves(int mt) { return mt <= 2 ? 3 : 2; }
+
+static int stream_dma_kw(int64_t K, int waves) {
+  int kw = (int)((K + waves - 1) / waves);
+  return (kw + 127) & ~127;
+}
+
+// Requires 17 <= M <= 64, K % 8 == 0, 16-byte aligned X and W, and M*K and
+// 32*K elements addressable with 32-bit byte offsets.
 tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M, int64_t N,
                                int64_t K, bool out_f32, hipStream_t s) {
-  constexpr int WV = 2;
-  int kw = (int)((K + WV - 1) / WV);
-  kw = (kw + 127) & ~127;
+  const int mt = (int)((M + 15) / 16);
+  const int WV = stream_dma_waves(mt);
+  const int kw = stream_dma_kw(K, WV);
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
-  if (M > 48) launch_stream_dma<WV, 4, 2, 8>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
-  else launch_stream_dma<WV, 3, 2, 8>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
+  if (mt <= 2) launch_stream_dma<3, 2, 1, 4>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
+  else if (mt == 3) launch_stream_dma<2, 3, 2, 3>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
+  else launch_stream_dma<2, 4, 2, 3>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
   TPL_LAUNCH_CHECK("gemm_bf16_stream_dma");
   return TP_OK;
 }
 
-// The same kernel with the rank-local activation fused (bf16 output [M, I]).
+// The same kernel with the rank-local activation fused (bf16 output [M, I]);
+// the K split is the plain call's for the same token count, so the results
+// equal the plain linear followed by the activation bit for bit.
 tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
                                    int64_t K, int act, hipStream_t s) {
-  constexpr int WV = 2;
-  int kw = (int)((K + WV - 1) / WV);
-  kw = (kw + 127) & ~127;
+  const int mt = (int)((M + 15) / 16);
+  const int WV = stream_dma_waves(mt);
+  const int kw = stream_dma_kw(K, WV);
   const int Mi = (int)M, Ii = (int)I, Ki = (int)K;
   if (act == TP_ACT_SWIGLU) {
-    if (M > 48) launch_stream_dma<WV, 4, 2, 8, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
-    else launch_stream_dma<WV, 3, 2, 8, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    if (mt <= 2) launch_stream_dma<3, 2, 2, 3, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    else if (mt == 3) launch_stream_dma<2, 3, 2, 3, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    else launch_stream_dma<2, 4, 2, 3, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
   } else {
-    if (M > 48) launch_stream_dma<WV, 4, 2, 8, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
-    else launch_stream_dma<WV, 3, 2, 8, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    if (mt <= 2) launch_stream_dma<3, 2, 1, 4, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    else if (mt == 3) launch_stream_dma<2, 3, 2, 3, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    else launch_stream_dma<2, 4, 2, 3, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
   }
   TPL_LAUNCH_CHECK("gemm_bf16_stream_dma_act");
   return TP_OK;
