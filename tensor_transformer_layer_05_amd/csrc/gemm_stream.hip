@@ -1,4 +1,4 @@
-// Decode bf16 linear for 1..16 tokens: weight streaming.
+// Decode bf16 linear for 1..3 tokens: weight streaming.
 //
 //   Y[m, n] = sum_k X[m, k] * W[n, k]
 //
@@ -204,10 +204,9 @@ static int stream_kw(int64_t K, int waves) {
 
 tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                            bool out_f32, hipStream_t s) {
-  const int mt = (int)((M + 15) / 16);
-  // Two to four token tiles: the kernel that streams weights and tokens
-  // through LDS (whole-line loads for both operands).
-  if (mt >= 2) return gemm_bf16_stream_dma(x, w, y, M, N, K, out_f32, s);
+  // From 4 tokens on, the kernel that streams weights and tokens through LDS
+  // (whole-line loads for both operands) is faster.
+  if (M >= 4) return gemm_bf16_stream_dma(x, w, y, M, N, K, out_f32, s);
   const int waves = stream_waves(N, K);
   const int kw = stream_kw(K, waves);
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
@@ -228,8 +227,7 @@ tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_
 // plain linear followed by the activation bit for bit.
 tp_status gemm_bf16_stream_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
                                int64_t K, int act, hipStream_t s) {
-  const int mt = (int)((M + 15) / 16);
-  if (mt >= 2) return gemm_bf16_stream_dma_act(x, w, h, M, I, K, act, s);
+  if (M >= 4) return gemm_bf16_stream_dma_act(x, w, h, M, I, K, act, s);
   const int waves = stream_waves(act == TP_ACT_SWIGLU ? 2 * I : I, K);
   const int kw = stream_kw(K, waves);
   const int Mi = (int)M, Ii = (int)I, Ki = (int)K;

@@ -1,9 +1,9 @@
-// Decode bf16 linear for 17..64 tokens through LDS: weight streaming.
+// Decode bf16 linear for 4..64 tokens through LDS: weight streaming.
 //
 //   Y[m, n] = sum_k X[m, k] * W[n, k]
 //
 // At decode the weight matrix is read once per call and dominates the HBM
-// bytes, but with 17..64 tokens the token rows are re-read from L2 by every
+// bytes, but with several tokens the token rows are re-read from L2 by every
 // workgroup and make up most of a workgroup's load traffic.  Loads whose 64
 // lanes each take 16 bytes of a different row (the MFMA operand layout) use
 // only half of every 128-byte line they touch, and measured per-CU load
@@ -220,16 +220,16 @@ static void launch_stream_dma(const void* x, const void* w, void* y, int M, int 
 }
 
 // Waves per workgroup by token tiles (the K split; the fused-activation
-// variant must use the same): 3 for 17..32 tokens, 2 for 33..64.  LDS per
-// workgroup = WAVES x S x (16 RT + 16 MT) x 256 bytes <= 144 KB.
-static int stream_dma_waves(int mt) { return mt <= 2 ? 3 : 2; }
+// variant must use the same): 2 for 4..16 tokens, 3 for 17..32, 2 for 33..64.
+// LDS per workgroup = WAVES x S x (16 RT + 16 MT) x 256 bytes <= 144 KB.
+static int stream_dma_waves(int mt) { return mt == 2 ? 3 : 2; }
 
 static int stream_dma_kw(int64_t K, int waves) {
   int kw = (int)((K + waves - 1) / waves);
   return (kw + 127) & ~127;
 }
 
-// Requires 17 <= M <= 64, K % 8 == 0, 16-byte aligned X and W, and M*K and
+// Requires 4 <= M <= 64, K % 8 == 0, 16-byte aligned X and W, and M*K and
 // 32*K elements addressable with 32-bit byte offsets.
 tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M, int64_t N,
                                int64_t K, bool out_f32, hipStream_t s) {
@@ -237,7 +237,8 @@ tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M,
   const int WV = stream_dma_waves(mt);
   const int kw = stream_dma_kw(K, WV);
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
-  if (mt <= 2) launch_stream_dma<3, 2, 1, 4>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
+  if (mt == 1) launch_stream_dma<2, 1, 2, 4>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
+  else if (mt == 2) launch_stream_dma<3, 2, 1, 4>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
   else if (mt == 3) launch_stream_dma<2, 3, 2, 3>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
   else launch_stream_dma<2, 4, 2, 3>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
   TPL_LAUNCH_CHECK("gemm_bf16_stream_dma");
@@ -254,11 +255,13 @@ tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_
   const int kw = stream_dma_kw(K, WV);
   const int Mi = (int)M, Ii = (int)I, Ki = (int)K;
   if (act == TP_ACT_SWIGLU) {
-    if (mt <= 2) launch_stream_dma<3, 2, 2, 3, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    if (mt == 1) launch_stream_dma<2, 1, 2, 4, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    else if (mt == 2) launch_stream_dma<3, 2, 2, 3, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
     else if (mt == 3) launch_stream_dma<2, 3, 2, 3, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
     else launch_stream_dma<2, 4, 2, 3, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
   } else {
-    if (mt <= 2) launch_stream_dma<3, 2, 1, 4, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    if (mt == 1) launch_stream_dma<2, 1, 1, 4, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    else if (mt == 2) launch_stream_dma<3, 2, 1, 4, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
     else if (mt == 3) launch_stream_dma<2, 3, 2, 3, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
     else launch_stream_dma<2, 4, 2, 3, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
   }
