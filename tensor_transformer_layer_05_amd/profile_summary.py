@@ -1,0 +1,149 @@
+"""Turn the rocprofv3 outputs of the profiling runs into the text summaries
+kept in ``profiles/`` (no measurement happens here; it only reads CSV files).
+
+    python3 -m tensor_transformer_layer_05_amd.profile_summary <out_dir>
+
+``<out_dir>`` holds ``prof_bench/`` (kernel trace + stats of a bench run, with
+``prof_bench.log`` beside it), ``pmc_fetch/`` and ``pmc_write/`` (FETCH_SIZE and
+WRITE_SIZE runs of ``profile_drivers gemm_traffic``)."""
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GEMM_SRC = "tensor_transformer_layer_05_amd/csrc/gemm_dma.hip"
+FUSED = "DmaTile<256, 256, 2, 4>, false, true, 1>"
+
+
+def _csv(pattern):
+    files = glob.glob(pattern, recursive=True)
+    if not files:
+        raise FileNotFoundError(pattern)
+    return list(csv.DictReader(open(files[0])))
+
+
+def _counters(d):
+    agg = collections.OrderedDict()
+    for r in _csv(os.path.join(d, "**", "*counter_collection.csv")):
+        k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        agg[k] = agg.get(k, 0.0) + float(r["Counter_Value"])
+    return agg
+
+
+def traffic(out):
+    fetch, write = _counters(os.path.join(out, "pmc_fetch")), _counters(os.path.join(out, "pmc_write"))
+
+    def pick(agg, needle):
+        return [v for (i, n), v in sorted(agg.items()) if needle in n]
+    cf, cw = pick(fetch, "copyBuffer")[0], pick(write, "copyBuffer")[0]
+    gemm_f = pick(fetch, "gemm_bf16_dma_kernel")
+    gemm_w = pick(write, "gemm_bf16_dma_kernel")
+    fs, ws = 262144.0 / cf, 262144.0 / cw
+    S, H, il = 4096, 8192, 14336
+    alg_fused = (S * H + 2 * il * H + S * il) * 2
+    alg_plain = (S * H + 2 * il * H + S * 2 * il) * 2
+    tf = (gemm_f[0] * fs + gemm_w[0] * ws) * 1024
+    tp = (gemm_f[1] * fs + gemm_w[1] * ws) * 1024
+    sha = hashlib.sha256(open(os.path.join(ROOT, GEMM_SRC), "rb").read()).hexdigest()[:16]
+    data = {"kernel": "gemm_bf16_dma_kernel<DmaTile<256,256,2,4>,false,true,1> (SwiGLU epilogue)",
+            "shape_mkn": [S, H, 2 * il], "source": GEMM_SRC, "source_sha256_16": sha,
+            "fetch_kib": round(gemm_f[0], 1), "write_kib": round(gemm_w[0], 1),
+            "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+            "traffic_bytes": int(tf), "algorithmic_bytes": alg_fused}
+    return f"""# HBM traffic of the gate|up projection (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)
+
+Commands (from the repository root; the driver runs one plain 256 MiB device-to-device copy, then one
+gate|up launch with the SwiGLU epilogue, then one plain gate|up launch; M=4096 K=8192 2I=28672 bf16):
+
+```
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o f -- python3 -m tensor_transformer_layer_05_amd.profile_drivers gemm_traffic
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o w -- python3 -m tensor_transformer_layer_05_amd.profile_drivers gemm_traffic
+python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
+```
+
+| dispatch | FETCH_SIZE KiB | WRITE_SIZE KiB |
+|---|---:|---:|
+| plain copy, 256 MiB read + 256 MiB written | {cf:.1f} | {cw:.1f} |
+| gate\\|up + SwiGLU epilogue (output [4096, 14336]) | {gemm_f[0]:.1f} | {gemm_w[0]:.1f} |
+| plain gate\\|up (output [4096, 28672]) | {gemm_f[1]:.1f} | {gemm_w[1]:.1f} |
+
+Calibration: the copy moves 262144 KiB each way, so FETCH_SIZE is scaled by {fs:.4f} and WRITE_SIZE by {ws:.4f}.
+
+- Fused launch: {tf / 1e9:.3f} GB (algorithmic {alg_fused / 1e9:.3f} GB: X and W read once, act(g)*u written once).
+- Plain launch: {tp / 1e9:.3f} GB (algorithmic {alg_plain / 1e9:.3f} GB).
+- The epilogue saves the write of the [4096, 28672] intermediate and the SwiGLU pass that read it back.
+- The excess over the algorithmic bytes is X re-fetched from the Infinity Cache. Each XCD runs 7 successive
+  rounds of 32 tiles, and its 4 MB L2 cannot keep the 8 X tiles (32 MB) of its M-range between rounds.
+
+bench.py reports `roofline.traffic` from the line below only while the kernel source still has this hash.
+
+DATA {json.dumps(data)}
+"""
+
+
+def kernel_stats(out):
+    rows = _csv(os.path.join(out, "prof_bench", "**", "*kernel_stats.csv"))
+    trace = _csv(os.path.join(out, "prof_bench", "**", "*kernel_trace.csv"))
+    bench = [l for l in open(os.path.join(out, "prof_bench.log")) if l.startswith('{"metric"')][0]
+    d = json.loads(bench)
+    f = sorted((r for r in trace if FUSED in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in f]
+    timed = durs[-d["steps"]:]
+    lines = []
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].split("(")[0].replace("void ", "")
+        lines.append(f'| `{name[:100]}` | {r["Calls"]} | {float(r["AverageNs"]) / 1e3:.1f} | '
+                     f'{float(r["MinNs"]) / 1e3:.1f} | {float(r["MaxNs"]) / 1e3:.1f} | {float(r["Percentage"]):.2f} |')
+    return f"""# Kernel stats: bench.py (prefill layer shard + decode shards), rocprofv3 --kernel-trace --stats
+
+Command (from /tmp with TMPDIR=/tmp; REPO = repository root), then the summary script:
+
+```
+rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_bench -o bench -- python3 $REPO/bench.py --steps 5 --warmup 2 --no-cpu-baseline
+python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
+```
+
+The bench line of the same run (under the profiler): value {d['value']} TFLOP/s, {d['ms_per_step']} ms per step;
+the dominant kernel's event-timed average {d['roofline']['avg_launch_ms'] * 1e3:.1f} us. From the trace of the same
+run, the {len(timed)} timed-step launches of that kernel (`gemm_bf16_dma_kernel<..., 1>`, the last {len(timed)} of its
+{len(durs)}) average {sum(timed) / len(timed):.1f} us ({', '.join(f'{x:.1f}' for x in timed)}); the table's averages
+include the set-up and warm-up launches.
+
+| kernel | calls | avg us | min us | max us | % time |
+|---|---:|---:|---:|---:|---:|
+""" + "\n".join(lines) + """
+
+Mapping (prefill calls = 2 set-up passes over both ranks + 2 warm-up + 5 timed steps = 9 per rank-0 call):
+- `gemm_bf16_dma_kernel<DmaTile<256,256,2,4>, false, true, 1>`: gate|up with the SwiGLU epilogue, M=4096 K=8192
+  2I=28672 -> [4096, 14336].
+- `gemm_bf16_dma_kernel<DmaTile<256,256,2,4>, true, true, 0>`: o_proj (K=4096) and down (K=14336), fp32 partials.
+- `gemm_bf16_dma_kernel<DmaTile<256,320,4,2>, false, true, 0>`: fused QKV, N=5120 (16 x 16 tiles).
+- `attn_prefill_tr_kernel`: causal 4096-token attention over 32 local q heads / 4 KV heads.
+- `reduce_rmsnorm_reg_kernel<4>`: sum of the two ranks' attention partials + residual, then the MLP's RMSNorm.
+- `reduce_kernel`, `rmsnorm_reg_kernel<4>`: the final sum of MLP partials; the first RMSNorm.
+- `gemm_stream_kernel<*, 1, *, *, *>`: decode linears with 1..3 tokens; `gemm_stream_dma_kernel<...>`: 4..64 tokens
+  (weights and tokens through the per-wave LDS ring).
+- `attn_decode_kernel<false|true>` + `attn_decode_combine_kernel`: decode attention (contiguous / paged cache).
+- `vocab_argmax_kernel`: the lm_head shard's local greedy step.
+
+Decode calls come from the eager and graph-replayed decode figures; kernel durations are per launch.
+"""
+
+
+def main(argv=None):
+    argv = argv or sys.argv[1:]
+    out = argv[0] if argv else "gpurun_out"
+    open(os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.md"), "w").write(traffic(out))
+    open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w").write(kernel_stats(out))
+    print("wrote profiles/gate_up_gemm_traffic.md and profiles/bench_kernel_stats.md")
+
+
+if __name__ == "__main__":
+    main()
