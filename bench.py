@@ -46,20 +46,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def traffic_source_hash(files):
+    """SHA-256 (first 16 hex digits) over the kernel's source files, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def recorded_traffic(name="gate_up_gemm_traffic.md"):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 FETCH_SIZE/WRITE_SIZE summary (scaled by a plain copy of known
-    size), or None once the kernel source no longer matches the hash recorded
+    size), or None once the kernel's sources no longer match the hash recorded
     with the counters."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", name)
     try:
         line = [l for l in open(path) if l.startswith("DATA ")][0]
         data = json.loads(line[5:])
-        src = open(os.path.join(ROOT, data["source"]), "rb").read()
+        if traffic_source_hash(data["sources"]) != data["sources_sha256_16"]:
+            return None
     except (OSError, IndexError, KeyError, ValueError):
-        return None
-    if hashlib.sha256(src).hexdigest()[:16] != data["source_sha256_16"]:
         return None
     return data
 

@@ -24,15 +24,15 @@ __device__ __forceinline__ float bf_lo(uint32_t pair) { return __uint_as_float(p
 __device__ __forceinline__ float bf_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// Round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t f2bf_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// Round to nearest even with gfx950's v_cvt_pk_bf16_f32 (one instruction
+// per pair; NaN stays a NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return f2bf_bits(lo) | (f2bf_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ uint32_t f2bf_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // 8 bf16 packed in a u32x4 -> 8 floats

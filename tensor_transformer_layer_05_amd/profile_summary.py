@@ -17,7 +17,8 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-GEMM_SRC = "tensor_transformer_layer_05_amd/csrc/gemm_dma.hip"
+GEMM_SRCS = ["tensor_transformer_layer_05_amd/csrc/gemm_dma.hip",
+             "tensor_transformer_layer_05_amd/csrc/common.h"]
 FUSED = "DmaTile<256, 256, 2, 4>, false, true, 1>"
 
 
@@ -50,9 +51,12 @@ def traffic(out):
     alg_plain = (S * H + 2 * il * H + S * 2 * il) * 2
     tf = (gemm_f[0] * fs + gemm_w[0] * ws) * 1024
     tp = (gemm_f[1] * fs + gemm_w[1] * ws) * 1024
-    sha = hashlib.sha256(open(os.path.join(ROOT, GEMM_SRC), "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    sha = h.hexdigest()[:16]
     data = {"kernel": "gemm_bf16_dma_kernel<DmaTile<256,256,2,4>,false,true,1> (SwiGLU epilogue)",
-            "shape_mkn": [S, H, 2 * il], "source": GEMM_SRC, "source_sha256_16": sha,
+            "shape_mkn": [S, H, 2 * il], "sources": GEMM_SRCS, "sources_sha256_16": sha,
             "fetch_kib": round(gemm_f[0], 1), "write_kib": round(gemm_w[0], 1),
             "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
             "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
@@ -82,7 +86,7 @@ Calibration: the copy moves 262144 KiB each way, so FETCH_SIZE is scaled by {fs:
 - The excess over the algorithmic bytes is X re-fetched from the Infinity Cache. Each XCD runs 7 successive
   rounds of 32 tiles, and its 4 MB L2 cannot keep the 8 X tiles (32 MB) of its M-range between rounds.
 
-bench.py reports `roofline.traffic` from the line below only while the kernel source still has this hash.
+bench.py reports `roofline.traffic` from the line below only while the kernel's sources still have this hash.
 
 DATA {json.dumps(data)}
 """
