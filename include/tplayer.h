@@ -29,7 +29,9 @@
  *     even.
  *   - Fast vector paths need 16-byte aligned base pointers and row lengths
  *     that are multiples of 16 bytes; other inputs take a slower element path
- *     with the same results.
+ *     (same arithmetic; sums may be ordered differently, so results can differ
+ *     in the last float32 bits).  For given sizes, alignment and dtype a call
+ *     always takes the same path and gives the same bits.
  */
 #ifndef TPLAYER_H
 #define TPLAYER_H
