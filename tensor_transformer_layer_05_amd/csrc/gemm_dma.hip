@@ -29,7 +29,8 @@
 //    256x320 tiles 8 waves of 64x160, for grids that 256x256 tiles would
 //    leave with a mostly empty last round.
 //  * Workgroup ids are remapped so that consecutive tile ids share an XCD
-//    (one L2 per XCD), walking groups of 8 M-tiles.
+//    (one L2 per XCD), walking groups of 4 M-tiles (measured: 4 and 8 within
+//    1%, 2 and 16 slower).
 #include "common.h"
 
 namespace tpl {
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   const int tiles_n = (N + OUT_BN - 1) / OUT_BN;
   const int ntile = tiles_m * tiles_n;
   const int pid = xcd_remap(blockIdx.x, ntile);
-  constexpr int GROUP_M = 8;
+  constexpr int GROUP_M = 4;
   const int in_group = GROUP_M * tiles_n;
   const int first_m = (pid / in_group) * GROUP_M;
   const int gsize = min(tiles_m - first_m, GROUP_M);
