@@ -160,12 +160,13 @@ size_t tp_local_attention_workspace(int64_t B, int64_t Sq, int64_t Skv,
  * key position `pos` (P1 "Tensor parallel 对 KV cache 的影响": each rank keeps
  * the cache of its own heads only).
  *   k_new, v_new : element (b,j,d) at k_new[b*new_stride + j*D + d]
- *   k_cache, v_cache : element (b,t,j,d) at k_cache[b*cs[0] + t*cs[1] + j*cs[2] + d]
- *   dt must be TP_BF16.
+ *   k_cache, v_cache : element (b,t,j,d) at k_cache[b*cs[0] + t*cs[1] + j*cs[2] + d],
+ *                      t < T (the cache's key capacity)
+ *   0 <= pos < T (TP_ERR_SHAPE otherwise).  dt must be TP_BF16.
  */
 tp_status tp_kv_append(const void* k_new, const void* v_new, int64_t new_stride,
                        void* k_cache, void* v_cache, const int64_t cs[3],
-                       int64_t B, int64_t Hkv, int64_t D, int64_t pos,
+                       int64_t B, int64_t Hkv, int64_t D, int64_t T, int64_t pos,
                        tp_dtype dt, void* stream);
 
 /*

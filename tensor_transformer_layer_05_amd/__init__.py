@@ -55,7 +55,7 @@ _SIGS = {
                                           _i64, _i64, _i64, ctypes.c_int, ctypes.c_float, ctypes.c_int,
                                           _vp, ctypes.c_size_t, _vp]),
     "tp_local_attention_workspace": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64, _i64]),
-    "tp_kv_append": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64p, _i64, _i64, _i64, _i64,
+    "tp_kv_append": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i64,
                                     ctypes.c_int, _vp]),
     "tp_reduce_partials": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, _vp, _vp, _i64, _i64,
                                           ctypes.c_int, _vp]),
@@ -283,7 +283,7 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
     cs = _arr3([k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)])
     _check("tp_kv_append", lib().tp_kv_append(
         k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_cache.data_ptr(), v_cache.data_ptr(),
-        cs, B, H, D, pos, _DT[k_new.dtype], _stream(k_new)))
+        cs, B, H, D, k_cache.shape[1], pos, _DT[k_new.dtype], _stream(k_new)))
 
 
 def reduce_partials(partials, residual: torch.Tensor | None = None, out: torch.Tensor | None = None,

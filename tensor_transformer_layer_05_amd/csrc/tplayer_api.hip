@@ -193,11 +193,11 @@ tp_status tp_local_attention(const void* q, const int64_t qs[3], const void* k, 
 
 tp_status tp_kv_append(const void* k_new, const void* v_new, int64_t new_stride, void* k_cache,
                        void* v_cache, const int64_t cs[3], int64_t B, int64_t Hkv, int64_t D,
-                       int64_t pos, tp_dtype dt, void* stream) {
+                       int64_t T, int64_t pos, tp_dtype dt, void* stream) {
   if (!k_new || !v_new || !k_cache || !v_cache || !cs) return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
   if (dt != TP_BF16) return TP_ERR_UNSUPPORTED;
-  if (B <= 0 || Hkv <= 0 || D <= 0 || pos < 0 || new_stride < Hkv * D) return TP_ERR_SHAPE;
+  if (B <= 0 || Hkv <= 0 || D <= 0 || pos < 0 || pos >= T || new_stride < Hkv * D) return TP_ERR_SHAPE;
   if (cs[0] < 0 || cs[1] < 0 || cs[2] < 0) return TP_ERR_SHAPE;
   if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(k_cache, 2) || !aligned(v_cache, 2))
     return TP_ERR_ALIGN;

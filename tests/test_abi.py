@@ -152,10 +152,11 @@ def test_rmsnorm_and_append_validation(lib):
     assert lib.tp_rmsnorm(P, P, P + 1, 4, 8, 1e-5, 1, S) == ALIGN
     cs = _s3(2 * 64 * 128, 128, 64 * 128)
     f = lib.tp_kv_append
-    assert f(None, P, 256, P, P, cs, 2, 2, 128, 0, 1, S) == NULL
-    assert f(P, P, 128, P, P, cs, 2, 2, 128, 0, 1, S) == SHAPE     # row stride < Hkv*D
-    assert f(P, P, 256, P, P, cs, 2, 2, 128, -1, 1, S) == SHAPE
-    assert f(P, P, 256, P, P, cs, 2, 2, 128, 0, 0, S) == UNSUPPORTED
+    assert f(None, P, 256, P, P, cs, 2, 2, 128, 64, 0, 1, S) == NULL
+    assert f(P, P, 128, P, P, cs, 2, 2, 128, 64, 0, 1, S) == SHAPE     # row stride < Hkv*D
+    assert f(P, P, 256, P, P, cs, 2, 2, 128, 64, -1, 1, S) == SHAPE
+    assert f(P, P, 256, P, P, cs, 2, 2, 128, 64, 64, 1, S) == SHAPE    # pos past the cache
+    assert f(P, P, 256, P, P, cs, 2, 2, 128, 64, 0, 0, S) == UNSUPPORTED
 
 
 @no_gpu
