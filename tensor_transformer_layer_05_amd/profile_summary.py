@@ -83,8 +83,10 @@ Calibration: the copy moves 262144 KiB each way, so FETCH_SIZE is scaled by {fs:
 - Fused launch: {tf / 1e9:.3f} GB (algorithmic {alg_fused / 1e9:.3f} GB: X and W read once, act(g)*u written once).
 - Plain launch: {tp / 1e9:.3f} GB (algorithmic {alg_plain / 1e9:.3f} GB).
 - The epilogue saves the write of the [4096, 28672] intermediate and the SwiGLU pass that read it back.
-- The excess over the algorithmic bytes is X re-fetched from the Infinity Cache. Each XCD runs 7 successive
-  rounds of 32 tiles, and its 4 MB L2 cannot keep the 8 X tiles (32 MB) of its M-range between rounds.
+- FETCH_SIZE counts reads that miss an XCD's L2; they may still hit the Infinity Cache. Each XCD runs 7
+  successive rounds of 32 tiles (4 M-tiles x 8 N-tiles), and its 4 MB L2 holds only the k-slices in flight,
+  so every round fetches its 4 X and 8 W row blocks (4 MB each) again: 8 XCDs x 7 rounds x 48 MB = 2.69 GB
+  of reads plus 0.12 GB of output is the floor for this tile order. The rest of the excess is small.
 
 bench.py reports `roofline.traffic` from the line below only while the kernel's sources still have this hash.
 
