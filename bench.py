@@ -1,6 +1,6 @@
 """Benchmark one tensor-parallel rank's decoder-layer shard on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-ffn]
 
 A step is one pass of the whole path for rank 0 of a TP=2 prefill layer
 (4096 tokens, hidden 8192, 64 q / 8 KV heads, head_dim 128, intermediate
@@ -17,6 +17,8 @@ cache), the same attention at TP=16 with replicated KV heads and the vocab-paral
 greedy argmax (TP=8), timed over rotating
 copies of the weights/caches so that the 256 MB Infinity Cache cannot hold
 the working set between steps (also as HIP-graph replays, "graph_ms").
+Key "ffn_tp8": rank 0's shard of the GELU FFN at TP=8 (2048 tokens, hidden
+12288): fc1 with GELU in its epilogue, fc2, and the sum of 8 partials.
 """
 from __future__ import annotations
 
@@ -357,6 +359,39 @@ def decode_figures(steps=30, warmup=5, copies=4):
     return out
 
 
+def ffn_figures(steps=20, warmup=3):
+    """Rank 0's shard of the GELU FFN at TP 8 (hidden 12288, 4x expansion,
+    2048 tokens): fc1 with GELU in its epilogue, fc2 to an fp32 partial, and the
+    8-rank sum of partials.  The eight partial buffers all sit on this GPU,
+    standing in for the peers' buffers of the in-HBM reduction."""
+    c = I.config("gelu_mlp_tp8")
+    M, H, F, R = c.tokens[0], c.hidden, c.inter, c.tp
+    fl_ = F // R
+    x = I.normal(c.seed, "x", (M, H), c.x_std).dev.to(DEV)
+    w1 = I.normal(c.seed, "w1", (fl_, H), c.w_std, rank=0).dev.to(DEV)
+    w2 = I.normal(c.seed, "w2", (H, fl_), c.w_std, rank=0).dev.to(DEV)
+    a = torch.empty((M, fl_), dtype=torch.bfloat16, device=DEV)
+    parts = [torch.empty((M, H), dtype=torch.float32, device=DEV) for _ in range(R)]
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=DEV)
+    tpl.column_linear_act(x, w1, "gelu", out=a)
+    for p_ in parts:
+        tpl.row_linear_partial(a, w2, out=p_)
+    ms1 = _median_ms(lambda i: tpl.column_linear_act(x, w1, "gelu", out=a), steps, warmup)
+    ms2 = _median_ms(lambda i: tpl.row_linear_partial(a, w2, out=parts[0]), steps, warmup)
+    msr = _median_ms(lambda i: tpl.reduce_partials(parts, out=y), steps, warmup)
+    f1 = 2.0 * M * H * fl_
+    rb = R * M * H * 4 + M * H * 2
+    out = {
+        "workload": f"gelu_mlp_tp8 rank 0: fc1 [{M},{H}]x[{H},{fl_}] + GELU, fc2 [{M},{fl_}]x[{fl_},{H}] "
+                    f"-> fp32, sum of {R} partials -> bf16",
+        "fc1_gelu": {"ms": ms1, "TFLOP/s": f1 / ms1 / 1e9, "mfma_frac": f1 / ms1 / 1e9 / PEAK_BF16_TFLOPS},
+        "fc2": {"ms": ms2, "TFLOP/s": f1 / ms2 / 1e9, "mfma_frac": f1 / ms2 / 1e9 / PEAK_BF16_TFLOPS},
+        "reduce8": {"ms": msr, "GB/s": rb / msr / 1e6, "hbm_frac": rb / msr / 1e6 / PEAK_HBM_GBPS},
+    }
+    del parts
+    return out
+
+
 def _lm_head_figures(steps, warmup, copies=2):
     """Rank 0's vocab-parallel lm_head shard with its local greedy argmax
     (128256-token vocab at TP 8: 16032 x 8192 bf16 rows, 263 MB per copy)."""
@@ -450,6 +485,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-ffn", action="store_true")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the multi-GPU all-reduce is "
@@ -502,6 +538,9 @@ def main(argv=None):
     if not a.no_decode:
         log("timing decode shards")
         res["decode"] = decode_figures()
+    if not a.no_ffn:
+        log("timing the GELU FFN shard at TP=8")
+        res["ffn_tp8"] = ffn_figures()
     if not a.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(st)

@@ -26,8 +26,8 @@
 //    barrier so that the next step's first fragment reads overlap them.
 //  * 256x256 tiles run 8 waves (2 per SIMD, 128x64 per wave, accumulators in
 //    128 VGPRs); 128x128 tiles run 4 waves with 2 workgroups per CU, and
-//    256x320 tiles 8 waves of 64x160, for grids that 256x256 tiles would
-//    leave with a mostly empty last round.
+//    256x320 and 256x192 tiles 8 waves of 64x160 and 64x96, for grids that
+//    256x256 tiles would leave with a partly empty last round.
 //  * Workgroup ids are remapped so that consecutive tile ids share an XCD
 //    (one L2 per XCD), walking groups of 4 M-tiles (measured: 4 and 8 within
 //    1%, 2 and 16 slower).
@@ -300,6 +300,10 @@ using Dma128 = DmaTile<128, 128, 2, 2>;   // 4 waves, two workgroups per CU
 // 256x256 tiles leave a mostly empty last round, e.g. the fused QKV at
 // N = 5120: 16 x 16 tiles fill 256 CUs exactly once.
 using Dma320 = DmaTile<256, 320, 4, 2>;
+// 256x192: 8 waves of 64x96 (112 KB).  For grids that 256x256 tiles fill only
+// partly, e.g. a 2048 x 6144 output: 8 x 32 tiles fill 256 CUs once where
+// 8 x 24 tiles of 256x256 would leave a quarter of them idle.
+using Dma192 = DmaTile<256, 192, 4, 2>;
 
 template <class C, int EPI>
 static tp_status launch_dma(const void* x, const void* w, void* y, int M, int N, int K,
@@ -325,18 +329,22 @@ static tp_status launch_dma(const void* x, const void* w, void* y, int M, int N,
   return TP_OK;
 }
 
-// 0 = 256x256 (8 waves), 1 = 128x128 (4 waves), 2 = 256x320 (8 waves).
+// 0 = 256x256 (8 waves), 1 = 128x128 (4 waves), 2 = 256x320 (8 waves),
+// 3 = 256x192 (8 waves).
 // Estimated time = full-chip rounds x round time in units of a 256x256 round:
 // a round of 128x128 tiles (two per CU) does half that work at ~85% of its
 // efficiency, a round of 256x320 tiles does 1.25x the work at the same
-// efficiency (measured on gate|up-, qkv- and o_proj-shaped problems).
+// efficiency, a round of 256x192 tiles takes 0.85 (measured on gate|up-, qkv-,
+// o_proj-, down- and GELU-FFN-shaped problems).
 // `wide` allows the 256x320 tile (its epilogue has no room for the SwiGLU
 // exchange).
 int gemm_dma_pick_tile(int M, int N, bool wide) {
   const double t256 = ceil((double)((M + 255) / 256) * ((N + 255) / 256) / 256.0);
   const double t128 = ceil((double)((M + 127) / 128) * ((N + 127) / 128) / 512.0) * 0.5 / 0.85;
   const double t320 = wide ? ceil((double)((M + 255) / 256) * ((N + 319) / 320) / 256.0) * 1.25 : 1e30;
-  if (t320 < t256 && t320 < t128) return 2;
+  const double t192 = ceil((double)((M + 255) / 256) * ((N + 191) / 192) / 256.0) * 0.85;
+  if (t320 < t256 && t320 < t128 && t320 < t192) return 2;
+  if (t192 < t256 && t192 < t128) return 3;
   return t128 < t256 ? 1 : 0;
 }
 
@@ -345,6 +353,7 @@ tp_status gemm_bf16_dma(const void* x, const void* w, void* y, int64_t M, int64_
   const int pick = force_tile >= 0 ? force_tile : gemm_dma_pick_tile((int)M, (int)N, true);
   if (pick == 0) return launch_dma<Dma256, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
   if (pick == 2) return launch_dma<Dma320, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
+  if (pick == 3) return launch_dma<Dma192, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
   return launch_dma<Dma128, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
 }
 
@@ -357,11 +366,13 @@ tp_status gemm_bf16_dma_act(const void* x, const void* w, void* h, int64_t M, in
     // a paired 256-wide tile yields 128 outputs: pick the tile on the doubled width
     const int pick = gemm_dma_pick_tile((int)M, (int)(2 * I), false);
     if (pick == 0) return launch_dma<Dma256, 1>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
+    if (pick == 3) return launch_dma<Dma192, 1>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
     return launch_dma<Dma128, 1>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
   }
   const int pick = gemm_dma_pick_tile((int)M, (int)I, true);
   if (pick == 0) return launch_dma<Dma256, 2>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
   if (pick == 2) return launch_dma<Dma320, 2>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
+  if (pick == 3) return launch_dma<Dma192, 2>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
   return launch_dma<Dma128, 2>(x, w, h, (int)M, (int)I, (int)K, false, vec_out, s);
 }
 

@@ -46,6 +46,7 @@ ACT_SHAPES = [
     (1000, 2048, 700),
     (2048, 1024, 3584),  # 256x256 tiles
     (4000, 520, 5100),   # GELU: 256x320 tiles
+    (1800, 264, 4700),   # GELU: 256x192 tiles; SwiGLU: 256x192 pairs (96 outputs each)
 ]
 
 

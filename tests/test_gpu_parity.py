@@ -58,6 +58,7 @@ INT_SHAPES = [
     # MFMA tile path: ragged M/N/K, each tile shape
     (65, 64, 16), (200, 136, 130), (300, 520, 300), (512, 264, 640), (4000, 264, 4000),
     (4096, 200, 2048), (4000, 136, 5100),   # the last picks 256x320 tiles
+    (1800, 136, 4700),                      # 256x192 tiles, ragged M and N
     # element path (K not a multiple of 8)
     (5, 13, 7), (70, 37, 50),
 ]
@@ -86,7 +87,8 @@ def test_linear_integer_exact(M, K, N, dtype):
 # ---------------------------------------------------------------------------
 
 FLOAT_SHAPES = [(1, 4096, 1536), (8, 8192, 512), (32, 1024, 4096), (64, 3584, 264), (17, 520, 100),
-                (128, 1024, 768), (1000, 2048, 1000), (4096, 256, 4096), (4096, 1024, 5120)]
+                (128, 1024, 768), (1000, 2048, 1000), (4096, 256, 4096), (4096, 1024, 5120),
+                (2048, 1032, 6144)]   # the last: 256x192 tiles
 
 
 @pytest.mark.parametrize("M,K,N", FLOAT_SHAPES)
