@@ -180,18 +180,24 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], st, 0, 0, 0);
     }
     // online softmax for column c32 over this tile's 32 keys (16 here, 16 in lane ^ 32)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] *= a.scale_log2;
+    const int t0 = tw + i * kDecTile;
+    if (t0 + kDecTile > L) {   // wave-uniform: only the span's last tile is ragged
+      // key t0 + 4 hl + 8 (r / 4) + r % 4 is valid while it is < L
+      const int rel = L - (t0 + 4 * hl);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) >= rel) st[r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = tw + i * kDecTile + 8 * (r >> 2) + 4 * hl + (r & 3);
-      const float x = t < L ? st[r] * a.scale_log2 : -INFINITY;
-      st[r] = x;
-      mx = fmaxf(mx, x);
-    }
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[r]);
     mx = dec_pair_max(mx);
     const float mnew = fmaxf(mrun, mx);
     const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = exp2f(mrun - muse);
+    // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 may flush to zero
+    const float alpha = __builtin_amdgcn_exp2f(mrun - muse);
     mrun = mnew;
     bf16x8 pb[2];
     float psum = 0.f;
@@ -200,7 +206,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = exp2f(st[half * 8 + e] - muse);
+        p[e] = __builtin_amdgcn_exp2f(st[half * 8 + e] - muse);
         psum += p[e];
       }
       pb[half] = as_bf16x8(pack8(p));

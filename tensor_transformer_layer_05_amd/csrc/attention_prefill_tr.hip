@@ -163,27 +163,35 @@ __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
         }
       }
 
-      // scale into the log2 domain, mask, online softmax for query c32
+      // scale into the log2 domain, mask, online softmax for query c32.  The
+      // mask sits behind one wave-uniform branch (most tiles need none).
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[kb][r] *= a.scale_log2;
       const bool need_mask = (t_first + kBK > a.Skv) ||
                              (a.causal && t_first + kBK - 1 > qw0 + off);
-      const int qpos = qw0 + c32 + off;
+      if (need_mask) {
+        // key t = t_first + 4 hl + 32 kb + 8 (r / 4) + r % 4 is valid while t < lim
+        const int qpos = qw0 + c32 + off;
+        const int lim = a.causal ? min(a.Skv, qpos + 1) : a.Skv;
+        const int rel = lim - (t_first + 4 * hl);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= rel) st[kb][r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = st[kb][r] * a.scale_log2;
-          if (need_mask) {
-            const int t = t_first + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (t >= a.Skv || (a.causal && t > qpos)) x = -INFINITY;
-          }
-          st[kb][r] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
       mx = pair_max(mx);
       const float mnew = fmaxf(mrun, mx);
       const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = exp2f(mrun - muse);
+      // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 may flush to zero
+      const float alpha = __builtin_amdgcn_exp2f(mrun - muse);
       mrun = mnew;
       bf16x8 pb[4];
       float psum = 0.f;
@@ -194,7 +202,7 @@ __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
           float p[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            p[e] = exp2f(st[kb][half * 8 + e] - muse);
+            p[e] = __builtin_amdgcn_exp2f(st[kb][half * 8 + e] - muse);
             psum += p[e];
           }
           pb[kb * 2 + half] = as_bf16x8(pack8(p));
