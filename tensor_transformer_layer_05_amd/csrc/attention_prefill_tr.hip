@@ -15,11 +15,14 @@
 //    each 16-lane group, lane s addresses the 4 d of row k0 + s/4 starting at
 //    d0 + 4 (s % 4), and lane j receives V[k0 + e][d0 + j], e = 0..3.
 //  * K and V tiles reach LDS through buffer_load_dwordx4 ... lds (1 KB = 4
-//    key rows per wave-level load), double-buffered, one barrier per tile.
-//    Rows past the key span read as zero through the buffer bound.  LDS rows
-//    are 256 bytes; K's 16-byte chunks are XOR-ed with (key % 16) so that the
-//    16 rows of an A-fragment read hit distinct banks, V's with 4 (key % 4)
-//    so that the 4 rows x 4 chunks of a transposed read do.
+//    key rows per wave-level load), one barrier per tile.  K runs two tiles
+//    ahead of the O product and V one, in two slots each: while the scores
+//    of tile t+1 are turned into probabilities, the MFMAs of O += V P for
+//    tile t can run.  Rows past the key span read as zero through the buffer
+//    bound.  LDS rows are 256 bytes; K's 16-byte chunks are XOR-ed with
+//    (key % 16) so that the 16 rows of an A-fragment read hit distinct banks,
+//    V's with 4 (key % 4) so that the 4 rows x 4 chunks of a transposed read
+//    do.
 //  * Causal masking is aligned to the end of the key span; tiles entirely
 //    above a wave's last query are skipped by that wave.  Workgroups are
 //    ordered longest first across all heads to balance the causal triangle.
@@ -59,7 +62,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 }  // namespace
 
 __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kTileE];  // [stage][K | V]
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * kTileE];  // K slots 0, 1, V slots 0, 1
 
   // longest-first over (query block, head, batch)
   const int nqb = (a.Sq + kBQ - 1) / kBQ;
@@ -104,21 +107,30 @@ __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
       (void*)(a.v + b * a.ks0 + hk * a.ks2), 0, nrec, 0x00020000);
   const int lr = lane >> 4, lp = lane & 15;   // row within the 4-row load, LDS chunk
   const uint32_t row_bytes = (uint32_t)(a.ks1 * 2);
-  auto issue = [&](int kt) {
-    const int stage = kt & 1;
-    TPL_LDS uint16_t* kdst = (TPL_LDS uint16_t*)lds + stage * 2 * kTileE;
-    TPL_LDS uint16_t* vdst = kdst + kTileE;
+  // LDS: K slots 0,1 then V slots 0,1 (64 keys x 256 B each).  K runs two
+  // tiles ahead of the O product, V one.
+  auto issue_k = [&](int kt) {
+    TPL_LDS uint16_t* dst = (TPL_LDS uint16_t*)lds + (kt & 1) * kTileE;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int row = (wave * 2 + i) * 4 + lr;           // 0..63 within the tile
+      const int row = (wave * 2 + i) * 4 + lr;
       const int t = kt * kBK + row;
-      const int kc = lp ^ (row & 15), vc = lp ^ (4 * (row & 3));
-      const uint32_t rb = (uint32_t)t * row_bytes;
+      const int kc = lp ^ (row & 15);
       const bool ok = t < a.Skv;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TPL_LDS void*)(kdst + (wave * 2 + i) * 4 * kD), 16,
-                                               ok ? rb + (uint32_t)kc * 16u : 0x80000000u, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TPL_LDS void*)(vdst + (wave * 2 + i) * 4 * kD), 16,
-                                               ok ? rb + (uint32_t)vc * 16u : 0x80000000u, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TPL_LDS void*)(dst + (wave * 2 + i) * 4 * kD), 16,
+                                               ok ? (uint32_t)t * row_bytes + (uint32_t)kc * 16u : 0x80000000u, 0, 0, 0);
+    }
+  };
+  auto issue_v = [&](int kt) {
+    TPL_LDS uint16_t* dst = (TPL_LDS uint16_t*)lds + (2 + (kt & 1)) * kTileE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (wave * 2 + i) * 4 + lr;
+      const int t = kt * kBK + row;
+      const int vc = lp ^ (4 * (row & 3));
+      const bool ok = t < a.Skv;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TPL_LDS void*)(dst + (wave * 2 + i) * 4 * kD), 16,
+                                               ok ? (uint32_t)t * row_bytes + (uint32_t)vc * 16u : 0x80000000u, 0, 0, 0);
     }
   };
 
@@ -135,112 +147,145 @@ __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
   const int tr_row = sidx >> 2;                      // + k0
   const int tr_d = 16 * (g16 & 1) + 4 * (sidx & 3);  // + 32 db
 
-  if (nkt > 0) issue(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
+  // tiles this wave takes part in (causal: up to its last query's last key)
+  const int nw = (wave_active && wave_last_key >= 0) ? min(nkt, wave_last_key / kBK + 1) : 0;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) issue(kt + 1);
-    const int t_first = kt * kBK;
-    const uint16_t* ks = lds + (kt & 1) * 2 * kTileE;
-    const uint16_t* vs = ks + kTileE;
-
-    if (wave_active && t_first <= wave_last_key) {
-      // S^T[key, query] for 2 blocks of 32 keys
-      f32x16 st[2];
+  // S^T[key, query] of tile kt, 2 blocks of 32 keys (K from slot kt & 1)
+  f32x16 st[2];
+  auto s_tile = [&](int kt) {
+    const uint16_t* ks = lds + (kt & 1) * kTileE;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int row = kb * 32 + c32;
-          const int ch = (2 * kk + hl) ^ (row & 15);
-          const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + row * kD + ch * 8));
-          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], st[kb], 0, 0, 0);
-        }
-      }
-
-      // scale into the log2 domain, mask, online softmax for query c32.  The
-      // mask sits behind one wave-uniform branch (most tiles need none).
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[kb][r] *= a.scale_log2;
-      const bool need_mask = (t_first + kBK > a.Skv) ||
-                             (a.causal && t_first + kBK - 1 > qw0 + off);
-      if (need_mask) {
-        // key t = t_first + 4 hl + 32 kb + 8 (r / 4) + r % 4 is valid while t < lim
-        const int qpos = qw0 + c32 + off;
-        const int lim = a.causal ? min(a.Skv, qpos + 1) : a.Skv;
-        const int rel = lim - (t_first + 4 * hl);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= rel) st[kb][r] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-      mx = pair_max(mx);
-      const float mnew = fmaxf(mrun, mx);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 may flush to zero
-      const float alpha = __builtin_amdgcn_exp2f(mrun - muse);
-      mrun = mnew;
-      bf16x8 pb[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(st[kb][half * 8 + e] - muse);
-            psum += p[e];
-          }
-          pb[kb * 2 + half] = as_bf16x8(pack8(p));
-        }
-      lrun = lrun * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-      // O^T[d, query] += V^T[d, keys] P^T[keys, query], 16 keys per step.
-      // Step (kb, half) covers keys kb*32 + 16 half + {4 hl + 0..3, 8 + 4 hl + 0..3}.
-#pragma unroll
-      for (int step = 0; step < 4; ++step) {
-        const int k0 = (step >> 1) * 32 + (step & 1) * 16 + 4 * hl;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int d = 32 * db + tr_d;
-          s16x4 lo, hi;
-          {
-            const int row = k0 + tr_row;
-            const int pos = ((d >> 3) ^ (4 * (row & 3))) * 8 + (d & 7);
-            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (TPL_LDS s16x4*)((TPL_LDS uint16_t*)vs + row * kD + pos));
-          }
-          {
-            const int row = k0 + 8 + tr_row;
-            const int pos = ((d >> 3) ^ (4 * (row & 3))) * 8 + (d & 7);
-            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (TPL_LDS s16x4*)((TPL_LDS uint16_t*)vs + row * kD + pos));
-          }
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          const bf16x8 af = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[step], oacc[db], 0, 0, 0);
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + c32;
+        const int ch = (2 * kk + hl) ^ (row & 15);
+        const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + row * kD + ch * 8));
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], st[kb], 0, 0, 0);
       }
     }
+  };
+  // scores into the log2 domain, then the mask behind one wave-uniform branch
+  // (only diagonal and ragged tiles need it): key t = t_first + 4 hl + 32 kb +
+  // 8 (r / 4) + r % 4 is valid while t < lim
+  auto softmax_a = [&](int kt) {
+    const int t_first = kt * kBK;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[kb][r] *= a.scale_log2;
+    const bool need_mask = (t_first + kBK > a.Skv) ||
+                           (a.causal && t_first + kBK - 1 > qw0 + off);
+    if (need_mask) {
+      const int qpos = qw0 + c32 + off;
+      const int lim = a.causal ? min(a.Skv, qpos + 1) : a.Skv;
+      const int rel = lim - (t_first + 4 * hl);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= rel) st[kb][r] = -INFINITY;
+    }
+  };
+  // online softmax for query c32: probabilities into pb (bf16, the B operand of
+  // the O product), running max and sum updated; returns the factor that
+  // rescales the older O sums.  v_exp_f32 is called directly: its arguments
+  // are <= 0, and results below 2^-126 may flush to zero.
+  auto softmax_b = [&](bf16x8* pb) -> float {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
+    mx = pair_max(mx);
+    const float mnew = fmaxf(mrun, mx);
+    const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(mrun - muse);
+    mrun = mnew;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(st[kb][half * 8 + e] - muse);
+          psum += p[e];
+        }
+        pb[kb * 2 + half] = as_bf16x8(pack8(p));
+      }
+    lrun = lrun * alpha + psum;
+    return alpha;
+  };
+  // O^T[d, query] += V^T[d, keys] P^T[keys, query], 16 keys per step (V from
+  // slot kt & 1).  Step (kb, half) covers keys kb*32 + 16 half + {4 hl + 0..3,
+  // 8 + 4 hl + 0..3} (the P^T register order).
+  auto o_tile = [&](int kt, const bf16x8* pb) {
+    const uint16_t* vs = lds + (2 + (kt & 1)) * kTileE;
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      const int k0 = (step >> 1) * 32 + (step & 1) * 16 + 4 * hl;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int d = 32 * db + tr_d;
+        s16x4 lo, hi;
+        {
+          const int row = k0 + tr_row;
+          const int pos = ((d >> 3) ^ (4 * (row & 3))) * 8 + (d & 7);
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (TPL_LDS s16x4*)((TPL_LDS uint16_t*)vs + row * kD + pos));
+        }
+        {
+          const int row = k0 + 8 + tr_row;
+          const int pos = ((d >> 3) ^ (4 * (row & 3))) * 8 + (d & 7);
+          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (TPL_LDS s16x4*)((TPL_LDS uint16_t*)vs + row * kD + pos));
+        }
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const bf16x8 af = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[step], oacc[db], 0, 0, 0);
+      }
+    }
+  };
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+  };
 
+  bf16x8 pb[4], pn[4];
+  if (nkt > 0) { issue_k(0); issue_v(0); }
+  if (nkt > 1) issue_k(1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  if (nw > 0) {
+    s_tile(0);
+    softmax_a(0);
+    softmax_b(pb);
+  }
+  // Iteration kt: scores and probabilities of tile kt+1, O product of tile kt
+  // (whose probabilities the previous iteration made); loads of V(kt+1) and
+  // K(kt+2) into the slots that V(kt-1) and K(kt) left.
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 1 < nkt) issue_v(kt + 1);
+    if (kt + 2 < nkt) issue_k(kt + 2);
+    if (kt + 1 < nw) {
+      s_tile(kt + 1);
+      softmax_a(kt + 1);
+      o_tile(kt, pb);
+      const float alpha = softmax_b(pn);
+      rescale(alpha);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = pn[i];
+    } else if (kt < nw) {
+      o_tile(kt, pb);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
