@@ -25,9 +25,14 @@
 //    first two sub-steps, and the last sub-step's MFMAs are split around the
 //    barrier so that the next step's first fragment reads overlap them.
 //  * 256x256 tiles run 8 waves (2 per SIMD, 128x64 per wave, accumulators in
-//    128 VGPRs); 128x128 tiles run 4 waves with 2 workgroups per CU, and
-//    256x320 and 256x192 tiles 8 waves of 64x160 and 64x96, for grids that
-//    256x256 tiles would leave with a partly empty last round.
+//    128 VGPRs), or for fp32 partials 4 waves of 128x128 (one per SIMD, 256
+//    accumulators, tile loads and fragment reads paired with MFMAs by
+//    scheduling groups); 128x128 tiles run 4 waves with 2 workgroups per CU,
+//    and 256x320 and 256x192 tiles 8 waves of 64x160 and 64x96, for grids
+//    that 256x256 tiles would leave with a partly empty last round.
+//  * SwiGLU: the W tile holds BN/2 gate rows then the matching BN/2 up rows.
+//    With an even number of W fragments per wave, each wave reads gate and up
+//    fragments of the same outputs and applies the activation in registers.
 //  * Workgroup ids are remapped so that consecutive tile ids share an XCD
 //    (one L2 per XCD), walking groups of 4 M-tiles (measured: 4 and 8 within
 //    1%, 2 and 16 slower).
@@ -54,6 +59,17 @@ struct DmaTile {
 
 __device__ __forceinline__ int dswz(int row, int kc) { return kc ^ ((row >> 1) & 7); }
 
+// Scheduling groups: N times (one instruction of class MASK, then one MFMA).
+constexpr int kSgMfma = 0x008, kSgVmem = 0x010, kSgDsRead = 0x100;
+template <int MASK, int N>
+__device__ __forceinline__ void sg_pairs() {
+#pragma unroll
+  for (int g = 0; g < N; ++g) {
+    __builtin_amdgcn_sched_group_barrier(MASK, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+  }
+}
+
 // EPI: 0 = plain product; 1 = SwiGLU on a paired tile (W rows [0, I) gate,
 // [I, 2I) up; the tile's first BN/2 W rows are gate rows n0.., the rest the
 // matching up rows; output [M, I]); 2 = GELU on each output.  The fused
@@ -66,6 +82,10 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
   // SwiGLU: N is the intermediate size I, each tile covers BN/2 outputs.
   constexpr int OUT_BN = EPI == 1 ? C::BN / 2 : C::BN;
+  // SwiGLU with an even number of W fragments per wave pairs gate and up rows
+  // inside each wave; otherwise up-row waves hand their sums to gate-row waves
+  // through LDS.
+  constexpr bool kPairInWave = EPI == 1 && C::FA % 2 == 0;
 
   const int tiles_m = (M + C::BM - 1) / C::BM;
   const int tiles_n = (N + OUT_BN - 1) / OUT_BN;
@@ -149,7 +169,11 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
     const int kc = 2 * kk + fh;
 #pragma unroll
     for (int i = 0; i < C::FA; ++i) {
-      const int row = wn * C::TN + i * 32 + frow;
+      // In-wave SwiGLU pairing: fragments i < FA/2 are gate rows and i + FA/2
+      // the up rows of the same outputs, so the epilogue pairs them in registers.
+      const int row = !kPairInWave ? wn * C::TN + i * 32 + frow
+                      : i < C::FA / 2 ? wn * (C::TN / 2) + i * 32 + frow
+                                      : C::BN / 2 + wn * (C::TN / 2) + (i - C::FA / 2) * 32 + frow;
       fa[buf][i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
           base + C::BM * C::BK + row * C::BK + dswz(row, kc) * 8));
     }
@@ -175,6 +199,45 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   __syncthreads();
   read_frags(0, 0, 0);
   pin();
+  if constexpr (C::NW == 4 && C::BM == 256) {
+    // One wave per SIMD: nothing else hides this wave's load issue or LDS
+    // latency, so each tile load and fragment read is paired with one MFMA
+    // (scheduling groups).  Loads past K use out-of-range offsets (zeros) so
+    // that every step has the same instruction mix.
+    for (int t = 0; t < nk; ++t) {
+      const int st = t & 1;
+      const int k1 = (t + 1) * C::BK;
+      // sub-step 0: X loads of the next step, fragments of sub-step 1
+      load_x(k1, st ^ 1);
+      read_frags(st, 1, 1);
+      mfmas(0, 0, C::FA);
+      sg_pairs<kSgVmem, C::XL>();
+      sg_pairs<kSgDsRead, C::FA + C::FB>();
+      pin();
+      // sub-step 1: W loads of the next step, fragments of sub-step 2
+      load_w(k1, st ^ 1);
+      read_frags(st, 2, 0);
+      mfmas(1, 0, C::FA);
+      sg_pairs<kSgVmem, C::WL>();
+      sg_pairs<kSgDsRead, C::FA + C::FB>();
+      pin();
+      // sub-step 2
+      read_frags(st, 3, 1);
+      mfmas(0, 0, C::FA);
+      sg_pairs<kSgDsRead, C::FA + C::FB>();
+      pin();
+      // sub-step 3, split around the barrier that publishes the next stage
+      mfmas(1, 0, C::FA / 2);
+      pin();
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_s_barrier();
+      pin();
+      read_frags(st ^ 1, 0, 0);   // unused after the last step
+      mfmas(1, C::FA / 2, C::FA);
+      sg_pairs<kSgDsRead, C::FA + C::FB>();
+      pin();
+    }
+  } else
   for (int t = 0; t < nk; ++t) {
     const int st = t & 1;
     const bool more = t + 1 < nk;
@@ -205,7 +268,38 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
 
   // Epilogue.  acc[i][j] lane holds token m = wm*TM + 32j + (lane&31) and
   // features n = wn*TN + 32i + 8*(r/4) + 4*(lane/32) + r%4, r = 0..15.
-  if constexpr (EPI == 1) {
+  if constexpr (kPairInWave) {
+    // acc[i] holds gate sums and acc[i + FA/2] the up sums of the same outputs
+    // n = n0 + wn*TN/2 + 32i + 8*(r/4) + 4*(lane/32) + r%4.
+#pragma unroll
+    for (int i = 0; i < C::FA / 2; ++i) {
+#pragma unroll
+      for (int j = 0; j < C::FB; ++j) {
+        const int m = m0 + wm * C::TM + j * 32 + frow;
+        if (m >= M) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * (C::TN / 2) + i * 32 + 8 * q + 4 * fh;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float g = bf2f((uint16_t)f2bf_bits(acc[i][j][4 * q + e]));
+            const float u = bf2f((uint16_t)f2bf_bits(acc[i + C::FA / 2][j][4 * q + e]));
+            v[e] = act_fn<TP_ACT_SWIGLU>(g, u);
+          }
+          if (VEC_OUT && n + 3 < N) {
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(Y) + (int64_t)m * N + n) =
+                u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n + e] = (uint16_t)f2bf_bits(v[e]);
+          }
+        }
+      }
+    }
+    return;
+  } else if constexpr (EPI == 1) {
     // Up-row waves (wn >= WN/2) park their accumulators in LDS; the gate-row
     // wave with the same lane layout (wn - WN/2) combines them.
     constexpr int PER_WAVE = C::FA * C::FB * 16 * 64;   // floats
@@ -296,6 +390,9 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
 
 using Dma256 = DmaTile<256, 256, 2, 4>;   // 8 waves, one workgroup per CU
 using Dma128 = DmaTile<128, 128, 2, 2>;   // 4 waves, two workgroups per CU
+// 256x256 with 4 waves of 128x128 (one per SIMD, 256 accumulators each): a
+// third less LDS fragment traffic per MFMA than 8 waves of 128x64.
+using Dma256w4 = DmaTile<256, 256, 2, 2>;
 // 256x320: 8 waves of 64x160 (144 KB of LDS for two stages).  For N where
 // 256x256 tiles leave a mostly empty last round, e.g. the fused QKV at
 // N = 5120: 16 x 16 tiles fill 256 CUs exactly once.
@@ -351,6 +448,9 @@ int gemm_dma_pick_tile(int M, int N, bool wide) {
 tp_status gemm_bf16_dma(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                         bool out_f32, bool vec_out, hipStream_t s, int force_tile) {
   const int pick = force_tile >= 0 ? force_tile : gemm_dma_pick_tile((int)M, (int)N, true);
+  // fp32 partials (the row-parallel products) run 2-3% faster on 4 waves of
+  // 128x128 than on 8 waves of 128x64; bf16 outputs run alike on both.
+  if (pick == 0 && out_f32) return launch_dma<Dma256w4, 0>(x, w, y, (int)M, (int)N, (int)K, true, vec_out, s);
   if (pick == 0) return launch_dma<Dma256, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
   if (pick == 2) return launch_dma<Dma320, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
   if (pick == 3) return launch_dma<Dma192, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
