@@ -129,7 +129,8 @@ include the set-up and warm-up launches.
 Mapping (prefill calls = 2 set-up passes over both ranks + 2 warm-up + 5 timed steps = 9 per rank-0 call):
 - `gemm_bf16_dma_kernel<DmaTile<256,256,2,4>, false, true, 1>`: gate|up with the SwiGLU epilogue, M=4096 K=8192
   2I=28672 -> [4096, 14336].
-- `gemm_bf16_dma_kernel<DmaTile<256,256,2,4>, true, true, 0>`: o_proj (K=4096) and down (K=14336), fp32 partials.
+- `gemm_bf16_dma_kernel<DmaTile<256,256,2,2>, true, true, 0>`: o_proj (K=4096) and down (K=14336), fp32 partials,
+  on 4 waves of 128x128.
 - `gemm_bf16_dma_kernel<DmaTile<256,320,4,2>, false, true, 0>`: fused QKV, N=5120 (16 x 16 tiles).
 - `attn_prefill_tr_kernel`: causal 4096-token attention over 32 local q heads / 4 KV heads.
 - `reduce_rmsnorm_reg_kernel<4>`: sum of the two ranks' attention partials + residual, then the MLP's RMSNorm.
