@@ -105,6 +105,22 @@ def test_linear_bf16_normal(M, K, N):
     assert_within(p, ref, gemm_bound(x.ref, w.ref, ref, False), "row partial fp32")
 
 
+# Row-parallel partials (fp32 out) on each prefill tile shape: 4-wave 256x256,
+# 256x192, 256x320, 128x128; ragged M, N and K tails.
+ROW_SHAPES = [(4000, 1000, 4000), (2048, 1032, 6144), (4000, 136, 5100), (1000, 520, 1000), (65, 64, 16)]
+
+
+@pytest.mark.parametrize("M,K,N", ROW_SHAPES)
+def test_row_partial_bf16_normal(M, K, N):
+    log(f"row partial bf16 normal M={M} K={K} N={N}")
+    x = I.normal(12, "x", (M, K), 1.0)
+    w = I.normal(12, "w", (N, K), 0.02)
+    ref = O.linear(x.ref, w.ref)
+    p = tpl.row_linear_partial(dev(x), dev(w))
+    assert p.dtype == torch.float32
+    assert_within(p, ref, gemm_bound(x.ref, w.ref, ref, False), "row partial fp32")
+
+
 def test_linear_deterministic():
     x = dev(I.normal(12, "x", (64, 8192)))
     w = dev(I.normal(12, "w", (1000, 8192), 0.02))
