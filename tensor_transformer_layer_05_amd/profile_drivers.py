@@ -9,6 +9,11 @@ prefill gate|up projection with SwiGLU in its epilogue (M=4096, K=8192,
 2I=28672, output [4096, 14336], bf16), then one launch of the plain gate|up
 GEMM on the same operands (output [4096, 28672]).  Run it under
 ``rocprofv3 --pmc FETCH_SIZE`` and, separately, ``--pmc WRITE_SIZE``.
+
+``decode_attn_span``: decode attention of the TP=4 shard shape (32 sequences,
+8 q / 2 KV heads of 128) over key spans of 512 .. 16384, 20 calls each on
+rotating cache copies, for ``rocprofv3 --kernel-trace``: the kernel durations
+per span separate the fixed cost of a launch from the streaming rate.
 """
 from __future__ import annotations
 
@@ -16,7 +21,7 @@ import sys
 
 import torch
 
-from . import column_linear, column_linear_act, lib
+from . import column_linear, column_linear_act, lib, local_attention, local_attention_workspace
 
 
 def gemm_traffic() -> None:
@@ -39,7 +44,33 @@ def gemm_traffic() -> None:
     print("gemm_traffic done", flush=True)
 
 
-DRIVERS = {"gemm_traffic": gemm_traffic}
+SPANS = (512, 1024, 2048, 4096, 8192, 16384)
+
+
+def decode_attn_span() -> None:
+    lib()
+    B, Hq, Hkv, D = 32, 8, 2, 128
+    for L in SPANS:
+        copies = 4 if L <= 4096 else 2
+        sets = []
+        for _ in range(copies):
+            q = torch.randn(B, 1, Hq, D, device="cuda").to(torch.bfloat16)
+            k = torch.randn(B, L, Hkv, D, device="cuda").to(torch.bfloat16)
+            v = torch.randn(B, L, Hkv, D, device="cuda").to(torch.bfloat16)
+            o = torch.empty(B, 1, Hq, D, device="cuda", dtype=torch.bfloat16)
+            ws = torch.empty(max(1, local_attention_workspace(B, 1, L, Hq, Hkv, D)), dtype=torch.uint8,
+                             device="cuda")
+            sets.append((q, k, v, o, ws))
+        torch.cuda.synchronize()
+        for i in range(20):
+            q, k, v, o, ws = sets[i % copies]
+            local_attention(q, k, v, causal=True, out=o, workspace=ws)
+        torch.cuda.synchronize()
+        print(f"decode_attn_span L={L} done", flush=True)
+        del sets
+
+
+DRIVERS = {"gemm_traffic": gemm_traffic, "decode_attn_span": decode_attn_span}
 
 if __name__ == "__main__":
     DRIVERS[sys.argv[1] if len(sys.argv) > 1 else "gemm_traffic"]()
