@@ -57,11 +57,11 @@ def traffic_source_hash(files):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(name="gate_up_gemm_traffic.md"):
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 FETCH_SIZE/WRITE_SIZE summary (scaled by a plain copy of known
-    size), or None once the kernel's sources no longer match the hash recorded
-    with the counters."""
+def recorded_profile(name):
+    """The DATA line of a committed rocprofv3 summary of the dominant kernel
+    (HBM traffic from FETCH_SIZE/WRITE_SIZE scaled by a plain copy of known
+    size; MFMA and LDS counters), or None once the kernel's sources no longer
+    match the hash recorded with the counters."""
     path = os.path.join(ROOT, "profiles", name)
     try:
         line = [l for l in open(path) if l.startswith("DATA ")][0]
@@ -504,7 +504,8 @@ def main(argv=None):
     DK = "gate_up_swiglu"
     m, k, n = gemm[DK]
     dom_ms = per[DK]
-    tr = recorded_traffic()
+    tr = recorded_profile("gate_up_gemm_traffic.md")
+    cn = recorded_profile("gate_up_gemm_counters.md")
     dom = {"bound": "mfma",
            "kernel": "column_linear_act gate|up + SwiGLU (gemm_bf16_dma_kernel, 256x256 tiles, "
                      "SwiGLU epilogue)",
@@ -513,6 +514,8 @@ def main(argv=None):
            "traffic": tr["traffic_bytes"] if tr else None,
            "traffic_unit": "HBM bytes per launch (profiles/gate_up_gemm_traffic.md)",
            "algorithmic_bytes": byts[DK],
+           "counters": ({k: cn[k] for k in ("mfma_util", "sclk_ghz", "lds_idx_active")}
+                        | {"source": "profiles/gate_up_gemm_counters.md"}) if cn else None,
            "flop_per_launch": flops[DK], "avg_launch_ms": dom_ms,
            "shape_mkn": [m, k, n]}
     kernels = {}
