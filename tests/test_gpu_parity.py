@@ -241,6 +241,21 @@ def test_attention_prefill(B, Sq, Skv, Hq, Hkv, causal):
     assert_normwise(o, ref, 1e-2, "prefill attention")
 
 
+@pytest.mark.parametrize("scale", [0.2, -0.05, 0.0])
+def test_attention_prefill_explicit_scale(scale):
+    """Scales other than 1/sqrt(D): positive (the scale folded into the
+    exponent), negative and zero (scores scaled before the row maximum; zero
+    gives the mean of V over the visible keys)."""
+    log(f"attention prefill scale={scale}")
+    B, S, Hq, Hkv, D = 1, 300, 4, 2, 128
+    q = I.normal(19, "q", (B, S, Hq, D))
+    k = I.normal(19, "k", (B, S, Hkv, D))
+    v = I.normal(19, "v", (B, S, Hkv, D))
+    ref = O.attention(q.ref, k.ref, v.ref, causal=True, scale=scale)
+    o = tpl.local_attention(dev(q), dev(k), dev(v), causal=True, scale=scale)
+    assert_within(o, ref, _attn_bound(ref, v.ref), f"prefill attention, scale {scale}")
+
+
 def test_attention_strided_qkv_views():
     """q/k/v as column slices of one fused [S, (Hq+2Hkv)D] projection output
     and the output written into a [S, Hq*D] buffer, as in the layer."""
