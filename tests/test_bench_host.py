@@ -1,0 +1,56 @@
+"""Host-side logic of bench.py (no GPU): the committed rocprofv3 summaries are
+used only while the measured kernel's sources still hash to the recorded
+value, and --gpus N > 1 is refused."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+PROFILES = ["gate_up_gemm_traffic.md", "gate_up_gemm_counters.md"]
+
+
+@pytest.mark.parametrize("name", PROFILES)
+def test_recorded_profile_matches_sources(name):
+    d = bench.recorded_profile(name)
+    assert d is not None, f"profiles/{name} no longer matches the GEMM sources; re-profile"
+    assert d["sources_sha256_16"] == bench.traffic_source_hash(d["sources"])
+
+
+def test_recorded_profile_rejects_changed_sources(monkeypatch):
+    monkeypatch.setattr(bench, "traffic_source_hash", lambda files: "0" * 16)
+    for name in PROFILES:
+        assert bench.recorded_profile(name) is None
+
+
+def test_recorded_profile_missing_file():
+    assert bench.recorded_profile("no_such_summary.md") is None
+
+
+def test_traffic_figures_are_consistent():
+    d = bench.recorded_profile("gate_up_gemm_traffic.md")
+    # scaled counters -> bytes, and the algorithmic bytes of the fused launch
+    # (the scales: 256 MiB of the calibration copy over what the counters read for it)
+    fetched = d["fetch_kib"] * (262144.0 / d["copy_fetch_kib"]) * 1024
+    written = d["write_kib"] * (262144.0 / d["copy_write_kib"]) * 1024
+    assert abs(fetched + written - d["traffic_bytes"]) <= 1e-6 * d["traffic_bytes"]
+    M, K, N2 = d["shape_mkn"]
+    assert d["algorithmic_bytes"] == (M * K + N2 * K + M * N2 // 2) * 2
+
+
+def test_counted_mfma_work_equals_algorithmic():
+    d = bench.recorded_profile("gate_up_gemm_counters.md")
+    assert d["mfma_flop_counted"] == 2 * 4096 * 8192 * 28672
+    assert 0.0 < d["mfma_util"] <= 1.0
+
+
+def test_multi_gpu_request_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
