@@ -1,4 +1,4 @@
-// Decode bf16 linear for 1..3 tokens: weight streaming.
+// Decode bf16 linear for 1..3 tokens, and up to 16 on long-K weights: weight streaming.
 //
 //   Y[m, n] = sum_k X[m, k] * W[n, k]
 //
@@ -202,11 +202,25 @@ static int stream_kw(int64_t K, int waves) {
   return (kw + 31) & ~31;
 }
 
+// The LDS-ring kernel (gemm_stream_dma.hip) serves 4..64 tokens, except that
+// up to 16 tokens stay on this kernel for weights of at most 8192 rows on
+// which each of its waves streams at least eight 128-k chunks (K / waves >=
+// 1024).  That is the decode gate|up weight (7168 x 8192): with SwiGLU fused,
+// this kernel's eight waves per workgroup ran 26.1 / 26.3 / 28.4 us at 4 / 8 /
+// 16 tokens against the ring's 32.6 / 32.8 / 34.1 us.  On taller weights the
+// ring wins (lm_head 16032 x 8192 at 8 and 16 tokens: 58.6 and 59.5 us
+// against 61.0 and 75.0), and on shorter K too (8192 x 3584: 13.7 against
+// 15.4 us at 8 tokens).  The choice depends only on (M, N, K) of the weight,
+// so the fused-activation call takes the same kernel and K split as the plain
+// call on the same weight, and the two give the same bits.
+static bool stream_regs(int64_t M, int64_t N, int64_t K) {
+  if (M <= 3) return true;
+  return M <= 16 && N <= 8192 && K / stream_waves(N, K) >= 1024;
+}
+
 tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                            bool out_f32, hipStream_t s) {
-  // From 4 tokens on, the kernel that streams weights and tokens through LDS
-  // (whole-line loads for both operands) is faster.
-  if (M >= 4) return gemm_bf16_stream_dma(x, w, y, M, N, K, out_f32, s);
+  if (!stream_regs(M, N, K)) return gemm_bf16_stream_dma(x, w, y, M, N, K, out_f32, s);
   const int waves = stream_waves(N, K);
   const int kw = stream_kw(K, waves);
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
@@ -227,8 +241,9 @@ tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_
 // plain linear followed by the activation bit for bit.
 tp_status gemm_bf16_stream_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
                                int64_t K, int act, hipStream_t s) {
-  if (M >= 4) return gemm_bf16_stream_dma_act(x, w, h, M, I, K, act, s);
-  const int waves = stream_waves(act == TP_ACT_SWIGLU ? 2 * I : I, K);
+  const int64_t rows = act == TP_ACT_SWIGLU ? 2 * I : I;
+  if (!stream_regs(M, rows, K)) return gemm_bf16_stream_dma_act(x, w, h, M, I, K, act, s);
+  const int waves = stream_waves(rows, K);
   const int kw = stream_kw(K, waves);
   const int Mi = (int)M, Ii = (int)I, Ki = (int)K;
 #define TPL_SACT(WV)                                                                         \

@@ -135,7 +135,7 @@ Mapping (prefill calls = 2 set-up passes over both ranks + 2 warm-up + 5 timed s
 - `attn_prefill_tr_kernel`: causal 4096-token attention over 32 local q heads / 4 KV heads.
 - `reduce_rmsnorm_reg_kernel<4>`: sum of the two ranks' attention partials + residual, then the MLP's RMSNorm.
 - `reduce_kernel`, `rmsnorm_reg_kernel<4>`: the final sum of MLP partials; the first RMSNorm.
-- `gemm_stream_kernel<*, 1, *, *, *>`: decode linears with 1..3 tokens; `gemm_stream_dma_kernel<...>`: 4..64 tokens
+- `gemm_stream_kernel<*, 1, *, *, *>`: decode linears with 1..3 tokens, and 4..16 tokens on the decode gate|up weight; `gemm_stream_dma_kernel<...>`: the other decode linears up to 64 tokens
   (weights and tokens through the per-wave LDS ring).
 - `attn_decode_kernel<false|true>` + `attn_decode_combine_kernel`: decode attention (contiguous / paged cache).
 - `vocab_argmax_kernel`: the lm_head shard's local greedy step.

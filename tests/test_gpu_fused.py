@@ -37,6 +37,8 @@ ACT_SHAPES = [
     (1, 8192, 1000),     # one token tile, 16 waves
     (1, 8192, 3584),     # decode gate|up shard (7168 rows), 8 waves
     (5, 520, 130),       # ragged K range per wave, ragged rows
+    (8, 8192, 3584),     # decode gate|up shard at 8 tokens: register kernel, 8 waves
+    (13, 16384, 200),    # register kernel, 16 waves, ragged tokens
     (17, 4096, 1000),    # two token tiles, 16 waves
     (32, 4096, 3584),    # two token tiles, two row tiles per wave
     (33, 1024, 300),     # LDS-ring kernel, three token tiles

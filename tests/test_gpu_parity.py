@@ -55,6 +55,8 @@ def test_worked_example(dtype):
 INT_SHAPES = [
     # decode weight-streaming path (M <= 64, K % 8 == 0)
     (1, 8, 16), (3, 64, 40), (17, 136, 130), (33, 1000, 70), (64, 520, 300), (64, 4096, 48),
+    # 4..16 tokens on long K stay on the register-streaming kernel (16 and 8 waves)
+    (4, 16384, 40), (16, 8192, 6200),
     # MFMA tile path: ragged M/N/K, each tile shape
     (65, 64, 16), (200, 136, 130), (300, 520, 300), (512, 264, 640), (4000, 264, 4000),
     (4096, 200, 2048), (4000, 136, 5100),   # the last picks 256x320 tiles
