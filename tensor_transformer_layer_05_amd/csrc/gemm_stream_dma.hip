@@ -63,6 +63,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
   const int n0 = blockIdx.x * OUT_ROWS;
   const int g = lane >> 4;         // k-group of this lane inside a 32-k step
   const int i16 = lane & 15;       // weight row / token inside a 16-tile
+  // blockIdx.y selects this workgroup's MT token tiles; the rest of the kernel
+  // sees them as tokens 0 .. M-1 of X and Y.
+  const int m0 = blockIdx.y * XROWS;
+  X += (int64_t)m0 * K;
+  Y = OUT_F32 ? (void*)((float*)Y + (int64_t)m0 * N) : (void*)((uint16_t*)Y + (int64_t)m0 * N);
+  M = min(M - m0, XROWS);
 
   // one resource per weight row tile, based at its first row and bounded to its valid rows
   __amdgpu_buffer_rsrc_t wr[RT];
@@ -202,11 +208,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
   }
 }
 
+static int stream_dma_kw(int64_t K, int waves) {
+  int kw = (int)((K + waves - 1) / waves);
+  return (kw + 127) & ~127;
+}
+
+// One workgroup per (OUT_ROWS output features, MT token tiles); the WAVES
+// waves split K into 128-aligned ranges of stream_dma_kw(K, WAVES).
 template <int WAVES, int MT, int RT, int S, int EPI = 0>
-static void launch_stream_dma(const void* x, const void* w, void* y, int M, int N, int K, int kw,
+static void launch_stream_dma(const void* x, const void* w, void* y, int M, int N, int K,
                               bool out_f32, hipStream_t s) {
   constexpr int OUT_ROWS = EPI == 1 ? 16 : 16 * RT;
-  dim3 grid((N + OUT_ROWS - 1) / OUT_ROWS), block(WAVES * 64);
+  const int kw = stream_dma_kw(K, WAVES);
+  dim3 grid((N + OUT_ROWS - 1) / OUT_ROWS, (M + 16 * MT - 1) / (16 * MT)), block(WAVES * 64);
   auto X = static_cast<const uint16_t*>(x);
   auto Wp = static_cast<const uint16_t*>(w);
   if constexpr (EPI == 0) {
@@ -221,26 +235,33 @@ static void launch_stream_dma(const void* x, const void* w, void* y, int M, int 
 
 // Waves per workgroup by token tiles (the K split; the fused-activation
 // variant must use the same): 2 for 4..16 tokens, 3 for 17..32, 2 for 33..64.
+// The sums depend only on the waves and their k ranges, not on how rows and
+// tokens are tiled over workgroups.
 // LDS per workgroup = WAVES x S x (16 RT + 16 MT) x 256 bytes <= 144 KB.
-static int stream_dma_waves(int mt) { return mt == 2 ? 3 : 2; }
 
-static int stream_dma_kw(int64_t K, int waves) {
-  int kw = (int)((K + waves - 1) / waves);
-  return (kw + 127) & ~127;
-}
+constexpr int64_t kStreamCUs = 256;   // compute units of an MI355X
 
 // Requires 4 <= M <= 64, K % 8 == 0, 16-byte aligned X and W, and M*K and
 // 32*K elements addressable with 32-bit byte offsets.
 tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M, int64_t N,
                                int64_t K, bool out_f32, hipStream_t s) {
   const int mt = (int)((M + 15) / 16);
-  const int WV = stream_dma_waves(mt);
-  const int kw = stream_dma_kw(K, WV);
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
-  if (mt == 1) launch_stream_dma<2, 1, 2, 4>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
-  else if (mt == 2) launch_stream_dma<3, 2, 1, 4>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
-  else if (mt == 3) launch_stream_dma<2, 3, 2, 3>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
-  else launch_stream_dma<2, 4, 2, 3>(x, w, y, Mi, Ni, Ki, kw, out_f32, s);
+  // 17..32 tokens (three waves and one K split whatever the tiling): the
+  // tiling whose grid comes closest to filling the 256 CUs once without a
+  // second round.  Short weights take one token tile per workgroup (twice the
+  // grid, half the token rows re-read per workgroup), tall ones two row tiles
+  // per workgroup (half the grid).  Kernel durations at 32 tokens:
+  // [1536, 4096] 10.0 -> 8.1 us and [2048, 4096] 8.8 -> 7.9 us split;
+  // [4096, 1024] 5.7 us as is (7.7 split); [7168, 8192] 35.3 -> 26.9 us and
+  // [8192, 3584] 16.0 -> 12.7 us with two row tiles.
+  const int64_t tiles16 = (N + 15) / 16;
+  if (mt == 1) launch_stream_dma<2, 1, 2, 4>(x, w, y, Mi, Ni, Ki, out_f32, s);
+  else if (mt == 2 && 2 * tiles16 <= kStreamCUs) launch_stream_dma<3, 1, 1, 4>(x, w, y, Mi, Ni, Ki, out_f32, s);
+  else if (mt == 2 && tiles16 > kStreamCUs) launch_stream_dma<3, 2, 2, 3>(x, w, y, Mi, Ni, Ki, out_f32, s);
+  else if (mt == 2) launch_stream_dma<3, 2, 1, 4>(x, w, y, Mi, Ni, Ki, out_f32, s);
+  else if (mt == 3) launch_stream_dma<2, 3, 2, 3>(x, w, y, Mi, Ni, Ki, out_f32, s);
+  else launch_stream_dma<2, 4, 2, 3>(x, w, y, Mi, Ni, Ki, out_f32, s);
   TPL_LAUNCH_CHECK("gemm_bf16_stream_dma");
   return TP_OK;
 }
@@ -251,19 +272,17 @@ tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M,
 tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
                                    int64_t K, int act, hipStream_t s) {
   const int mt = (int)((M + 15) / 16);
-  const int WV = stream_dma_waves(mt);
-  const int kw = stream_dma_kw(K, WV);
   const int Mi = (int)M, Ii = (int)I, Ki = (int)K;
   if (act == TP_ACT_SWIGLU) {
-    if (mt == 1) launch_stream_dma<2, 1, 2, 4, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
-    else if (mt == 2) launch_stream_dma<3, 2, 2, 3, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
-    else if (mt == 3) launch_stream_dma<2, 3, 2, 3, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
-    else launch_stream_dma<2, 4, 2, 3, 1>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    if (mt == 1) launch_stream_dma<2, 1, 2, 4, 1>(x, w, h, Mi, Ii, Ki, false, s);
+    else if (mt == 2) launch_stream_dma<3, 2, 2, 3, 1>(x, w, h, Mi, Ii, Ki, false, s);
+    else if (mt == 3) launch_stream_dma<2, 3, 2, 3, 1>(x, w, h, Mi, Ii, Ki, false, s);
+    else launch_stream_dma<2, 4, 2, 3, 1>(x, w, h, Mi, Ii, Ki, false, s);
   } else {
-    if (mt == 1) launch_stream_dma<2, 1, 1, 4, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
-    else if (mt == 2) launch_stream_dma<3, 2, 1, 4, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
-    else if (mt == 3) launch_stream_dma<2, 3, 2, 3, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
-    else launch_stream_dma<2, 4, 2, 3, 2>(x, w, h, Mi, Ii, Ki, kw, false, s);
+    if (mt == 1) launch_stream_dma<2, 1, 1, 4, 2>(x, w, h, Mi, Ii, Ki, false, s);
+    else if (mt == 2) launch_stream_dma<3, 2, 1, 4, 2>(x, w, h, Mi, Ii, Ki, false, s);
+    else if (mt == 3) launch_stream_dma<2, 3, 2, 3, 2>(x, w, h, Mi, Ii, Ki, false, s);
+    else launch_stream_dma<2, 4, 2, 3, 2>(x, w, h, Mi, Ii, Ki, false, s);
   }
   TPL_LAUNCH_CHECK("gemm_bf16_stream_dma_act");
   return TP_OK;

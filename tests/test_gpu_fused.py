@@ -39,7 +39,7 @@ ACT_SHAPES = [
     (5, 520, 130),       # ragged K range per wave, ragged rows
     (8, 8192, 3584),     # decode gate|up shard at 8 tokens: register kernel, 8 waves
     (13, 16384, 200),    # register kernel, 16 waves, ragged tokens
-    (17, 4096, 1000),    # two token tiles, 16 waves
+    (17, 4096, 1000),    # two token tiles; the plain call (2000 rows) splits them over workgroups
     (32, 4096, 3584),    # two token tiles, two row tiles per wave
     (33, 1024, 300),     # LDS-ring kernel, three token tiles
     (64, 3584, 264),     # LDS-ring kernel, four token tiles

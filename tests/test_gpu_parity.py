@@ -57,6 +57,8 @@ INT_SHAPES = [
     (1, 8, 16), (3, 64, 40), (17, 136, 130), (33, 1000, 70), (64, 520, 300), (64, 4096, 48),
     # 4..16 tokens on long K stay on the register-streaming kernel (16 and 8 waves)
     (4, 16384, 40), (16, 8192, 6200),
+    # 17..32 tokens: one token tile per workgroup up to 2048 rows, two row tiles past 4096
+    (29, 264, 4200), (20, 520, 2040),
     # MFMA tile path: ragged M/N/K, each tile shape
     (65, 64, 16), (200, 136, 130), (300, 520, 300), (512, 264, 640), (4000, 264, 4000),
     (4096, 200, 2048), (4000, 136, 5100),   # the last picks 256x320 tiles
