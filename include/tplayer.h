@@ -170,6 +170,33 @@ tp_status tp_kv_append(const void* k_new, const void* v_new, int64_t new_stride,
                        tp_dtype dt, void* stream);
 
 /*
+ * One decode step's cache append and local attention in one launch (the same
+ * P1 section: each rank appends its own heads' k/v and attends over its own
+ * heads; P3 GQA section for the q -> KV head map): equal, bit for bit, to
+ *     tp_kv_append(k_new, v_new, new_stride, k_cache, v_cache, cs, B, Hkv, D, T, pos)
+ *     tp_local_attention(q, k_cache, v_cache, Sq = 1, Skv = pos + 1)
+ * on the same stream.
+ *   q : element (b,h,d) at q[b*qs[0] + h*qs[1] + d]                bf16
+ *   k_new, v_new : element (b,j,d) at k_new[b*new_stride + j*D + d] bf16
+ *   k_cache, v_cache : element (b,t,j,d) at k_cache[b*cs[0] + t*cs[1] + j*cs[2] + d]
+ *   o : element (b,h,d) at o[b*os[0] + h*os[1] + d]                bf16
+ *   0 <= pos < T, new_stride >= Hkv*D (TP_ERR_SHAPE otherwise).  dt must be
+ *   TP_BF16, D = 128, G = Hq/Hkv <= 32, (pos*cs[1] + D)*2 < 2^31
+ *   (TP_ERR_UNSUPPORTED otherwise).  Strides and new_stride multiples of 8
+ *   elements (os: of 4), q, k_new, v_new and the caches 16-byte aligned, o
+ *   8-byte aligned (TP_ERR_ALIGN otherwise).
+ *   workspace: as for tp_local_attention, of at least
+ *   tp_local_attention_workspace(B, 1, pos + 1, Hq, Hkv, D) bytes.
+ */
+tp_status tp_decode_attention_append(const void* q, const int64_t qs[2],
+                                     const void* k_new, const void* v_new, int64_t new_stride,
+                                     void* k_cache, void* v_cache, const int64_t cs[3],
+                                     int64_t T, int64_t pos, void* o, const int64_t os[2],
+                                     int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                     float scale, tp_dtype dt,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The arithmetic of the all-reduce after a row-parallel linear (P1 "Row
  * Parallel Linear": the partial outputs are summed; P2 section 二
  * all_reduce(output); P3: partials must be summed, not concatenated),
@@ -256,6 +283,27 @@ tp_status tp_paged_kv_append(const void* k_new, const void* v_new, int64_t new_s
                              const int32_t* block_table, int64_t table_stride,
                              const int32_t* context_lens, int64_t B, int64_t Hkv, int64_t D,
                              int64_t block_size, tp_dtype dt, void* stream);
+
+/*
+ * The paged cache's append and decode attention in one launch (the same P1
+ * section): equal, bit for bit, to tp_paged_kv_append(...) followed by
+ * tp_paged_attention_decode(...) with the same arguments, provided no slot
+ * written by the append is read by another sequence of the call or through a
+ * second table entry (no block shared with a sequence that reads that slot,
+ * no block listed twice up to a sequence's length).
+ *   k_new, v_new : element (b,j,d) at k_new[b*new_stride + j*D + d]   bf16,
+ *   16-byte aligned, new_stride >= Hkv*D and a multiple of 8.
+ *   Every other argument, limit and error as tp_paged_attention_decode.
+ */
+tp_status tp_paged_decode_attention_append(const void* q, const int64_t qs[2], const void* k_new,
+                                           const void* v_new, int64_t new_stride, void* k_pool,
+                                           void* v_pool, const int64_t ps[3], int64_t num_blocks,
+                                           const int32_t* block_table, int64_t table_stride,
+                                           const int32_t* context_lens, int64_t max_context_len,
+                                           int64_t block_size, void* o, const int64_t os[2],
+                                           int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                           float scale, tp_dtype dt, void* workspace,
+                                           size_t workspace_bytes, void* stream);
 
 /*
  * Greedy token choice of a vocab-parallel lm_head (P1 "lm_head 怎么处理": the

@@ -11,7 +11,8 @@ Entry points (same names as the C ABI, without the ``tp_`` prefix):
 ``column_linear``, ``column_linear_act``, ``row_linear_partial``,
 ``swiglu_local``, ``local_attention``, ``kv_append``, ``reduce_partials``,
 ``reduce_partials_rmsnorm``, ``rmsnorm``, ``paged_attention_decode``,
-``paged_kv_append``, ``vocab_argmax_local``, ``vocab_argmax_reduce``.
+``paged_kv_append``, ``decode_attention_append``, ``paged_decode_attention_append``,
+``vocab_argmax_local``, ``vocab_argmax_reduce``.
 Weights use the nn.Linear layout ``[out_features, in_features]``.
 """
 from __future__ import annotations
@@ -27,6 +28,7 @@ __all__ = [
     "local_attention", "local_attention_workspace", "kv_append", "reduce_partials",
     "reduce_partials_rmsnorm", "rmsnorm", "vocab_argmax_local", "vocab_argmax_reduce",
     "paged_attention_decode", "paged_attention_workspace", "paged_kv_append",
+    "decode_attention_append", "paged_decode_attention_append",
     "shard_column", "shard_row", "shard_qkv", "kv_heads_of_rank", "kv_cache_bytes_per_rank",
     "F32", "BF16", "ACT_NONE", "ACT_SWIGLU", "ACT_GELU",
 ]
@@ -69,6 +71,14 @@ _SIGS = {
     "tp_paged_attention_workspace": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
     "tp_paged_kv_append": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64p, _i64, _vp, _i64, _vp,
                                           _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
+    "tp_decode_attention_append": (ctypes.c_int, [_vp, _i64p, _vp, _vp, _i64, _vp, _vp, _i64p, _i64,
+                                                  _i64, _vp, _i64p, _i64, _i64, _i64, _i64,
+                                                  ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t,
+                                                  _vp]),
+    "tp_paged_decode_attention_append": (ctypes.c_int, [_vp, _i64p, _vp, _vp, _i64, _vp, _vp, _i64p,
+                                                        _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64p,
+                                                        _i64, _i64, _i64, _i64, ctypes.c_float,
+                                                        ctypes.c_int, _vp, ctypes.c_size_t, _vp]),
     "tp_vocab_argmax_local": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "tp_vocab_argmax_reduce": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64, _i64,
                                               _vp, _vp, _vp]),
@@ -286,6 +296,55 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
         cs, B, H, D, k_cache.shape[1], pos, _DT[k_new.dtype], _stream(k_new)))
 
 
+def _new_rows(k_new, v_new):
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, n)
+    B, H, D = k_new.shape
+    if k_new.stride(2) != 1 or k_new.stride(1) != D or v_new.stride() != k_new.stride():
+        raise ValueError("k_new/v_new must be [B, Hkv, D] rows of one stride")
+    return B, H, D
+
+
+def decode_attention_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            k_cache: torch.Tensor, v_cache: torch.Tensor, pos: int,
+                            scale: float | None = None, out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None):
+    """One decode step in one launch: store k_new/v_new (``[B, Hkv, D]``
+    views with a shared row stride) at key position ``pos`` of the caches
+    (``[B, T, Hkv, D]``, any strides, last dim contiguous) and attend q
+    (``[B, Hq, D]``) over keys ``0..pos``.  The same bits as ``kv_append``
+    followed by ``local_attention`` with ``Skv = pos + 1``.  Returns o
+    ``[B, Hq, D]``."""
+    _dev(q, "q")
+    if q.dim() != 3 or q.stride(2) != 1:
+        raise ValueError("q must be [B, Hq, D] with a contiguous last dimension")
+    B, H, D = _new_rows(k_new, v_new)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape or k_cache.stride(3) != 1:
+        raise ValueError("caches must share shape and strides with a contiguous last dim")
+    if not (0 <= pos < k_cache.shape[1]):
+        raise ValueError("pos outside the cache")
+    Hq = q.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    if out.dim() != 3 or out.stride(2) != 1:
+        raise ValueError("out must be [B, Hq, D] with a contiguous last dimension")
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    need = local_attention_workspace(B, 1, pos + 1, Hq, H, D)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    qs = (ctypes.c_int64 * 2)(q.stride(0), q.stride(1))
+    os_ = (ctypes.c_int64 * 2)(out.stride(0), out.stride(1))
+    cs = _arr3([k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)])
+    _check("tp_decode_attention_append", lib().tp_decode_attention_append(
+        q.data_ptr(), qs, k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_cache.data_ptr(),
+        v_cache.data_ptr(), cs, k_cache.shape[1], pos, out.data_ptr(), os_, B, Hq, H, D,
+        float(scale), _DT[q.dtype], workspace.data_ptr() if need else None, need, _stream(q)))
+    return out
+
+
 def reduce_partials(partials, residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
                     out_dtype: torch.dtype | None = None):
     """``y = residual + sum_r partials[r]`` in rank order (float32 sums)."""
@@ -429,6 +488,44 @@ def paged_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tens
         k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_pool.data_ptr(), v_pool.data_ptr(), ps,
         k_pool.shape[0], block_table.data_ptr(), block_table.stride(0), context_lens.data_ptr(), B, H,
         D, k_pool.shape[1], _DT[k_new.dtype], _stream(k_new)))
+
+
+def paged_decode_attention_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                  k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                  block_table: torch.Tensor, context_lens: torch.Tensor,
+                                  max_context_len: int, scale: float | None = None,
+                                  out: torch.Tensor | None = None,
+                                  workspace: torch.Tensor | None = None):
+    """``paged_kv_append`` followed by ``paged_attention_decode`` in one
+    launch, with the same bits (no slot the append writes may be read by
+    another sequence or through a second table entry).  Returns o
+    ``[B, Hq, D]``."""
+    _dev(q, "q")
+    if q.dim() != 3 or q.stride(2) != 1:
+        raise ValueError("q must be [B, Hq, D] with a contiguous last dimension")
+    B, H, D = _new_rows(k_new, v_new)
+    ps = _paged_common(block_table, context_lens, k_pool, v_pool)
+    Hq = q.shape[1]
+    nb, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    if block_table.shape[0] != B or q.shape[0] != B or Hkv != H:
+        raise ValueError("q, k_new, block_table and the pools must agree on sequences and KV heads")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    if out.dim() != 3 or out.stride(2) != 1:
+        raise ValueError("out must be [B, Hq, D] with a contiguous last dimension")
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    need = paged_attention_workspace(B, Hq, Hkv, max_context_len, bs)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    qs = (ctypes.c_int64 * 2)(q.stride(0), q.stride(1))
+    os_ = (ctypes.c_int64 * 2)(out.stride(0), out.stride(1))
+    _check("tp_paged_decode_attention_append", lib().tp_paged_decode_attention_append(
+        q.data_ptr(), qs, k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_pool.data_ptr(),
+        v_pool.data_ptr(), ps, nb, block_table.data_ptr(), block_table.stride(0),
+        context_lens.data_ptr(), int(max_context_len), bs, out.data_ptr(), os_, B, Hq, Hkv, D,
+        float(scale), _DT[q.dtype], workspace.data_ptr() if need else None, need, _stream(q)))
+    return out
 
 
 def vocab_argmax_local(logits: torch.Tensor, vocab_offset: int = 0):

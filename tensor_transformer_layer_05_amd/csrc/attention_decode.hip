@@ -32,6 +32,14 @@
 // block (bs is a multiple of 16), so its buffer resource is based at that
 // block and bounded to it.  Sequences have their own lengths; entries outside
 // [0, num_blocks) read as zero instead of faulting.
+//
+// Fused append (kn != nullptr): the decode step's own k and v rows are stored
+// to their cache slot by the first wave of chunk 0 (contiguous: position
+// Skv - 1; paged: context_lens[b] - 1, skipped where the append would skip
+// it), and the wave whose tile holds key L - 1 writes those rows over the
+// cached ones in its landed LDS tile before reading it.  The result equals
+// the append launch followed by the attention launch, bit for bit, without
+// the attention depending on the store.
 #include <algorithm>
 
 #include "common.h"
@@ -55,6 +63,10 @@ struct DecArgs {
   float scale_log2;                             // softmax scale * log2(e)
   // paged only
   const int* table; int64_t tstride; const int* lens; int bs; int64_t nblocks;
+  // fused append only (else kn == nullptr): element (b, j, d) of the new rows at
+  // kn[b*nstride + j*D + d]; kst, vst: the caches (pools) written
+  const uint16_t* kn; const uint16_t* vn; int64_t nstride;
+  uint16_t* kst; uint16_t* vst;
 };
 
 namespace {
@@ -75,9 +87,15 @@ template <bool PAGED>
 __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   constexpr int TE = kDecTile * kDecD;                 // bf16 elements of one K (or V) tile
   constexpr int WRING = 2 * 2 * TE;                    // per wave: 2 stages x (K, V)
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * WRING];   // 128 KB
-  __shared__ float wstat[4][kDecMaxG][2];
-  __shared__ int tbl[PAGED ? kPagedMaxBlocks : 1];
+  // One LDS object: the rings (128 KB), then the waves' softmax statistics
+  // (1 KB) and the paged variant's copy of the chunk's table entries (2 KB).
+  // With a second __shared__ object the compiler can no longer tell the ring
+  // reads from the in-flight direct-to-LDS writes and waits for all of them
+  // before each tile's reads, which defeats the two-stage ring.
+  constexpr int STAT_E = 4 * kDecMaxG * 2 * 2;          // bf16-sized elements of wstat
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * WRING + STAT_E + (PAGED ? 2 * kPagedMaxBlocks : 0)];
+  auto wstat = reinterpret_cast<float (*)[kDecMaxG][2]>(lds + 4 * WRING);
+  int* tbl = reinterpret_cast<int*>(lds + 4 * WRING + STAT_E);
 
   const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -89,6 +107,37 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   const int wkeys = a.chunk / 4;                       // keys per wave (multiple of 32)
   const int tw = split * a.chunk + wave * wkeys;       // first key of this wave
   const int nt = max(0, min(wkeys, L - tw) + kDecTile - 1) / kDecTile;   // tiles with keys
+
+  // Fused append: where this sequence's new rows go (pos_new, slot offset dst)
+  // and whether they stand in for key L - 1 of the attention.  All uniform.
+  bool store_ok = false, subst = false;
+  int64_t dst = 0;
+  if (a.kn != nullptr) {
+    if constexpr (PAGED) {
+      const int pos_new = a.lens[b] - 1;
+      int pb = -1;
+      if (pos_new >= 0 && pos_new / a.bs < a.tstride) pb = a.table[(int64_t)b * a.tstride + pos_new / a.bs];
+      store_ok = pb >= 0 && pb < a.nblocks;
+      dst = (int64_t)pb * a.ks0 + (int64_t)(pos_new % a.bs) * a.ks1 + (int64_t)j * a.ks2;
+      subst = store_ok && pos_new == L - 1;
+    } else {
+      store_ok = subst = true;
+      dst = (int64_t)b * a.ks0 + (int64_t)(L - 1) * a.ks1 + (int64_t)j * a.ks2;
+    }
+  }
+  const bool wave_store = store_ok && split == 0 && wave == 0;
+  const bool wave_subst = subst && L - 1 >= tw && L - 1 < tw + wkeys;
+  uint32_t knew = 0u, vnew = 0u;   // d = 2 lane, 2 lane + 1 of the new rows
+  if (wave_store || wave_subst) {
+    const int64_t src = (int64_t)b * a.nstride + (int64_t)j * kDecD + 2 * lane;
+    knew = *reinterpret_cast<const uint32_t*>(a.kn + src);
+    vnew = *reinterpret_cast<const uint32_t*>(a.vn + src);
+  }
+  if (wave_store) {
+    *reinterpret_cast<uint32_t*>(a.kst + dst + 2 * lane) = knew;
+    *reinterpret_cast<uint32_t*>(a.vst + dst + 2 * lane) = vnew;
+  }
+  const int tnew = wave_subst ? (L - 1 - tw) / kDecTile : -1;   // tile of this wave holding it
 
   const int blk0 = PAGED ? split * a.chunk / a.bs : 0;   // first table entry of the chunk
   if constexpr (PAGED) {
@@ -168,6 +217,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     // the other stage was last read by tile i-1, whose reads completed before its MFMAs
     issue(i + 1);
     __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | 0x0F70);   // tile i landed; tile i+1 (16 loads) may pend
+    if (i == tnew) {   // fused append: the new rows replace the cached key L - 1
+      uint16_t* kt = lds + wave * WRING + (i & 1) * 2 * TE;
+      const int r = L - 1 - (tw + i * kDecTile);
+      const int c = lane >> 2, e = 2 * (lane & 3);   // 16-byte chunk and element of d = 2 lane
+      *reinterpret_cast<uint32_t*>(kt + r * kDecD + (c ^ (r & 15)) * 8 + e) = knew;
+      *reinterpret_cast<uint32_t*>(kt + TE + r * kDecD + (c ^ (4 * (r & 3))) * 8 + e) = vnew;
+    }
     const uint16_t* ks = lds + wave * WRING + (i & 1) * 2 * TE;
     const uint16_t* vs = ks + TE;
     f32x16 st;
@@ -217,23 +273,50 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     // O^T[d, col] += V^T[d, keys] P^T[keys, col]; step `half` covers keys
-    // 16 half + {4 hl + 0..3, 8 + 4 hl + 0..3} (the P^T register order)
+    // 16 half + {4 hl + 0..3, 8 + 4 hl + 0..3} (the P^T register order).
+    // The V^T fragments come from 16 transposing reads (row r0 and r0 + 8,
+    // 2048 bytes further, share the chunk swizzle).  They are issued by one
+    // asm block that also waits for them: the compiler would otherwise wait
+    // for every load in flight, the next tile's included, before its own
+    // ds_read_b64_tr_b16, because it cannot tell that they read the other
+    // stage.
+    u32x2 vf[2][4][2];
+    {
+      uint32_t va[2][4];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int k0 = half * 16 + 4 * hl;
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int d = 32 * db + tr_d, r0 = half * 16 + 4 * hl + tr_row;
+          va[half][db] = (uint32_t)reinterpret_cast<uintptr_t>(
+              (TPL_DLDS uint16_t*)vs + r0 * kDecD + ((d >> 3) ^ (4 * (r0 & 3))) * 8 + (d & 7));
+        }
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16\n\tds_read_b64_tr_b16 %1, %16 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %2, %17\n\tds_read_b64_tr_b16 %3, %17 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %4, %18\n\tds_read_b64_tr_b16 %5, %18 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %6, %19\n\tds_read_b64_tr_b16 %7, %19 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %8, %20\n\tds_read_b64_tr_b16 %9, %20 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %10, %21\n\tds_read_b64_tr_b16 %11, %21 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %12, %22\n\tds_read_b64_tr_b16 %13, %22 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %14, %23\n\tds_read_b64_tr_b16 %15, %23 offset:2048\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(vf[0][0][0]), "=&v"(vf[0][0][1]), "=&v"(vf[0][1][0]), "=&v"(vf[0][1][1]),
+            "=&v"(vf[0][2][0]), "=&v"(vf[0][2][1]), "=&v"(vf[0][3][0]), "=&v"(vf[0][3][1]),
+            "=&v"(vf[1][0][0]), "=&v"(vf[1][0][1]), "=&v"(vf[1][1][0]), "=&v"(vf[1][1][1]),
+            "=&v"(vf[1][2][0]), "=&v"(vf[1][2][1]), "=&v"(vf[1][3][0]), "=&v"(vf[1][3][1])
+          : "v"(va[0][0]), "v"(va[0][1]), "v"(va[0][2]), "v"(va[0][3]),
+            "v"(va[1][0]), "v"(va[1][1]), "v"(va[1][2]), "v"(va[1][3])
+          : "memory");
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int d = 32 * db + tr_d;
-        const int r0 = k0 + tr_row, r1 = k0 + 8 + tr_row;
-        const dec_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (TPL_DLDS dec_s16x4*)((TPL_DLDS uint16_t*)vs + r0 * kDecD + ((d >> 3) ^ (4 * (r0 & 3))) * 8 + (d & 7)));
-        const dec_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (TPL_DLDS dec_s16x4*)((TPL_DLDS uint16_t*)vs + r1 * kDecD + ((d >> 3) ^ (4 * (r1 & 3))) * 8 + (d & 7)));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x2 l2 = vf[half][db][0], h2 = vf[half][db][1];
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]}),
                                                            pb[half], oacc[db], 0, 0, 0);
       }
-    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // the trailing (out-of-range) DMA has landed
   const float lsum = dec_pair_sum(lrun);
@@ -342,8 +425,12 @@ size_t attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv) {
 
 tp_status attn_decode(const void* q, const int64_t qs[3], const void* k, const void* v,
                       const int64_t kvs[3], void* o, const int64_t os[3], int64_t B, int64_t Skv,
-                      int64_t Hq, int64_t Hkv, float scale, void* ws, hipStream_t s) {
+                      int64_t Hq, int64_t Hkv, float scale, void* ws, hipStream_t s,
+                      const void* kn, const void* vn, int64_t nstride) {
   DecArgs a;
+  a.kn = static_cast<const uint16_t*>(kn); a.vn = static_cast<const uint16_t*>(vn); a.nstride = nstride;
+  a.kst = const_cast<uint16_t*>(static_cast<const uint16_t*>(k));
+  a.vst = const_cast<uint16_t*>(static_cast<const uint16_t*>(v));
   a.q = static_cast<const uint16_t*>(q); a.qs0 = qs[0]; a.qs2 = qs[2];
   a.k = static_cast<const uint16_t*>(k); a.v = static_cast<const uint16_t*>(v);
   a.ks0 = kvs[0]; a.ks1 = kvs[1]; a.ks2 = kvs[2];
@@ -385,8 +472,12 @@ tp_status attn_decode_paged(const void* q, const int64_t qs[2], const void* kp, 
                             const int64_t ps[3], int64_t nblocks, const int* table, int64_t tstride,
                             const int* lens, int64_t max_len, int64_t bs, void* o,
                             const int64_t os[2], int64_t B, int64_t Hq, int64_t Hkv, float scale,
-                            void* ws, hipStream_t s) {
+                            void* ws, hipStream_t s, const void* kn, const void* vn,
+                            int64_t nstride) {
   DecArgs a;
+  a.kn = static_cast<const uint16_t*>(kn); a.vn = static_cast<const uint16_t*>(vn); a.nstride = nstride;
+  a.kst = const_cast<uint16_t*>(static_cast<const uint16_t*>(kp));
+  a.vst = const_cast<uint16_t*>(static_cast<const uint16_t*>(vp));
   a.q = static_cast<const uint16_t*>(q); a.qs0 = qs[0]; a.qs2 = qs[1];
   a.k = static_cast<const uint16_t*>(kp); a.v = static_cast<const uint16_t*>(vp);
   a.ks0 = ps[0]; a.ks1 = ps[1]; a.ks2 = ps[2];

@@ -34,7 +34,8 @@ tp_status kv_append(const void* kn, const void* vn, int64_t new_stride, void* kc
                     hipStream_t s);
 tp_status attn_decode(const void* q, const int64_t qs[3], const void* k, const void* v,
                       const int64_t kvs[3], void* o, const int64_t os[3], int64_t B, int64_t Skv,
-                      int64_t Hq, int64_t Hkv, float scale, void* ws, hipStream_t s);
+                      int64_t Hq, int64_t Hkv, float scale, void* ws, hipStream_t s,
+                      const void* kn = nullptr, const void* vn = nullptr, int64_t nstride = 0);
 tp_status attn_prefill_tr(const void* q, const int64_t qs[3], const void* k, const void* v,
                           const int64_t kvs[3], void* o, const int64_t os[3], int64_t B,
                           int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv, int causal, float scale,
@@ -60,7 +61,8 @@ tp_status attn_decode_paged(const void* q, const int64_t qs[2], const void* kp, 
                             const int64_t ps[3], int64_t nblocks, const int* table, int64_t tstride,
                             const int* lens, int64_t max_len, int64_t bs, void* o,
                             const int64_t os[2], int64_t B, int64_t Hq, int64_t Hkv, float scale,
-                            void* ws, hipStream_t s);
+                            void* ws, hipStream_t s, const void* kn = nullptr,
+                            const void* vn = nullptr, int64_t nstride = 0);
 tp_status paged_kv_append(const void* kn, const void* vn, int64_t new_stride, void* kp, void* vp,
                           const int64_t ps[3], int64_t nblocks, const int* table, int64_t tstride,
                           int64_t maxblk, const int* lens, int64_t B, int64_t H, int64_t D, int64_t bs,
@@ -205,6 +207,43 @@ tp_status tp_kv_append(const void* k_new, const void* v_new, int64_t new_stride,
                         as_stream(stream));
 }
 
+tp_status tp_decode_attention_append(const void* q, const int64_t qs[2], const void* k_new,
+                                     const void* v_new, int64_t new_stride, void* k_cache,
+                                     void* v_cache, const int64_t cs[3], int64_t T, int64_t pos,
+                                     void* o, const int64_t os[2], int64_t B, int64_t Hq,
+                                     int64_t Hkv, int64_t D, float scale, tp_dtype dt,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !qs || !k_new || !v_new || !k_cache || !v_cache || !cs || !o || !os) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return TP_ERR_SHAPE;
+  if (pos < 0 || pos >= T || new_stride < Hkv * D) return TP_ERR_SHAPE;
+  if (!isfinite(scale)) return TP_ERR_SHAPE;
+  if (dt != TP_BF16 || D != 128 || Hq / Hkv > 32) return TP_ERR_UNSUPPORTED;
+  if (B > 65535 || Hkv > 65535 || pos >= kIntMax) return TP_ERR_UNSUPPORTED;
+  for (int i = 0; i < 3; ++i) {
+    if (cs[i] < 0) return TP_ERR_SHAPE;
+    if (cs[i] % 8) return TP_ERR_ALIGN;
+  }
+  for (int i = 0; i < 2; ++i) {
+    if (qs[i] < 0 || os[i] < 0) return TP_ERR_SHAPE;
+    if (qs[i] % 8 || os[i] % 4) return TP_ERR_ALIGN;
+  }
+  if (new_stride % 8) return TP_ERR_ALIGN;
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(o, 8))
+    return TP_ERR_ALIGN;
+  const int64_t Skv = pos + 1;
+  // the kernel addresses one sequence's key span with 32-bit offsets
+  if ((pos * cs[1] + D) * 2 >= (int64_t{1} << 31)) return TP_ERR_UNSUPPORTED;
+  const size_t need = tpl::attn_decode_workspace(B, Hq, Hkv, Skv);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return TP_ERR_ALIGN;
+  const int64_t q3[3] = {qs[0], 0, qs[1]}, o3[3] = {os[0], 0, os[1]};
+  return tpl::attn_decode(q, q3, k_cache, v_cache, cs, o, o3, B, Skv, Hq, Hkv, scale,
+                          need > 0 ? workspace : nullptr, as_stream(stream), k_new, v_new,
+                          new_stride);
+}
+
 tp_status tp_reduce_partials(const float* const* partials, int64_t R, const void* residual,
                              void* y, int64_t M, int64_t N, tp_dtype out_dt, void* stream) {
   if (!partials || !y) return TP_ERR_NULL;
@@ -259,13 +298,14 @@ size_t tp_paged_attention_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t 
   return tpl::attn_paged_workspace(B, Hq, Hkv, max_context_len, block_size);
 }
 
-tp_status tp_paged_attention_decode(const void* q, const int64_t qs[2], const void* k_pool,
-                                    const void* v_pool, const int64_t ps[3], int64_t num_blocks,
-                                    const int32_t* block_table, int64_t table_stride,
-                                    const int32_t* context_lens, int64_t max_context_len,
-                                    int64_t block_size, void* o, const int64_t os[2], int64_t B,
-                                    int64_t Hq, int64_t Hkv, int64_t D, float scale, tp_dtype dt,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+static tp_status paged_decode_common(const void* q, const int64_t qs[2], const void* k_pool,
+                                     const void* v_pool, const int64_t ps[3], int64_t num_blocks,
+                                     const int32_t* block_table, int64_t table_stride,
+                                     const int32_t* context_lens, int64_t max_context_len,
+                                     int64_t block_size, void* o, const int64_t os[2], int64_t B,
+                                     int64_t Hq, int64_t Hkv, int64_t D, float scale, tp_dtype dt,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     const void* k_new, const void* v_new, int64_t new_stride) {
   if (!q || !qs || !k_pool || !v_pool || !ps || !block_table || !context_lens || !o || !os)
     return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
@@ -294,7 +334,35 @@ tp_status tp_paged_attention_decode(const void* q, const int64_t qs[2], const vo
   if (need > 0 && !aligned(workspace, 4)) return TP_ERR_ALIGN;
   return tpl::attn_decode_paged(q, qs, k_pool, v_pool, ps, num_blocks, block_table, table_stride,
                                 context_lens, max_context_len, block_size, o, os, B, Hq, Hkv, scale,
-                                workspace, as_stream(stream));
+                                workspace, as_stream(stream), k_new, v_new, new_stride);
+}
+
+tp_status tp_paged_attention_decode(const void* q, const int64_t qs[2], const void* k_pool,
+                                    const void* v_pool, const int64_t ps[3], int64_t num_blocks,
+                                    const int32_t* block_table, int64_t table_stride,
+                                    const int32_t* context_lens, int64_t max_context_len,
+                                    int64_t block_size, void* o, const int64_t os[2], int64_t B,
+                                    int64_t Hq, int64_t Hkv, int64_t D, float scale, tp_dtype dt,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return paged_decode_common(q, qs, k_pool, v_pool, ps, num_blocks, block_table, table_stride,
+                             context_lens, max_context_len, block_size, o, os, B, Hq, Hkv, D, scale,
+                             dt, workspace, workspace_bytes, stream, nullptr, nullptr, 0);
+}
+
+tp_status tp_paged_decode_attention_append(
+    const void* q, const int64_t qs[2], const void* k_new, const void* v_new, int64_t new_stride,
+    void* k_pool, void* v_pool, const int64_t ps[3], int64_t num_blocks, const int32_t* block_table,
+    int64_t table_stride, const int32_t* context_lens, int64_t max_context_len, int64_t block_size,
+    void* o, const int64_t os[2], int64_t B, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+    tp_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new) return TP_ERR_NULL;
+  if (new_stride < Hkv * D) return TP_ERR_SHAPE;
+  if (new_stride % 8 || !aligned(k_new, 16) || !aligned(v_new, 16)) return TP_ERR_ALIGN;
+  // every other argument as tp_paged_attention_decode, which validates them
+  // and then runs the fused kernel when given the new rows
+  return paged_decode_common(q, qs, k_pool, v_pool, ps, num_blocks, block_table, table_stride,
+                             context_lens, max_context_len, block_size, o, os, B, Hq, Hkv, D, scale,
+                             dt, workspace, workspace_bytes, stream, k_new, v_new, new_stride);
 }
 
 tp_status tp_paged_kv_append(const void* k_new, const void* v_new, int64_t new_stride, void* k_pool,

@@ -27,9 +27,10 @@ from __future__ import annotations
 
 import torch
 
-from . import (column_linear, column_linear_act, local_attention, kv_append, reduce_partials,
-               reduce_partials_rmsnorm, rmsnorm, row_linear_partial, swiglu_local,
-               vocab_argmax_local, vocab_argmax_reduce, paged_attention_decode, paged_kv_append)
+from . import (column_linear, column_linear_act, decode_attention_append, kv_append,
+               local_attention, paged_attention_workspace, paged_decode_attention_append,
+               reduce_partials, reduce_partials_rmsnorm, rmsnorm, row_linear_partial,
+               swiglu_local, vocab_argmax_local, vocab_argmax_reduce)
 
 
 class MlpShard:
@@ -115,12 +116,15 @@ class AttnShard:
         qkv = self.qkv[:B]
         column_linear(x, self.wqkv, out=qkv)
         q, k, v = self._views(qkv, B, 1)
-        kv_append(k[:, 0], v[:, 0], k_cache, v_cache, pos)
-        kc = k_cache[:, :pos + 1]
-        vc = v_cache[:, :pos + 1]
         o = self.o[:B]
-        local_attention(q, kc, vc, causal=True, out=o.view(B, 1, self.n_q, self.D),
-                        workspace=self._workspace(B, pos + 1, x.device))
+        ws = self._workspace(B, pos + 1, x.device)
+        if self.n_q // self.n_kv <= 32:   # append and attention in one launch
+            decode_attention_append(q[:, 0], k[:, 0], v[:, 0], k_cache, v_cache, pos,
+                                    out=o.view(B, self.n_q, self.D), workspace=ws)
+        else:
+            kv_append(k[:, 0], v[:, 0], k_cache, v_cache, pos)
+            local_attention(q, k_cache[:, :pos + 1], v_cache[:, :pos + 1], causal=True,
+                            out=o.view(B, 1, self.n_q, self.D), workspace=ws)
         row_linear_partial(o, self.wo, out=out)
         return out
 
@@ -135,14 +139,14 @@ class AttnShard:
         qkv = self.qkv[:B]
         column_linear(x, self.wqkv, out=qkv)
         q, k, v = self._views(qkv, B, 1)
-        paged_kv_append(k[:, 0], v[:, 0], k_pool, v_pool, block_table, context_lens)
         o = self.o[:B]
-        from . import paged_attention_workspace
         need = paged_attention_workspace(B, self.n_q, self.n_kv, max_context_len, k_pool.shape[1])
         if need and (self.ws is None or self.ws.numel() < need):
             self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
-        paged_attention_decode(q[:, 0], k_pool, v_pool, block_table, context_lens, max_context_len,
-                               out=o.view(B, self.n_q, self.D), workspace=self.ws)
+        # append and attention in one launch (the kernel takes G <= 32 in both forms)
+        paged_decode_attention_append(q[:, 0], k[:, 0], v[:, 0], k_pool, v_pool, block_table,
+                                      context_lens, max_context_len,
+                                      out=o.view(B, self.n_q, self.D), workspace=self.ws)
         row_linear_partial(o, self.wo, out=out)
         return out
 
