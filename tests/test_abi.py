@@ -288,3 +288,53 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(2, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         tpl.column_linear(x, x)
+
+
+@no_gpu
+def test_decode_attention_append_validation(lib):
+    """The fused append + decode attention entry points reject bad arguments on
+    the host, before any launch (made-up addresses are never dereferenced)."""
+    f = lib.tp_decode_attention_append
+    cs = _s3(64 * 2 * 128, 2 * 128, 128)      # [B, T=64, Hkv=2, D=128]
+
+    def call(q=P, qs=_s2(1536, 128), kn=P, vn=P, ns=1536, kc=P, vc=P, cs=cs, T=64, pos=10, o=P,
+             os_=_s2(1024, 128), B=2, Hq=8, Hkv=2, D=128, scale=0.088, dt=1, ws=None, wsb=0):
+        return f(q, qs, kn, vn, ns, kc, vc, cs, T, pos, o, os_, B, Hq, Hkv, D, scale, dt, ws, wsb, S)
+
+    assert call(q=None) == NULL
+    assert call(kn=None) == NULL
+    assert call(cs=None) == NULL
+    assert call(dt=7) == DTYPE
+    assert call(Hq=6, Hkv=4) == SHAPE                 # Hq % Hkv != 0
+    assert call(pos=64) == SHAPE                      # past the cache's capacity
+    assert call(pos=-1) == SHAPE
+    assert call(ns=128) == SHAPE                      # row stride < Hkv*D
+    assert call(scale=float("nan")) == SHAPE
+    assert call(D=64) == UNSUPPORTED
+    assert call(dt=0) == UNSUPPORTED
+    assert call(Hq=66, Hkv=1) == UNSUPPORTED          # G > 32
+    assert call(cs=_s3(64 * 2 * 128, 2 * 128 + 4, 128)) == ALIGN
+    assert call(ns=1540) == ALIGN
+    assert call(kn=P + 2) == ALIGN
+    assert call(qs=_s2(1536, 100)) == ALIGN
+    # one sequence, long span: split-key path, workspace required
+    need = lib.tp_local_attention_workspace(1, 1, 4096, 8, 2, 128)
+    assert need > 0
+    big = _s3(4096 * 2 * 128, 2 * 128, 128)
+    assert call(B=1, T=4096, pos=4095, cs=big) == WORKSPACE
+    assert call(B=1, T=4096, pos=4095, cs=big, ws=P, wsb=need - 1) == WORKSPACE
+
+    g = lib.tp_paged_decode_attention_append
+    ps = _s3(16 * 2 * 128, 2 * 128, 128)
+
+    def pcall(kn=P, vn=P, ns=1536, ts=8, Hq=8, Hkv=2, maxl=100, B=2, ws=None, wsb=0):
+        return g(P, _s2(1536, 128), kn, vn, ns, P, P, ps, 64, P, ts, P, maxl, 16, P, _s2(1024, 128),
+                 B, Hq, Hkv, 128, 0.088, 1, ws, wsb, S)
+
+    assert pcall(kn=None) == NULL
+    assert pcall(ns=128) == SHAPE
+    assert pcall(ns=1540) == ALIGN
+    assert pcall(vn=P + 8) == ALIGN
+    assert pcall(ts=6) == SHAPE                       # table rows shorter than max_context_len needs
+    assert pcall(Hq=66, Hkv=1) == UNSUPPORTED
+    assert pcall(B=1, maxl=4096, ts=256) == WORKSPACE
