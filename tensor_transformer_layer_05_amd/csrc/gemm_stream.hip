@@ -186,14 +186,17 @@ tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M,
                                int64_t K, bool out_f32, hipStream_t s);
 
 // Waves per workgroup of the one-token-tile decode linear on an [N, K]
-// weight: split K so that every wave streams >= 256 k; 16 waves (1024
-// threads) when there are few row tiles to spread over the chip.  The
-// fused-activation variant takes the same split (hence the same float sums)
-// as the plain linear on the full weight.
+// weight: 16 waves (1024 threads) when there are few row tiles to spread over
+// the chip, fewer until every wave streams >= 512 k (four 128-k chunks, so
+// its double-buffered loads have a run to overlap; one token, kernel trace:
+// [1536, 4096] 8.22 -> 7.38 us with 8 waves instead of 16, [8192, 3584]
+// 14.0 -> 13.9 us with 4 instead of 8).  The fused-activation variant takes
+// the same split (hence the same float sums) as the plain linear on the full
+// weight.
 static int stream_waves(int64_t N, int64_t K) {
   const int64_t nblk = (N + 15) / 16;
   int waves = nblk < 384 ? 16 : 8;
-  while (waves > 4 && K / waves < 256) waves >>= 1;
+  while (waves > 4 && K / waves < 512) waves >>= 1;
   return waves;
 }
 
