@@ -158,6 +158,25 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   auto issue = [&](int i) {
     TPL_DLDS uint16_t* kd = ring + (i & 1) * 2 * TE;
     TPL_DLDS uint16_t* vd = kd + TE;
+    // Paged: the tile starts at a multiple of 32 keys and bs is a multiple of
+    // 16, so each 16-row half of the tile lies in one block: two table
+    // lookups and four buffer resources per tile.  A half that starts past
+    // the span, or whose entry is outside [0, nblocks), gets an empty
+    // resource (zeros); rows past the span inside a valid half read zero
+    // through their per-lane offsets.
+    __amdgpu_buffer_rsrc_t pk[2], pv[2];
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int t0 = tw + i * kDecTile + 16 * hf;
+        int pb = (t0 < L && i < nt) ? tbl[t0 / a.bs - blk0] : -1;
+        pb = __builtin_amdgcn_readfirstlane(pb);
+        const bool bok = pb >= 0 && pb < a.nblocks;
+        const int64_t base = (bok ? pb * a.ks0 : 0) + j * a.ks2;
+        pk[hf] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + base), 0, bok ? nrec : 0u, 0x00020000);
+        pv[hf] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + base), 0, bok ? nrec : 0u, 0x00020000);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < kDecTile / 4; ++u) {
       const int row = 4 * u + lr;
@@ -165,20 +184,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       const bool ok = t < L && i < nt;
       const int kc = lp ^ (row & 15), vc = lp ^ (4 * (row & 3));
       if constexpr (PAGED) {
-        // rows t0 .. t0+3 of this load share one block (bs % 16 == 0)
-        const int t0 = tw + i * kDecTile + 4 * u;
-        int pb = (t0 < L && i < nt) ? tbl[t0 / a.bs - blk0] : -1;
-        pb = __builtin_amdgcn_readfirstlane(pb);
-        const bool bok = pb >= 0 && pb < a.nblocks;
-        const int64_t base = (bok ? pb * a.ks0 : 0) + j * a.ks2;
-        const __amdgpu_buffer_rsrc_t kb = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(a.k + base), 0, bok ? nrec : 0u, 0x00020000);
-        const __amdgpu_buffer_rsrc_t vb = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(a.v + base), 0, bok ? nrec : 0u, 0x00020000);
         const uint32_t rb = (uint32_t)((int64_t)(t % a.bs) * a.ks1 * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kb, (TPL_DLDS void*)(kd + u * 4 * kDecD), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pk[u >= 4], (TPL_DLDS void*)(kd + u * 4 * kDecD), 16,
                                                  ok ? rb + (uint32_t)kc * 16u : 0x80000000u, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vb, (TPL_DLDS void*)(vd + u * 4 * kDecD), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pv[u >= 4], (TPL_DLDS void*)(vd + u * 4 * kDecD), 16,
                                                  ok ? rb + (uint32_t)vc * 16u : 0x80000000u, 0, 0, 0);
       } else {
         const uint32_t rb = (uint32_t)((int64_t)t * a.ks1 * 2);
