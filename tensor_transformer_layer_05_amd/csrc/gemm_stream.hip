@@ -38,14 +38,16 @@ __device__ __forceinline__ u32x4 bload(const __amdgpu_buffer_rsrc_t r, uint32_t 
 template <int WAVES, int MT, int RT, bool OUT_F32, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
-    int M, int N, int K, int kw) {
+    int M, int N, int K, int kw, int rows_wg) {
   __shared__ float red[WAVES * RT * MT * 256];
   static_assert(EPI != 1 || RT == 2, "SwiGLU pairs a gate and an up row tile");
-  constexpr int OUT_ROWS = EPI == 1 ? 16 : 16 * RT;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * OUT_ROWS;
+  // this workgroup's output rows n0 .. n0 + nrows - 1 (rows_wg <= 16 RT, or
+  // <= 16 gate|up pairs): fewer than a full tile when that fills more CUs
+  const int n0 = blockIdx.x * rows_wg;
+  const int nrows = min(rows_wg, N - n0);
   const int g = lane >> 4;         // k-group of this lane inside a 32-k step
   const int i16 = lane & 15;       // weight row / token inside a 16-tile
 
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     const int base = EPI == 1 ? (r == 0 ? n0 : N + n0) : n0 + 16 * r;
-    const int rows = EPI == 1 ? min(16, N - n0) : max(0, min(16, N - n0 - 16 * r));
+    const int rows = EPI == 1 ? nrows : max(0, min(16, nrows - 16 * r));
     wr[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)base * K), 0,
                                               (uint32_t)rows * (uint32_t)K * 2u, 0x00020000);
   }
@@ -139,8 +141,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
       for (int w = 0; w < WAVES; ++w) { sg += red[w * PER + v]; su += red[w * PER + MT * 256 + v]; }
       const int t = v / 256, l = (v >> 2) & 63, e = v & 3;
       const int m = t * 16 + (l & 15);
-      const int n = n0 + (l >> 4) * 4 + e;
-      if (m < M && n < N)
+      const int nl = (l >> 4) * 4 + e, n = n0 + nl;
+      if (m < M && nl < nrows)
         reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] = (uint16_t)f2bf_bits(
             act_fn<TP_ACT_SWIGLU>(bf2f((uint16_t)f2bf_bits(sg)), bf2f((uint16_t)f2bf_bits(su))));
     }
@@ -152,8 +154,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
     for (int w = 0; w < WAVES; ++w) s += red[w * PER + v];
     const int rt = v / (MT * 256), t = (v / 256) % MT, l = (v >> 2) & 63, e = v & 3;
     const int m = t * 16 + (l & 15);
-    const int n = n0 + rt * 16 + (l >> 4) * 4 + e;
-    if (m < M && n < N) {
+    const int nl = rt * 16 + (l >> 4) * 4 + e, n = n0 + nl;
+    if (m < M && nl < nrows) {
       if constexpr (EPI == 2)
         reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] =
             (uint16_t)f2bf_bits(act_fn<TP_ACT_GELU>(bf2f((uint16_t)f2bf_bits(s)), 0.f));
@@ -165,20 +167,37 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
   }
 }
 
+constexpr int64_t kStreamRegCUs = 256;   // compute units of an MI355X
+
+// Output rows per workgroup: a full tile (16 RT rows, or 16 gate|up pairs),
+// or, when full tiles would leave CUs idle, the fewest rows that still give
+// one workgroup per CU (rows past them read as zero through the buffer bound
+// and are not stored).  The K split does not depend on it, so neither do the
+// sums.  Kernel trace, same bits: the decode gate|up + SwiGLU [7168, 8192] on
+// 256 workgroups of 14 pairs instead of 224 of 16, 23.6 -> 22.4 us at one
+// token and 24.3 -> 22.9 us at eight; a one-token QKV [1536, 4096] on 256
+// workgroups of 6 rows instead of 96 of 16, 7.5 -> 5.8 us.
+static int stream_rows(int64_t nout, int out_rows) {
+  const int64_t tiles = (nout + out_rows - 1) / out_rows;
+  if (tiles >= kStreamRegCUs) return out_rows;
+  return (int)((nout + kStreamRegCUs - 1) / kStreamRegCUs);
+}
+
 template <int WAVES, int MT, int RT, int EPI = 0>
 static void launch_stream(const void* x, const void* w, void* y, int M, int N, int K, int kw,
                           bool out_f32, hipStream_t s) {
   constexpr int OUT_ROWS = EPI == 1 ? 16 : 16 * RT;
-  dim3 grid((N + OUT_ROWS - 1) / OUT_ROWS), block(WAVES * 64);
+  const int rows_wg = stream_rows(N, OUT_ROWS);
+  dim3 grid((N + rows_wg - 1) / rows_wg), block(WAVES * 64);
   auto X = static_cast<const uint16_t*>(x);
   auto Wp = static_cast<const uint16_t*>(w);
   if constexpr (EPI == 0) {
     if (out_f32)
-      hipLaunchKernelGGL((gemm_stream_kernel<WAVES, MT, RT, true, 0>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+      hipLaunchKernelGGL((gemm_stream_kernel<WAVES, MT, RT, true, 0>), grid, block, 0, s, X, Wp, y, M, N, K, kw, rows_wg);
     else
-      hipLaunchKernelGGL((gemm_stream_kernel<WAVES, MT, RT, false, 0>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+      hipLaunchKernelGGL((gemm_stream_kernel<WAVES, MT, RT, false, 0>), grid, block, 0, s, X, Wp, y, M, N, K, kw, rows_wg);
   } else {
-    hipLaunchKernelGGL((gemm_stream_kernel<WAVES, MT, RT, false, EPI>), grid, block, 0, s, X, Wp, y, M, N, K, kw);
+    hipLaunchKernelGGL((gemm_stream_kernel<WAVES, MT, RT, false, EPI>), grid, block, 0, s, X, Wp, y, M, N, K, kw, rows_wg);
   }
 }
 
