@@ -43,6 +43,7 @@ ACT_SHAPES = [
     (32, 4096, 3584),    # two token tiles, two row tiles per wave
     (33, 1024, 300),     # LDS-ring kernel, three token tiles
     (64, 3584, 264),     # LDS-ring kernel, four token tiles
+    (64, 520, 3001),     # LDS-ring kernel, 12 gate|up pairs per workgroup, last one 1
     (65, 1024, 448),     # prefill tile kernel, ragged tokens
     (300, 520, 1000),
     (1000, 2048, 700),

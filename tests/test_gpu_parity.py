@@ -59,6 +59,8 @@ INT_SHAPES = [
     (4, 16384, 40), (16, 8192, 6200),
     # 17..32 tokens: one token tile per workgroup up to 2048 rows, two row tiles past 4096
     (29, 264, 4200), (20, 520, 2040),
+    # LDS-ring kernel with rows per workgroup cut to fill the CUs (ragged last workgroup)
+    (40, 1000, 4999), (32, 1000, 1499),
     # MFMA tile path: ragged M/N/K, each tile shape
     (65, 64, 16), (200, 136, 130), (300, 520, 300), (512, 264, 640), (4000, 264, 4000),
     (4096, 200, 2048), (4000, 136, 5100),   # the last picks 256x320 tiles
