@@ -28,25 +28,53 @@ __device__ __forceinline__ void take(float v, int i, float& bv, int& bi) {
 
 }  // namespace
 
-// One workgroup per token row: 256 threads scan the row (16-byte loads when
-// the row is 16-byte aligned), then combine across the wave and the 4 waves.
-__global__ __launch_bounds__(256) void vocab_argmax_kernel(const float* __restrict__ logits, int V,
-                                                           int64_t offset, float* __restrict__ mv,
-                                                           int64_t* __restrict__ mi, int vec) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
+// One workgroup of 1024 threads per token row.  Each thread issues up to
+// kArgUnroll loads (16-byte ones when the row is 16-byte aligned) before it
+// scans any of them, so a 16032-entry row costs one memory round trip rather
+// than one per 1024 entries; then the waves combine by shuffles and LDS.
+constexpr int kArgThreads = 1024, kArgWaves = kArgThreads / 64, kArgUnroll = 8;
+
+__global__ __launch_bounds__(kArgThreads) void vocab_argmax_kernel(const float* __restrict__ logits, int V,
+                                                                   int64_t offset, float* __restrict__ mv,
+                                                                   int64_t* __restrict__ mi, int vec) {
+  __shared__ float sv[kArgWaves];
+  __shared__ int si[kArgWaves];
   const int64_t m = blockIdx.x;
   const float* row = logits + m * (int64_t)V;
   float bv = -INFINITY;
   int bi = INT32_MAX;
-  if (vec) {
-    for (int c = threadIdx.x * 4; c < V; c += 256 * 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(row + c);
+  if (vec) {   // V % 4 == 0, row 16-byte aligned
+    const int n4 = V >> 2;
+    for (int c0 = threadIdx.x; c0 < n4; c0 += kArgThreads * kArgUnroll) {
+      f32x4 x[kArgUnroll];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) take(x[e], c + e, bv, bi);
+      for (int u = 0; u < kArgUnroll; ++u) {
+        const int c = c0 + u * kArgThreads;
+        if (c < n4) x[u] = reinterpret_cast<const f32x4*>(row)[c];
+      }
+#pragma unroll
+      for (int u = 0; u < kArgUnroll; ++u) {
+        const int c = c0 + u * kArgThreads;
+        if (c < n4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) take(x[u][e], 4 * c + e, bv, bi);
+        }
+      }
     }
   } else {
-    for (int c = threadIdx.x; c < V; c += 256) take(row[c], c, bv, bi);
+    for (int c0 = threadIdx.x; c0 < V; c0 += kArgThreads * kArgUnroll) {
+      float x[kArgUnroll];
+#pragma unroll
+      for (int u = 0; u < kArgUnroll; ++u) {
+        const int c = c0 + u * kArgThreads;
+        if (c < V) x[u] = row[c];
+      }
+#pragma unroll
+      for (int u = 0; u < kArgUnroll; ++u) {
+        const int c = c0 + u * kArgThreads;
+        if (c < V) take(x[u], c, bv, bi);
+      }
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -57,7 +85,7 @@ __global__ __launch_bounds__(256) void vocab_argmax_kernel(const float* __restri
   if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
+    for (int w = 1; w < kArgWaves; ++w)
       if (beats(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
     mv[m] = bv;
     mi[m] = offset + bi;
@@ -66,7 +94,7 @@ __global__ __launch_bounds__(256) void vocab_argmax_kernel(const float* __restri
 
 tp_status vocab_argmax_local(const float* logits, int64_t M, int64_t V, int64_t offset, float* mv,
                              int64_t* mi, bool vec, hipStream_t s) {
-  hipLaunchKernelGGL(vocab_argmax_kernel, dim3((unsigned)M), dim3(256), 0, s, logits, (int)V, offset,
+  hipLaunchKernelGGL(vocab_argmax_kernel, dim3((unsigned)M), dim3(kArgThreads), 0, s, logits, (int)V, offset,
                      mv, mi, (int)vec);
   TPL_LAUNCH_CHECK("vocab_argmax_local");
   return TP_OK;
