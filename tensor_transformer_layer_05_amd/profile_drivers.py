@@ -14,6 +14,12 @@ GEMM on the same operands (output [4096, 28672]).  Run it under
 8 q / 2 KV heads of 128) over key spans of 512 .. 16384, 20 calls each on
 rotating cache copies, for ``rocprofv3 --kernel-trace``: the kernel durations
 per span separate the fixed cost of a launch from the streaming rate.
+
+``hbm_reference``: what plain streaming reaches on this GPU, next to the
+library's own decode weight stream: 20 device-to-device copies of 1 GiB, 20
+full sums of a 1 GiB float32 tensor (read only), then 20 one-token decode
+gate|up + SwiGLU calls (weight [7168, 8192] bf16, four rotating copies), for
+``rocprofv3 --kernel-trace``.
 """
 from __future__ import annotations
 
@@ -70,7 +76,31 @@ def decode_attn_span() -> None:
         del sets
 
 
-DRIVERS = {"gemm_traffic": gemm_traffic, "decode_attn_span": decode_attn_span}
+HBM_REF_BYTES = 1 << 30
+HBM_REF_CALLS = 20
+
+
+def hbm_reference() -> None:
+    lib()
+    a = torch.ones(HBM_REF_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    f = torch.ones(HBM_REF_BYTES // 4, dtype=torch.float32, device="cuda")
+    ws = [(torch.randn(7168, 8192, device="cuda") * 0.02).to(torch.bfloat16) for _ in range(4)]
+    x = torch.randn(1, 8192, device="cuda").to(torch.bfloat16)
+    torch.cuda.synchronize()
+    for _ in range(HBM_REF_CALLS):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    for _ in range(HBM_REF_CALLS):
+        f.sum()
+    torch.cuda.synchronize()
+    for i in range(HBM_REF_CALLS):
+        column_linear_act(x, ws[i % 4], "swiglu")
+    torch.cuda.synchronize()
+    print("hbm_reference done", flush=True)
+
+
+DRIVERS = {"gemm_traffic": gemm_traffic, "decode_attn_span": decode_attn_span, "hbm_reference": hbm_reference}
 
 if __name__ == "__main__":
     DRIVERS[sys.argv[1] if len(sys.argv) > 1 else "gemm_traffic"]()

@@ -252,6 +252,38 @@ are about half of the attention time.
 """
 
 
+def hbm_reference(out):
+    from .profile_drivers import HBM_REF_BYTES, HBM_REF_CALLS
+    trace = _csv(os.path.join(out, "prof_hbm", "**", "*kernel_trace.csv"))
+    ks = sorted(trace, key=lambda r: int(r["Start_Timestamp"]))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    med = lambda v: sorted(v)[len(v) // 2]
+    copy = [dur(r) for r in ks if "copyBuffer" in r["Kernel_Name"]]    # the runtime's blit kernel
+    red = [dur(r) for r in ks if "reduce_kernel" in r["Kernel_Name"]]
+    gemv = [dur(r) for r in ks if "gemm_stream_kernel" in r["Kernel_Name"]]
+    gemv_name = next(r["Kernel_Name"] for r in ks if "gemm_stream_kernel" in r["Kernel_Name"])
+    wbytes = 7168 * 8192 * 2
+    rows = [("device-to-device copy, 1 GiB read + 1 GiB written", copy, 2 * HBM_REF_BYTES),
+            ("torch sum of a 1 GiB float32 tensor (read only)", red, HBM_REF_BYTES),
+            (f"decode gate|up + SwiGLU, one token (`{gemv_name[:60]}`), weight read", gemv, wbytes)]
+    lines = [f"| {what} | {len(v)} | {med(v):.1f} | {b / (med(v) * 1e-6) / 1e12:.2f} | "
+             f"{b / (med(v) * 1e-6) / 8e12:.2f} |" for what, v, b in rows]
+    return f"""# Plain streaming rates on this GPU next to the decode weight stream (rocprofv3 --kernel-trace)
+
+Command (from /tmp with TMPDIR=/tmp; REPO = repository root), then the summary script:
+
+```
+rocprofv3 --kernel-trace --output-format csv -d $REPO/gpurun_out/prof_hbm -o h -- python3 -m tensor_transformer_layer_05_amd.profile_drivers hbm_reference
+python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
+```
+
+{HBM_REF_CALLS} calls each; median kernel durations from the trace; the fraction is of the 8 TB/s HBM peak.
+
+| kernel | calls | median us | TB/s | of 8 TB/s |
+|---|---:|---:|---:|---:|
+""" + "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     argv = argv or sys.argv[1:]
     out = argv[0] if argv else "gpurun_out"
@@ -264,6 +296,9 @@ def main(argv=None):
     if glob.glob(os.path.join(out, "prof_span", "**", "*kernel_trace.csv"), recursive=True):
         open(os.path.join(ROOT, "profiles", "decode_attention_span.md"), "w").write(decode_span(out))
         print("wrote profiles/decode_attention_span.md")
+    if glob.glob(os.path.join(out, "prof_hbm", "**", "*kernel_trace.csv"), recursive=True):
+        open(os.path.join(ROOT, "profiles", "hbm_reference.md"), "w").write(hbm_reference(out))
+        print("wrote profiles/hbm_reference.md")
 
 
 if __name__ == "__main__":
