@@ -39,7 +39,11 @@ def _planted_logits(seed, M, V):
 
 
 @pytest.mark.parametrize("M,V", [(1, 1), (1, 7), (3, 1000), (8, 16032), (64, 16032), (5, 128256),
-                                 (2, 130), (6, 131)])
+                                 (2, 130), (6, 131),
+                                 # 16-byte path: a second pass over the row with one live
+                                 # element, where row 3 has its max; 4-byte path (V % 4 != 0)
+                                 # over several passes
+                                 (4, 4 * 8192 + 4), (5, 70001)])
 def test_vocab_argmax_local_exact(M, V):
     log(f"vocab argmax local M={M} V={V}")
     z = _planted_logits(50, M, V)

@@ -44,6 +44,8 @@ ACT_SHAPES = [
     (33, 1024, 300),     # LDS-ring kernel, three token tiles
     (64, 3584, 264),     # LDS-ring kernel, four token tiles
     (64, 520, 3001),     # LDS-ring kernel, 12 gate|up pairs per workgroup, last one 1
+    (40, 520, 2501),     # LDS-ring kernel, 3 token tiles: SwiGLU cut to 10 pairs, last 1
+    (48, 264, 4999),     # LDS-ring kernel: GELU cut to 20 rows per workgroup, last 19
     (65, 1024, 448),     # prefill tile kernel, ragged tokens
     (300, 520, 1000),
     (1000, 2048, 700),
