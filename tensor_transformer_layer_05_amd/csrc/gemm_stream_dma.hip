@@ -254,15 +254,13 @@ static void launch_stream_dma(const void* x, const void* w, void* y, int M, int 
   }
 }
 
-// Waves per workgroup by token tiles (the K split; the fused-activation
-// variant must use the same): 2 for 4..16 tokens, 3 for 17..32, 2 for 33..64.
-// The sums depend only on the waves and their k ranges, not on how rows and
-// tokens are tiled over workgroups.
-// LDS per workgroup = WAVES x S x (16 RT + 16 MT) x 256 bytes <= 144 KB.
-
-
 // Requires 4 <= M <= 64, K % 8 == 0, 16-byte aligned X and W, and M*K and
 // 32*K elements addressable with 32-bit byte offsets.
+// Waves per workgroup by token tiles (the K split; the fused-activation
+// variant uses the same): 2 for 4..16 tokens, 3 for 17..32, 2 for 33..64.
+// The sums depend only on the waves and their k ranges, not on how rows and
+// tokens are tiled over workgroups.  LDS per workgroup = WAVES x S x (16 RT +
+// 16 MT) x 256 bytes <= 144 KB.
 tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M, int64_t N,
                                int64_t K, bool out_f32, hipStream_t s) {
   const int mt = (int)((M + 15) / 16);
