@@ -5,8 +5,9 @@
 // At decode the weight matrix is read once per call and dominates the bytes
 // (the "mostly GEMV" regime of decode), so the kernel is organised around
 // keeping many weight loads in flight:
-//   * a workgroup owns RT tiles of 16 consecutive weight rows (output
-//     features) and all of K; its WAVES waves split K into contiguous ranges;
+//   * a workgroup owns up to RT tiles of 16 consecutive weight rows (output
+//     features; fewer rows when that fills more CUs) and all of K; its WAVES
+//     waves split K into contiguous ranges;
 //   * each wave multiplies its (16 RT) x krange slice of W by the matching
 //     slice of X^T on v_mfma_f32_16x16x32_bf16 (W rows are the A operand, 16
 //     tokens per token tile the B operand); every X fragment feeds RT MFMAs;

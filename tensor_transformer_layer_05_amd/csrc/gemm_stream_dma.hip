@@ -9,8 +9,9 @@
 // only half of every 128-byte line they touch, and measured per-CU load
 // throughput is then what bounds these shapes.  So both operands go through
 // LDS:
-//   * a workgroup owns RT tiles of 16 consecutive weight rows and all of K;
-//     its WAVES waves split K into contiguous 128-k-aligned ranges;
+//   * a workgroup owns up to RT tiles of 16 consecutive weight rows (fewer
+//     rows when that fills more CUs), MT tiles of 16 tokens and all of K; its
+//     WAVES waves split K into contiguous 128-k-aligned ranges;
 //   * every wave streams its weight rows AND the token rows of its k range
 //     through a private S-stage LDS ring with buffer_load_dwordx4 ... lds: one
 //     wave-level load writes 4 rows x 256 contiguous bytes (two whole lines
