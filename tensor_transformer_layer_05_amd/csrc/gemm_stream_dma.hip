@@ -43,7 +43,7 @@ constexpr uint32_t kSOob = 0x80000000u;   // offset past any buffer bound -> rea
 // matching up rows N + n0.. of a [2N, K] weight; output [M, N]), 2 GELU.  The
 // fused epilogues round the sums to bf16 before the activation, as the
 // unfused path stores them.
-template <int WAVES, int MT, int RT, int S, bool OUT_F32, int EPI>
+template <int WAVES, int MT, int RT, int S, bool OUT_F32, int EPI, int TG>
 __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
     int M, int N, int K, int kw, int rows_wg) {
@@ -52,7 +52,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
   constexpr int WROWS = 16 * RT, XROWS = 16 * MT, ROWS = WROWS + XROWS;
   constexpr int STAGE = ROWS * 128;                   // bf16 elements per stage (256-byte rows)
   constexpr int RING = S * STAGE;                     // per wave
-  constexpr int DPC = ROWS / 4;                       // DMA instructions per chunk
+  static_assert(TG >= 1 && TG <= 4 * MT, "token row groups of 4 that are loaded");
+  constexpr int DPC = WROWS / 4 + TG;                 // DMA instructions per chunk
   constexpr int RED = WAVES * RT * MT * 256;          // floats for the final reduction
   constexpr int LDS_E = (WAVES * RING * 2 > RED * 4) ? WAVES * RING : RED * 2;
   static_assert(S >= 3 && (S - 2) * DPC <= 63, "ring depth within the vmcnt range");
@@ -156,6 +157,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  if constexpr (TG < 4 * MT) {   // zero the token rows that are never loaded, in every stage
+    constexpr int ZROWS = XROWS - 4 * TG;
+    for (int e = lane; e < S * ZROWS * 16; e += 64) {
+      const int st = e / (ZROWS * 16), rr = (e / 16) % ZROWS, ch = e % 16;
+      *reinterpret_cast<u32x4*>(lds + wave * RING + st * STAGE + (WROWS + 4 * TG + rr) * 128 + ch * 8) =
+          u32x4{0u, 0u, 0u, 0u};
+    }
+  }
   if (nc > 0) {
 #pragma unroll
     for (int c = 0; c < S - 1; ++c) issue(c);
@@ -235,7 +244,7 @@ static int stream_dma_rows(int64_t nout, int out_rows, int ty) {
 
 // One workgroup per (rows_wg output features, MT token tiles); the WAVES
 // waves split K into 128-aligned ranges of stream_dma_kw(K, WAVES).
-template <int WAVES, int MT, int RT, int S, int EPI = 0>
+template <int WAVES, int MT, int RT, int S, int EPI = 0, int TG = 4 * MT>
 static void launch_stream_dma(const void* x, const void* w, void* y, int M, int N, int K,
                               bool out_f32, hipStream_t s) {
   constexpr int OUT_ROWS = EPI == 1 ? 16 : 16 * RT;
@@ -247,12 +256,30 @@ static void launch_stream_dma(const void* x, const void* w, void* y, int M, int 
   auto Wp = static_cast<const uint16_t*>(w);
   if constexpr (EPI == 0) {
     if (out_f32)
-      hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, true, 0>), grid, block, 0, s, X, Wp, y, M, N, K, kw, rows_wg);
+      hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, true, 0, TG>), grid, block, 0, s, X, Wp, y, M, N, K, kw, rows_wg);
     else
-      hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, false, 0>), grid, block, 0, s, X, Wp, y, M, N, K, kw, rows_wg);
+      hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, false, 0, TG>), grid, block, 0, s, X, Wp, y, M, N, K, kw, rows_wg);
   } else {
-    hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, false, EPI>), grid, block, 0, s, X, Wp, y, M, N, K, kw, rows_wg);
+    hipLaunchKernelGGL((gemm_stream_dma_kernel<WAVES, MT, RT, S, false, EPI, TG>), grid, block, 0, s, X, Wp, y, M, N, K, kw, rows_wg);
   }
+}
+
+// One token tile: load only the 4-row token groups that hold a token (M <=
+// 4 TG); the other token rows of the ring are zeroed once per launch.  Rows
+// past M read as zero either way, so the sums keep their bits.  Kernel trace,
+// 8 tokens: SwiGLU on [2048, 4096] 8.36 -> 7.64 us, [8192, 3584] 12.3 -> 11.9
+// us, [1536, 4096] 12.6 -> 12.2 us; the lm_head [16032, 8192] unchanged.
+// These shapes are bound by the chain of chunk latencies of each wave (16
+// chunks of 128 k per wave at K = 4096, three in flight), not by idle CUs:
+// cutting the [1536, 4096] rows to fill all 256 CUs left it at 12.5 us.
+template <int WAVES, int RT, int S, int EPI>
+static void launch_stream_dma_tg(const void* x, const void* w, void* y, int M, int N, int K,
+                                 bool out_f32, hipStream_t s) {
+  const int tg = (M + 3) / 4;
+  if (tg == 1) launch_stream_dma<WAVES, 1, RT, S, EPI, 1>(x, w, y, M, N, K, out_f32, s);
+  else if (tg == 2) launch_stream_dma<WAVES, 1, RT, S, EPI, 2>(x, w, y, M, N, K, out_f32, s);
+  else if (tg == 3) launch_stream_dma<WAVES, 1, RT, S, EPI, 3>(x, w, y, M, N, K, out_f32, s);
+  else launch_stream_dma<WAVES, 1, RT, S, EPI, 4>(x, w, y, M, N, K, out_f32, s);
 }
 
 // Requires 4 <= M <= 64, K % 8 == 0, 16-byte aligned X and W, and M*K and
@@ -275,7 +302,7 @@ tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M,
   // [4096, 1024] 5.7 us as is (7.7 split); [7168, 8192] 35.3 -> 26.9 us and
   // [8192, 3584] 16.0 -> 12.7 us with two row tiles.
   const int64_t tiles16 = (N + 15) / 16;
-  if (mt == 1) launch_stream_dma<2, 1, 2, 4>(x, w, y, Mi, Ni, Ki, out_f32, s);
+  if (mt == 1) launch_stream_dma_tg<2, 2, 4, 0>(x, w, y, Mi, Ni, Ki, out_f32, s);
   else if (mt == 2 && 2 * tiles16 <= kStreamCUs) launch_stream_dma<3, 1, 1, 4>(x, w, y, Mi, Ni, Ki, out_f32, s);
   else if (mt == 2 && tiles16 > kStreamCUs) launch_stream_dma<3, 2, 2, 3>(x, w, y, Mi, Ni, Ki, out_f32, s);
   else if (mt == 2) launch_stream_dma<3, 2, 1, 4>(x, w, y, Mi, Ni, Ki, out_f32, s);
@@ -293,7 +320,7 @@ tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_
   const int mt = (int)((M + 15) / 16);
   const int Mi = (int)M, Ii = (int)I, Ki = (int)K;
   if (act == TP_ACT_SWIGLU) {
-    if (mt == 1) launch_stream_dma<2, 1, 2, 4, 1>(x, w, h, Mi, Ii, Ki, false, s);
+    if (mt == 1) launch_stream_dma_tg<2, 2, 4, 1>(x, w, h, Mi, Ii, Ki, false, s);
     else if (mt == 2) launch_stream_dma<3, 2, 2, 3, 1>(x, w, h, Mi, Ii, Ki, false, s);
     else if (mt == 3) launch_stream_dma<2, 3, 2, 3, 1>(x, w, h, Mi, Ii, Ki, false, s);
     else launch_stream_dma<2, 4, 2, 3, 1>(x, w, h, Mi, Ii, Ki, false, s);
