@@ -233,12 +233,18 @@ static int stream_kw(int64_t K, int waves) {
 // 16 tokens against the ring's 32.6 / 32.8 / 34.1 us.  On taller weights the
 // ring wins (lm_head 16032 x 8192 at 8 and 16 tokens: 58.6 and 59.5 us
 // against 61.0 and 75.0), and on shorter K too (8192 x 3584: 13.7 against
-// 15.4 us at 8 tokens).  The choice depends only on (M, N, K) of the weight,
-// so the fused-activation call takes the same kernel and K split as the plain
-// call on the same weight, and the two give the same bits.
+// 15.4 us at 8 tokens).  Short weights stay here too: under 64 workgroups of
+// 32 rows the ring has little data in flight, while this kernel cuts rows to
+// give every CU a workgroup of eight waves (QKV 1536 x 4096 at 4 / 8 / 16
+// tokens: 6.3 / 6.9 / 8.2 us against 12.6 / 12.3 / 12.8; 2048 x 4096, 64
+// workgroups, stays on the ring at 7.6 / 7.3 against 7.7 / 8.3 us).  The
+// choice depends only on (M, N, K) of the weight, and the fused-activation
+// call counts the same workgroups (16 gate|up pairs or 32 rows each), so it
+// takes the same kernel and K split as the plain call on the same weight, and
+// the two give the same bits.
 static bool stream_regs(int64_t M, int64_t N, int64_t K) {
   if (M <= 3) return true;
-  return M <= 16 && N <= 8192 && K / stream_waves(N, K) >= 1024;
+  return M <= 16 && N <= 8192 && (K / stream_waves(N, K) >= 1024 || (N + 31) / 32 < 64);
 }
 
 tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,

@@ -61,8 +61,10 @@ INT_SHAPES = [
     (29, 264, 4200), (20, 520, 2040),
     # LDS-ring kernel with rows per workgroup cut to fill the CUs (ragged last workgroup)
     (40, 1000, 4999), (32, 1000, 1499),
-    # LDS-ring kernel, one token tile: only the 4-token groups that hold tokens are loaded
+    # 4..16 tokens on short weights (fewer than 64 ring workgroups): register kernel
     (4, 1000, 300), (8, 4096, 1536), (13, 3584, 700),
+    # LDS-ring kernel, one token tile: only the 4-token groups that hold tokens are loaded
+    (6, 3584, 8192), (13, 1000, 2500),
     # MFMA tile path: ragged M/N/K, each tile shape
     (65, 64, 16), (200, 136, 130), (300, 520, 300), (512, 264, 640), (4000, 264, 4000),
     (4096, 200, 2048), (4000, 136, 5100),   # the last picks 256x320 tiles
