@@ -57,18 +57,27 @@ def traffic_source_hash(files):
     return h.hexdigest()[:16]
 
 
+def profile_data(name):
+    """The DATA line of a committed rocprofv3 summary (a JSON object), or None
+    if the summary or its DATA line is missing."""
+    path = os.path.join(ROOT, "profiles", name)
+    try:
+        line = [l for l in open(path) if l.startswith("DATA ")][0]
+        return json.loads(line[5:])
+    except (OSError, IndexError, ValueError):
+        return None
+
+
 def recorded_profile(name):
     """The DATA line of a committed rocprofv3 summary of the dominant kernel
     (HBM traffic from FETCH_SIZE/WRITE_SIZE scaled by a plain copy of known
     size; MFMA and LDS counters), or None once the kernel's sources no longer
     match the hash recorded with the counters."""
-    path = os.path.join(ROOT, "profiles", name)
+    data = profile_data(name)
     try:
-        line = [l for l in open(path) if l.startswith("DATA ")][0]
-        data = json.loads(line[5:])
-        if traffic_source_hash(data["sources"]) != data["sources_sha256_16"]:
+        if data is None or traffic_source_hash(data["sources"]) != data["sources_sha256_16"]:
             return None
-    except (OSError, IndexError, KeyError, ValueError):
+    except (OSError, KeyError, TypeError):
         return None
     return data
 
@@ -112,7 +121,7 @@ def prefill_setup():
     # every rank's partials once (rank 1's stay as the all-reduce contribution)
     for r in range(R):
         shards[r].attn_partial(X, pa[r])
-    h = tpl.reduce_partials(pa, residual=X)
+    h = tpl.reduce_partials(pa, residual=X, out_dtype=torch.float32)   # float32 residual stream
     for r in range(R):
         shards[r].mlp_partial(h, pm[r])
     y = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
@@ -136,12 +145,13 @@ def prefill_counts(c):
         "qkv": (S * H + nqkv * H + S * nqkv) * b2,
         "attention": S * nqkv * b2 + S * hq * D * b2,
         "o_proj": (S * hq * D + H * hq * D) * b2 + S * H * b4,
-        # partials + residual read, h and RMSNorm(h) written
-        "reduce1_rmsnorm2": R * S * H * b4 + 3 * S * H * b2 + H * b2,
+        # partials + bf16 residual x read, float32 h and bf16 RMSNorm(h) written
+        "reduce1_rmsnorm2": R * S * H * b4 + S * H * b2 + S * H * b4 + S * H * b2 + H * b2,
         # activation in the epilogue: only h = act(g) * u ([S, il]) is written
         "gate_up_swiglu": (S * H + 2 * il * H + S * il) * b2,
         "down": (S * il + H * il) * b2 + S * H * b4,
-        "reduce2": R * S * H * b4 + 2 * S * H * b2,
+        # partials + float32 h read, bf16 y written
+        "reduce2": R * S * H * b4 + S * H * b4 + S * H * b2,
     }
     return gemm, flops, byts
 

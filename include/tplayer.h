@@ -108,10 +108,12 @@ tp_status tp_swiglu_local(const void* gate, const void* up, void* h,
  * Column-parallel linear with the rank-local activation fused into its
  * epilogue (P1 "MLP 里的 tensor parallel": gate_i and up_i are both local to
  * rank i, so activation(gate_i) * up_i needs no exchange; P2 section 二: GELU
- * directly after the column-parallel fc1).  The result equals tp_column_linear
- * followed by tp_swiglu_local bit for bit (the products are rounded to bf16
- * before the activation, as the unfused path stores them), without writing
- * the [M, 2I] gate|up intermediate:
+ * directly after the column-parallel fc1).  The activation is applied to the
+ * float32 sums of the projection, so the gate and up products are never
+ * rounded and the [M, 2I] gate|up intermediate never reaches memory; only h
+ * is rounded to bf16.  (tp_column_linear followed by tp_swiglu_local stores
+ * g and u as bf16 first, so the two routes agree to bf16 rounding of g and u,
+ * not bit for bit.)
  *     TP_ACT_SWIGLU: h[m, i] = act(x . w[i, :], x . w[I + i, :])   w: [2I, K]
  *                    (gate rows, then the matching up rows)
  *     TP_ACT_GELU:   h[m, i] = gelu(x . w[i, :])                    w: [I, K]
@@ -201,40 +203,50 @@ tp_status tp_decode_attention_append(const void* q, const int64_t qs[2],
  * Parallel Linear": the partial outputs are summed; P2 section 二
  * all_reduce(output); P3: partials must be summed, not concatenated),
  * emulated on one GPU as an in-HBM sum of every rank's partial:
- *     y[m, n] = (residual[m, n] if residual) + sum_{r=0}^{R-1} partials[r][m, n]
+ *     y[m, n] = sum_{r=0}^{R-1} partials[r][m, n] (+ residual[m, n])
  * summed in float32 in rank order 0..R-1, the residual added last, then
- * stored as out_dt.
+ * rounded once to out_dt.
  *   partials : host array of R device pointers to [M, N] float32 buffers
- *   residual : [M, N] out_dt or NULL
- *   y        : [M, N] out_dt (may alias residual)
+ *   residual : [M, N] in res_dt, or NULL (res_dt is then ignored).  A
+ *              residual stream kept in float32 is passed with res_dt = TP_F32
+ *              while y is bf16, and the other way round.
+ *   y        : [M, N] out_dt.  y may be the residual buffer itself when
+ *              res_dt == out_dt; any other overlap of the two is TP_ERR_SHAPE.
  *   1 <= R <= 16
  */
 tp_status tp_reduce_partials(const float* const* partials, int64_t R,
-                             const void* residual, void* y,
+                             const void* residual, tp_dtype res_dt, void* y,
                              int64_t M, int64_t N, tp_dtype out_dt, void* stream);
 
 /*
  * The all-reduce's arithmetic followed by the next sub-block's pre-norm, in
  * one pass (P2 section 二 all_reduce(output) + the residual; the RMSNorm is
  * the standard pre-norm of a decoder layer, not on the source pages):
- *     y  = (residual if residual) + sum_{r=0}^{R-1} partials[r]   (as tp_reduce_partials)
- *     yn = y * rsqrt(mean_n y^2 + eps) * gamma                   (as tp_rmsnorm on the stored y)
- * Both outputs equal the two unfused calls bit for bit.
+ *     y  = sum_{r=0}^{R-1} partials[r] (+ residual)     (as tp_reduce_partials,
+ *                                                       stored as y_dt)
+ *     yn = y * rsqrt(mean_n y^2 + eps) * gamma          (as tp_rmsnorm on the
+ *                                                       stored y)
+ * Both outputs equal the two unfused calls bit for bit.  In a pre-norm layer
+ * y is the residual stream h (kept in float32 with y_dt = TP_F32, it is never
+ * rounded) and yn the normalised input of the next column-parallel GEMM.
  *   partials : host array of R device pointers to [M, N] float32 buffers
- *   residual : [M, N] dt or NULL;  y, yn : [M, N] dt (y may alias residual);
- *   gamma : [N] dt;  1 <= R <= 16
+ *   residual : [M, N] in res_dt, or NULL;  y : [M, N] in y_dt (may be the
+ *   residual buffer itself when res_dt == y_dt; other overlaps TP_ERR_SHAPE);
+ *   gamma : [N] dt;  yn : [M, N] dt;  1 <= R <= 16
  */
 tp_status tp_reduce_partials_rmsnorm(const float* const* partials, int64_t R,
-                                     const void* residual, void* y, const void* gamma, void* yn,
+                                     const void* residual, tp_dtype res_dt,
+                                     void* y, tp_dtype y_dt, const void* gamma, void* yn,
                                      int64_t M, int64_t N, float eps, tp_dtype dt, void* stream);
 
 /*
  * Replicated pre-norm RMSNorm (every rank normalises the full hidden row):
  *     y[m, :] = x[m, :] * rsqrt(mean_n x[m, n]^2 + eps) * gamma[:]
- * in float32 arithmetic.  x, gamma, y in dtype dt; x, y are [M, N].
+ * in float32 arithmetic.  x : [M, N] in x_dt (a float32 residual stream may
+ * feed a bf16 normalisation); gamma : [N] and y : [M, N] in dt.
  * Not on the source pages (a standard pre-norm layer's normalisation).
  */
-tp_status tp_rmsnorm(const void* x, const void* gamma, void* y,
+tp_status tp_rmsnorm(const void* x, tp_dtype x_dt, const void* gamma, void* y,
                      int64_t M, int64_t N, float eps, tp_dtype dt, void* stream);
 
 /*

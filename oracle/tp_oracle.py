@@ -44,7 +44,7 @@ import numpy as np
 from scipy.special import erfc as _erfc
 
 __all__ = [
-    "round_bf16", "linear", "column_shard", "row_shard", "input_shard",
+    "round_bf16", "bf16_storage", "STORED", "linear", "column_shard", "row_shard", "input_shard",
     "column_linear", "row_linear_partial", "reduce_partials", "concat_columns",
     "silu", "gelu", "local_activation", "rmsnorm", "attention", "qkv_shard",
     "kv_heads_of_rank", "kv_cache_bytes_per_rank", "vocab_argmax_local", "vocab_argmax_reduce",
@@ -55,8 +55,9 @@ __all__ = [
 ]
 
 
-def _identity(a):
-    return a
+def _exact(name: str, a):
+    """The default storage policy: every intermediate is kept exactly."""
+    return np.asarray(a, np.float64)
 
 
 # ---------------------------------------------------------------------------
@@ -72,6 +73,30 @@ def round_bf16(a) -> np.ndarray:
     a = np.asarray(a, dtype=np.float64)
     m, e = np.frexp(a)
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+# Named intermediates of the layer, in the order the layer produces them:
+# xn (first pre-norm), qkv (the projections q, k, v), o (attention output),
+# h (the residual stream after the attention sub-block), hn (second pre-norm),
+# gu (the gate/up or fc1 projections), a (the activation).
+STORED = ("xn", "qkv", "o", "h", "hn", "gu", "a")
+
+
+def bf16_storage(*names):
+    """A storage policy for the diagnostic mode: the named intermediates
+    (default: all of ``STORED``) are rounded to bfloat16 where an
+    implementation stores them, every other one is kept exactly.  A policy is
+    called as ``store(name, value)``."""
+    chosen = frozenset(names or STORED)
+    unknown = chosen - set(STORED)
+    if unknown:
+        raise ValueError(f"unknown intermediates {sorted(unknown)}")
+
+    def store(name: str, a):
+        if name not in STORED:
+            raise ValueError(f"unknown intermediate {name!r}")
+        return round_bf16(a) if name in chosen else np.asarray(a, np.float64)
+    return store
 
 
 # ---------------------------------------------------------------------------
@@ -364,15 +389,15 @@ def mlp_unsharded(x, w_in, w_out, act: str, w_up=None):
 
 
 def mlp_rank_partial(x, w_in, w_out, act: str, r: int, R: int, w_up=None,
-                     store=_identity):
+                     store=_exact):
     """Rank r's MLP share: column-parallel gate/up (or fc1), the local
     activation on the rank's intermediate slice, row-parallel down (or fc2)
-    giving the rank's partial of the hidden output.  ``store`` is applied where
-    an implementation keeps an intermediate in its storage type."""
-    g = store(column_linear(x, column_shard(w_in, r, R)))
-    u = store(column_linear(x, column_shard(w_up, r, R))) if act == "swiglu" else None
-    h = store(local_activation(g, u, act))
-    return row_linear_partial(h, row_shard(w_out, r, R))
+    giving the rank's partial of the hidden output.  ``store`` (a policy from
+    ``bf16_storage``) is applied to the named intermediates ``gu`` and ``a``."""
+    g = store("gu", column_linear(x, column_shard(w_in, r, R)))
+    u = store("gu", column_linear(x, column_shard(w_up, r, R))) if act == "swiglu" else None
+    a = store("a", local_activation(g, u, act))
+    return row_linear_partial(a, row_shard(w_out, r, R))
 
 
 # ---------------------------------------------------------------------------
@@ -400,7 +425,7 @@ def attention_block_unsharded(x, wq, wk, wv, wo, head_dim: int, causal: bool = T
 
 
 def attention_rank_partial(x, wq, wk, wv, wo, head_dim: int, r: int, R: int,
-                           causal: bool = True, rows=None, store=_identity):
+                           causal: bool = True, rows=None, store=_exact):
     """Rank r's attention share: its fused QKV slice (column-parallel), local
     attention over its q heads and their KV heads, its o_proj input block
     (row-parallel) giving a partial of the hidden output."""
@@ -409,12 +434,12 @@ def attention_rank_partial(x, wq, wk, wv, wo, head_dim: int, r: int, R: int,
     hq, hkv = n_q // R, len(kv_heads_of_rank(n_q, n_kv, r, R))
     wqkv = qkv_shard(wq, wk, wv, r, R, head_dim)
     dq, dkv = hq * head_dim, hkv * head_dim
-    kv = store(column_linear(x, wqkv[dq:, :]))
+    kv = store("qkv", column_linear(x, wqkv[dq:, :]))
     k = _split_heads(kv[:, :dkv], hkv, head_dim)
     v = _split_heads(kv[:, dkv:], hkv, head_dim)
     rows = np.arange(S) if rows is None else np.asarray(rows)
-    q = _split_heads(store(column_linear(x[rows], wqkv[:dq, :])), hq, head_dim)
-    o = store(attention(q, k, v, causal=causal, q_pos=rows))
+    q = _split_heads(store("qkv", column_linear(x[rows], wqkv[:dq, :])), hq, head_dim)
+    o = store("o", attention(q, k, v, causal=causal, q_pos=rows))
     return row_linear_partial(o.reshape(len(rows), dq), row_shard(wo, r, R))
 
 
@@ -433,7 +458,7 @@ def layer_unsharded(x, p: dict, head_dim: int, eps: float, act: str = "swiglu",
 
 
 def layer_sharded(x, p: dict, head_dim: int, eps: float, R: int, act: str = "swiglu",
-                  rows=None, store=_identity):
+                  rows=None, store=_exact):
     """The same layer computed the tensor-parallel way: every rank's attention
     partial, their sum plus the residual, every rank's MLP partial on the
     normalised sum, their sum plus the residual (two all-reduces per layer:
@@ -441,12 +466,12 @@ def layer_sharded(x, p: dict, head_dim: int, eps: float, R: int, act: str = "swi
     ``(y, h, attn_partials, mlp_partials)`` at ``rows``."""
     x = np.asarray(x, np.float64)
     rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
-    xn = store(rmsnorm(x, p["g1"], eps))
+    xn = store("xn", rmsnorm(x, p["g1"], eps))
     pa = [attention_rank_partial(xn, p["wq"], p["wk"], p["wv"], p["wo"], head_dim,
                                  r, R, causal=True, rows=rows, store=store)
           for r in range(R)]
-    h = store(reduce_partials(pa, residual=x[rows]))
-    hn = store(rmsnorm(h, p["g2"], eps))
+    h = store("h", reduce_partials(pa, residual=x[rows]))
+    hn = store("hn", rmsnorm(h, p["g2"], eps))
     pm = [mlp_rank_partial(hn, p["wg"], p["wd"], act, r, R, w_up=p.get("wu"),
                            store=store) for r in range(R)]
     y = reduce_partials(pm, residual=h)

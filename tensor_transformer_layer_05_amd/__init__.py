@@ -59,11 +59,13 @@ _SIGS = {
     "tp_local_attention_workspace": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "tp_kv_append": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i64,
                                     ctypes.c_int, _vp]),
-    "tp_reduce_partials": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, _vp, _vp, _i64, _i64,
-                                          ctypes.c_int, _vp]),
-    "tp_reduce_partials_rmsnorm": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, _vp, _vp, _vp, _vp,
-                                                  _i64, _i64, ctypes.c_float, ctypes.c_int, _vp]),
-    "tp_rmsnorm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, ctypes.c_float, ctypes.c_int, _vp]),
+    "tp_reduce_partials": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, _vp, ctypes.c_int, _vp, _i64,
+                                          _i64, ctypes.c_int, _vp]),
+    "tp_reduce_partials_rmsnorm": (ctypes.c_int, [ctypes.POINTER(_vp), _i64, _vp, ctypes.c_int, _vp,
+                                                  ctypes.c_int, _vp, _vp, _i64, _i64, ctypes.c_float,
+                                                  ctypes.c_int, _vp]),
+    "tp_rmsnorm": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _i64, _i64, ctypes.c_float,
+                                  ctypes.c_int, _vp]),
     "tp_paged_attention_decode": (ctypes.c_int, [_vp, _i64p, _vp, _vp, _i64p, _i64, _vp, _i64, _vp,
                                                  _i64, _i64, _vp, _i64p, _i64, _i64, _i64, _i64,
                                                  ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t,
@@ -305,16 +307,7 @@ def _new_rows(k_new, v_new):
     return B, H, D
 
 
-def decode_attention_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
-                            k_cache: torch.Tensor, v_cache: torch.Tensor, pos: int,
-                            scale: float | None = None, out: torch.Tensor | None = None,
-                            workspace: torch.Tensor | None = None):
-    """One decode step in one launch: store k_new/v_new (``[B, Hkv, D]``
-    views with a shared row stride) at key position ``pos`` of the caches
-    (``[B, T, Hkv, D]``, any strides, last dim contiguous) and attend q
-    (``[B, Hq, D]``) over keys ``0..pos``.  The same bits as ``kv_append``
-    followed by ``local_attention`` with ``Skv = pos + 1``.  Returns o
-    ``[B, Hq, D]``."""
+def _decode_append_args(q, k_new, v_new, k_cache, v_cache, pos, scale, out):
     _dev(q, "q")
     if q.dim() != 3 or q.stride(2) != 1:
         raise ValueError("q must be [B, Hq, D] with a contiguous last dimension")
@@ -332,22 +325,35 @@ def decode_attention_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
         raise ValueError("out must be [B, Hq, D] with a contiguous last dimension")
     if scale is None:
         scale = 1.0 / (D ** 0.5)
-    need = local_attention_workspace(B, 1, pos + 1, Hq, H, D)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     qs = (ctypes.c_int64 * 2)(q.stride(0), q.stride(1))
     os_ = (ctypes.c_int64 * 2)(out.stride(0), out.stride(1))
     cs = _arr3([k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)])
+    args = (q.data_ptr(), qs, k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_cache.data_ptr(),
+            v_cache.data_ptr(), cs, k_cache.shape[1], pos, out.data_ptr(), os_, B, Hq, H, D,
+            float(scale), _DT[q.dtype])
+    return out, args, (B, Hq, H, D)
+
+
+def decode_attention_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            k_cache: torch.Tensor, v_cache: torch.Tensor, pos: int,
+                            scale: float | None = None, out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None):
+    """One decode step in one launch: store k_new/v_new (``[B, Hkv, D]``
+    views with a shared row stride) at key position ``pos`` of the caches
+    (``[B, T, Hkv, D]``, any strides, last dim contiguous) and attend q
+    (``[B, Hq, D]``) over keys ``0..pos``.  The same bits as ``kv_append``
+    followed by ``local_attention`` with ``Skv = pos + 1``.  Returns o
+    ``[B, Hq, D]``."""
+    out, args, (B, Hq, H, D) = _decode_append_args(q, k_new, v_new, k_cache, v_cache, pos, scale, out)
+    need = local_attention_workspace(B, 1, pos + 1, Hq, H, D)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check("tp_decode_attention_append", lib().tp_decode_attention_append(
-        q.data_ptr(), qs, k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_cache.data_ptr(),
-        v_cache.data_ptr(), cs, k_cache.shape[1], pos, out.data_ptr(), os_, B, Hq, H, D,
-        float(scale), _DT[q.dtype], workspace.data_ptr() if need else None, need, _stream(q)))
+        *args, workspace.data_ptr() if need else None, need, _stream(q)))
     return out
 
 
-def reduce_partials(partials, residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                    out_dtype: torch.dtype | None = None):
-    """``y = residual + sum_r partials[r]`` in rank order (float32 sums)."""
+def _partials(partials):
     parts = list(partials)
     if not parts:
         raise ValueError("need at least one partial")
@@ -355,69 +361,86 @@ def reduce_partials(partials, residual: torch.Tensor | None = None, out: torch.T
         _contig(p, f"partials[{i}]")
         if p.dtype != torch.float32 or p.shape != parts[0].shape:
             raise ValueError("partials must be float32 tensors of one shape")
+    return parts
+
+
+def reduce_partials(partials, residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    out_dtype: torch.dtype | None = None):
+    """``y = sum_r partials[r] + residual`` in rank order (float32 sums, the
+    residual added last).  The residual may be bf16 or float32 whatever the
+    output dtype; ``out`` may be the residual tensor itself when the two share
+    a dtype."""
+    parts = _partials(partials)
     M, N = parts[0].shape
     if out is None:
         dt = out_dtype or (residual.dtype if residual is not None else torch.float32)
         out = torch.empty((M, N), dtype=dt, device=parts[0].device)
     _contig(out, "out")
+    if out.shape != (M, N):
+        raise ValueError("out must be [M, N]")
     if residual is not None:
         _contig(residual, "residual")
-        if residual.dtype != out.dtype or residual.shape != out.shape:
-            raise ValueError("residual must match out")
+        if residual.shape != (M, N):
+            raise ValueError("residual must be [M, N]")
     arr = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
     _check("tp_reduce_partials", lib().tp_reduce_partials(
-        arr, len(parts), residual.data_ptr() if residual is not None else None, out.data_ptr(),
-        M, N, _DT[out.dtype], _stream(parts[0])))
+        arr, len(parts), residual.data_ptr() if residual is not None else None,
+        _DT[residual.dtype] if residual is not None else F32, out.data_ptr(), M, N,
+        _DT[out.dtype], _stream(parts[0])))
     return out
 
 
 def reduce_partials_rmsnorm(partials, gamma: torch.Tensor, residual: torch.Tensor | None = None,
                             eps: float = 1e-5, out: torch.Tensor | None = None,
-                            out_norm: torch.Tensor | None = None):
-    """``y = residual + sum_r partials[r]`` (as ``reduce_partials``) and
+                            out_norm: torch.Tensor | None = None,
+                            out_dtype: torch.dtype | None = None):
+    """``y = sum_r partials[r] + residual`` (as ``reduce_partials``) and
     ``yn = rmsnorm(y) * gamma`` (as ``rmsnorm`` on the stored y) in one pass.
-    Returns ``(y, yn)`` in gamma's dtype."""
-    parts = list(partials)
-    if not parts:
-        raise ValueError("need at least one partial")
-    for i, p in enumerate(parts):
-        _contig(p, f"partials[{i}]")
-        if p.dtype != torch.float32 or p.shape != parts[0].shape:
-            raise ValueError("partials must be float32 tensors of one shape")
+    ``yn`` has gamma's dtype; ``y`` has ``out``'s dtype, else ``out_dtype``,
+    else gamma's (float32 keeps the residual stream unrounded).  Returns
+    ``(y, yn)``."""
+    parts = _partials(partials)
     M, N = parts[0].shape
     _contig(gamma, "gamma")
     dt = gamma.dtype
     if gamma.shape != (N,):
         raise ValueError("gamma must be [N]")
     if out is None:
-        out = torch.empty((M, N), dtype=dt, device=parts[0].device)
+        out = torch.empty((M, N), dtype=out_dtype or dt, device=parts[0].device)
     if out_norm is None:
         out_norm = torch.empty((M, N), dtype=dt, device=parts[0].device)
-    for t, n in ((out, "out"), (out_norm, "out_norm")):
-        _contig(t, n)
-        if t.dtype != dt or t.shape != (M, N):
-            raise ValueError(f"{n} must be [M, N] with gamma's dtype")
+    _contig(out, "out")
+    _contig(out_norm, "out_norm")
+    if out.shape != (M, N):
+        raise ValueError("out must be [M, N]")
+    if out_norm.dtype != dt or out_norm.shape != (M, N):
+        raise ValueError("out_norm must be [M, N] with gamma's dtype")
     if residual is not None:
         _contig(residual, "residual")
-        if residual.dtype != dt or residual.shape != (M, N):
-            raise ValueError("residual must be [M, N] with gamma's dtype")
+        if residual.shape != (M, N):
+            raise ValueError("residual must be [M, N]")
     arr = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
     _check("tp_reduce_partials_rmsnorm", lib().tp_reduce_partials_rmsnorm(
-        arr, len(parts), residual.data_ptr() if residual is not None else None, out.data_ptr(),
+        arr, len(parts), residual.data_ptr() if residual is not None else None,
+        _DT[residual.dtype] if residual is not None else F32, out.data_ptr(), _DT[out.dtype],
         gamma.data_ptr(), out_norm.data_ptr(), M, N, float(eps), _DT[dt], _stream(parts[0])))
     return out, out_norm
 
 
 def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, out: torch.Tensor | None = None):
+    """``y = x * rsqrt(mean(x^2) + eps) * gamma`` per row; y has gamma's dtype
+    (x may be a float32 residual stream with bf16 gamma)."""
     _contig(x, "x"); _contig(gamma, "gamma")
     M, N = x.shape
-    if gamma.shape != (N,) or gamma.dtype != x.dtype:
-        raise ValueError("gamma must be [N] with the dtype of x")
+    if gamma.shape != (N,):
+        raise ValueError("gamma must be [N]")
     if out is None:
-        out = torch.empty_like(x)
+        out = torch.empty((M, N), dtype=gamma.dtype, device=x.device)
     _contig(out, "out")
-    _check("tp_rmsnorm", lib().tp_rmsnorm(x.data_ptr(), gamma.data_ptr(), out.data_ptr(), M, N,
-                                          float(eps), _DT[x.dtype], _stream(x)))
+    if out.dtype != gamma.dtype or out.shape != (M, N):
+        raise ValueError("out must be [M, N] with gamma's dtype")
+    _check("tp_rmsnorm", lib().tp_rmsnorm(x.data_ptr(), _DT[x.dtype], gamma.data_ptr(), out.data_ptr(),
+                                          M, N, float(eps), _DT[gamma.dtype], _stream(x)))
     return out
 
 

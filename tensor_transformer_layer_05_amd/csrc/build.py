@@ -30,7 +30,7 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics", "-Wall", "-Wno-unused-variable",
+    "-Wall", "-Wno-unused-variable",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

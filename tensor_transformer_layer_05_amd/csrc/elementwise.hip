@@ -100,13 +100,54 @@ tp_status act_local(const void* g, const void* u, void* h, int64_t M, int64_t I,
   return TP_OK;
 }
 
+// ---- 8-element row chunks in either storage type ------------------------------
+
+template <bool F32>
+__device__ __forceinline__ void load8(const void* base, int64_t off, float* f) {
+  if constexpr (F32) {
+    const float* p = static_cast<const float*>(base) + off;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = a[i];
+      f[4 + i] = b[i];
+    }
+  } else {
+    unpack8(*reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off), f);
+  }
+}
+
+// Stores 8 values and replaces them by what was stored (the bf16 rounding).
+template <bool F32>
+__device__ __forceinline__ void store8(void* base, int64_t off, float* f) {
+  if constexpr (F32) {
+    float* p = static_cast<float*>(base) + off;
+    *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+  } else {
+    const u32x4 b = pack8(f);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + off) = b;
+    unpack8(b, f);
+  }
+}
+
+__device__ __forceinline__ float load1(const void* base, int64_t i, bool f32) {
+  return f32 ? static_cast<const float*>(base)[i] : bf2f(static_cast<const uint16_t*>(base)[i]);
+}
+
+// Residual operand of the sums: none, bfloat16 or float32 storage.
+enum { kResNone = 0, kResBf16 = 1, kResF32 = 2 };
+
 // ---- sum of rank partials --------------------------------------------------
 
 struct PartialPtrs {
   const float* p[16];
 };
 
-template <bool BF16, bool VEC>
+// y = sum_r P[r] (+ residual): float32 sums in rank order 0..R-1, the residual
+// added last, one rounding to y's storage type.
+template <int RES, bool OUT_BF16, bool VEC>
 __global__ __launch_bounds__(256) void reduce_kernel(PartialPtrs P, int R,
                                                      const void* __restrict__ residual,
                                                      void* __restrict__ y, int64_t total) {
@@ -116,74 +157,82 @@ __global__ __launch_bounds__(256) void reduce_kernel(PartialPtrs P, int R,
     for (int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v < nv; v += stride) {
       f32x4 acc = *reinterpret_cast<const f32x4*>(P.p[0] + 4 * v);
       for (int r = 1; r < R; ++r) acc += *reinterpret_cast<const f32x4*>(P.p[r] + 4 * v);
-      if constexpr (BF16) {
-        if (residual) {
-          const u32x2 rv = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(residual) + 4 * v);
-          acc[0] += bf_lo(rv[0]); acc[1] += bf_hi(rv[0]);
-          acc[2] += bf_lo(rv[1]); acc[3] += bf_hi(rv[1]);
-        }
+      if constexpr (RES == kResBf16) {
+        const u32x2 rv = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(residual) + 4 * v);
+        acc[0] += bf_lo(rv[0]); acc[1] += bf_hi(rv[0]);
+        acc[2] += bf_lo(rv[1]); acc[3] += bf_hi(rv[1]);
+      } else if constexpr (RES == kResF32) {
+        acc += *reinterpret_cast<const f32x4*>(static_cast<const float*>(residual) + 4 * v);
+      }
+      if constexpr (OUT_BF16)
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + 4 * v) =
             u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
-      } else {
-        if (residual) acc += *reinterpret_cast<const f32x4*>(static_cast<const float*>(residual) + 4 * v);
+      else
         *reinterpret_cast<f32x4*>(static_cast<float*>(y) + 4 * v) = acc;
-      }
     }
   } else {
     for (int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v < total; v += stride) {
       float acc = P.p[0][v];
       for (int r = 1; r < R; ++r) acc += P.p[r][v];
-      if constexpr (BF16) {
-        if (residual) acc += bf2f(static_cast<const uint16_t*>(residual)[v]);
+      if constexpr (RES != kResNone) acc += load1(residual, v, RES == kResF32);
+      if constexpr (OUT_BF16)
         static_cast<uint16_t*>(y)[v] = (uint16_t)f2bf_bits(acc);
-      } else {
-        if (residual) acc += static_cast<const float*>(residual)[v];
+      else
         static_cast<float*>(y)[v] = acc;
-      }
     }
   }
 }
 
-tp_status reduce_partials(const float* const* partials, int R, const void* residual, void* y,
+template <int RES>
+static void launch_reduce(const PartialPtrs& P, int R, const void* residual, void* y,
                           int64_t total, bool bf16, bool vec, hipStream_t s) {
-  PartialPtrs P = {};
-  for (int r = 0; r < R; ++r) P.p[r] = partials[r];
   const unsigned gr = grid_for(vec ? total / 4 : total);
   if (bf16) {
-    if (vec) hipLaunchKernelGGL((reduce_kernel<true, true>), dim3(gr), dim3(256), 0, s, P, R, residual, y, total);
-    else hipLaunchKernelGGL((reduce_kernel<true, false>), dim3(gr), dim3(256), 0, s, P, R, residual, y, total);
+    if (vec) hipLaunchKernelGGL((reduce_kernel<RES, true, true>), dim3(gr), dim3(256), 0, s, P, R, residual, y, total);
+    else hipLaunchKernelGGL((reduce_kernel<RES, true, false>), dim3(gr), dim3(256), 0, s, P, R, residual, y, total);
   } else {
-    if (vec) hipLaunchKernelGGL((reduce_kernel<false, true>), dim3(gr), dim3(256), 0, s, P, R, residual, y, total);
-    else hipLaunchKernelGGL((reduce_kernel<false, false>), dim3(gr), dim3(256), 0, s, P, R, residual, y, total);
+    if (vec) hipLaunchKernelGGL((reduce_kernel<RES, false, true>), dim3(gr), dim3(256), 0, s, P, R, residual, y, total);
+    else hipLaunchKernelGGL((reduce_kernel<RES, false, false>), dim3(gr), dim3(256), 0, s, P, R, residual, y, total);
   }
+}
+
+tp_status reduce_partials(const float* const* partials, int R, const void* residual, bool res_f32,
+                          void* y, int64_t total, bool bf16, bool vec, hipStream_t s) {
+  PartialPtrs P = {};
+  for (int r = 0; r < R; ++r) P.p[r] = partials[r];
+  if (!residual) launch_reduce<kResNone>(P, R, residual, y, total, bf16, vec, s);
+  else if (res_f32) launch_reduce<kResF32>(P, R, residual, y, total, bf16, vec, s);
+  else launch_reduce<kResBf16>(P, R, residual, y, total, bf16, vec, s);
   TPL_LAUNCH_CHECK("reduce_partials");
   return TP_OK;
 }
 
 // ---- RMSNorm -----------------------------------------------------------------
 
-// One 256-thread workgroup per row.  Sum of squares in fp32: per-thread partial
-// sums, a wave reduction, then the 4 wave sums in wave order.
-template <bool BF16, bool VEC>
+// One 256-thread workgroup per row; x in float32 (XF32) or in the output type,
+// gamma and y in the output type (bf16 when BF16).  Sum of squares in fp32:
+// per-thread partial sums (the vector path: chunks of 8 consecutive elements
+// at a stride of 2048, each chunk in order), a wave reduction, then the 4
+// wave sums in wave order.
+template <bool XF32, bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x,
                                                       const void* __restrict__ gamma,
                                                       void* __restrict__ y, int64_t N, float eps) {
+  static_assert(!VEC || BF16, "the vector path stores bf16");
   __shared__ float wsum[4];
   const int64_t m = blockIdx.x;
   const int tid = threadIdx.x;
   float ss = 0.f;
-  if constexpr (BF16 && VEC) {
-    const uint16_t* xr = static_cast<const uint16_t*>(x) + m * N;
+  if constexpr (VEC) {
     for (int64_t c = tid * 8; c < N; c += 256 * 8) {
       float f[8];
-      unpack8(*reinterpret_cast<const u32x4*>(xr + c), f);
+      load8<XF32>(x, m * N + c, f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
     }
   } else {
     for (int64_t c = tid; c < N; c += 256) {
-      const float f = BF16 ? bf2f(static_cast<const uint16_t*>(x)[m * N + c])
-                           : static_cast<const float*>(x)[m * N + c];
+      const float f = load1(x, m * N + c, XF32);
       ss = fmaf(f, f, ss);
     }
   }
@@ -192,58 +241,56 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x
   __syncthreads();
   const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
   const float inv = rsqrtf(tot / (float)N + eps);
-  if constexpr (BF16 && VEC) {
-    const uint16_t* xr = static_cast<const uint16_t*>(x) + m * N;
+  if constexpr (VEC) {
     const uint16_t* gr = static_cast<const uint16_t*>(gamma);
-    uint16_t* yr = static_cast<uint16_t*>(y) + m * N;
     for (int64_t c = tid * 8; c < N; c += 256 * 8) {
       float f[8], gm[8], o[8];
-      unpack8(*reinterpret_cast<const u32x4*>(xr + c), f);
+      load8<XF32>(x, m * N + c, f);
       unpack8(*reinterpret_cast<const u32x4*>(gr + c), gm);
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] = f[i] * inv * gm[i];
-      *reinterpret_cast<u32x4*>(yr + c) = pack8(o);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + m * N + c) = pack8(o);
     }
   } else {
     for (int64_t c = tid; c < N; c += 256) {
-      if constexpr (BF16) {
-        const float f = bf2f(static_cast<const uint16_t*>(x)[m * N + c]);
-        const float gm = bf2f(static_cast<const uint16_t*>(gamma)[c]);
+      const float f = load1(x, m * N + c, XF32);
+      const float gm = load1(gamma, c, !BF16);
+      if constexpr (BF16)
         static_cast<uint16_t*>(y)[m * N + c] = (uint16_t)f2bf_bits(f * inv * gm);
-      } else {
-        const float f = static_cast<const float*>(x)[m * N + c];
-        const float gm = static_cast<const float*>(gamma)[c];
+      else
         static_cast<float*>(y)[m * N + c] = f * inv * gm;
-      }
     }
   }
 }
 
-// Rows of at most 8 x 2048 bf16 elements: the same arithmetic in the same order
-// as rmsnorm_kernel<true, true>, with the row held in registers between the
-// two passes and every load of the row issued before the first use.
-template <int CH>
-__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const uint16_t* __restrict__ x,
+// Rows of at most 8 x 2048 elements, bf16 gamma and y: the same arithmetic in
+// the same order as rmsnorm_kernel's vector path, with the row held in
+// registers between the two passes and every load of the row issued before
+// the first use.
+template <int CH, bool XF32>
+__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const void* __restrict__ x,
                                                           const uint16_t* __restrict__ gamma,
                                                           uint16_t* __restrict__ y, int64_t N, float eps) {
   __shared__ float wsum[4];
   const int64_t m = blockIdx.x;
   const int tid = threadIdx.x;
-  const uint16_t* xr = x + m * N;
-  u32x4 xv[CH];
+  float xv[CH][8];
 #pragma unroll
   for (int k = 0; k < CH; ++k) {
     const int64_t c = tid * 8 + k * 2048;
-    xv[k] = c < N ? *reinterpret_cast<const u32x4*>(xr + c) : u32x4{0u, 0u, 0u, 0u};
+    if (c < N) {
+      load8<XF32>(x, m * N + c, xv[k]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xv[k][i] = 0.f;
+    }
   }
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < CH; ++k) {
     if (tid * 8 + k * 2048 < N) {
-      float f[8];
-      unpack8(xv[k], f);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+      for (int i = 0; i < 8; ++i) ss = fmaf(xv[k][i], xv[k][i], ss);
     }
   }
   ss = wave_sum(ss);
@@ -255,44 +302,52 @@ __global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const uint16_t* __rest
   for (int k = 0; k < CH; ++k) {
     const int64_t c = tid * 8 + k * 2048;
     if (c < N) {
-      float f[8], gm[8], o[8];
-      unpack8(xv[k], f);
+      float gm[8], o[8];
       unpack8(*reinterpret_cast<const u32x4*>(gamma + c), gm);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = f[i] * inv * gm[i];
+      for (int i = 0; i < 8; ++i) o[i] = xv[k][i] * inv * gm[i];
       *reinterpret_cast<u32x4*>(y + m * N + c) = pack8(o);
     }
   }
 }
 
-tp_status rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t N, float eps,
-                  bool bf16, bool vec, hipStream_t s) {
+template <bool XF32>
+static void launch_rmsnorm_reg(int ch, const void* x, const void* gamma, void* y, int64_t M,
+                               int64_t N, float eps, hipStream_t s) {
+  dim3 grid((unsigned)M), block(256);
+  auto G = static_cast<const uint16_t*>(gamma);
+  auto Y = static_cast<uint16_t*>(y);
+#define TPL_RMS(C) hipLaunchKernelGGL((rmsnorm_reg_kernel<C, XF32>), grid, block, 0, s, x, G, Y, N, eps)
+  switch (ch) {
+    case 1: TPL_RMS(1); break;
+    case 2: TPL_RMS(2); break;
+    case 3: TPL_RMS(3); break;
+    case 4: TPL_RMS(4); break;
+    case 5: TPL_RMS(5); break;
+    case 6: TPL_RMS(6); break;
+    case 7: TPL_RMS(7); break;
+    default: TPL_RMS(8); break;
+  }
+#undef TPL_RMS
+}
+
+// x_f32: x is float32 storage; bf16: gamma and y are bf16 (x too unless x_f32).
+tp_status rmsnorm(const void* x, bool x_f32, const void* gamma, void* y, int64_t M, int64_t N,
+                  float eps, bool bf16, bool vec, hipStream_t s) {
   dim3 grid((unsigned)M), block(256);
   const int ch = (int)((N + 2047) / 2048);
   if (bf16 && vec && ch <= 8) {
-    auto X = static_cast<const uint16_t*>(x);
-    auto G = static_cast<const uint16_t*>(gamma);
-    auto Y = static_cast<uint16_t*>(y);
-#define TPL_RMS(C) hipLaunchKernelGGL((rmsnorm_reg_kernel<C>), grid, block, 0, s, X, G, Y, N, eps)
-    switch (ch) {
-      case 1: TPL_RMS(1); break;
-      case 2: TPL_RMS(2); break;
-      case 3: TPL_RMS(3); break;
-      case 4: TPL_RMS(4); break;
-      case 5: TPL_RMS(5); break;
-      case 6: TPL_RMS(6); break;
-      case 7: TPL_RMS(7); break;
-      default: TPL_RMS(8); break;
-    }
-#undef TPL_RMS
-    TPL_LAUNCH_CHECK("rmsnorm");
-    return TP_OK;
-  }
-  if (bf16) {
-    if (vec) hipLaunchKernelGGL((rmsnorm_kernel<true, true>), grid, block, 0, s, x, gamma, y, N, eps);
-    else hipLaunchKernelGGL((rmsnorm_kernel<true, false>), grid, block, 0, s, x, gamma, y, N, eps);
+    if (x_f32) launch_rmsnorm_reg<true>(ch, x, gamma, y, M, N, eps, s);
+    else launch_rmsnorm_reg<false>(ch, x, gamma, y, M, N, eps, s);
+  } else if (bf16 && vec) {
+    if (x_f32) hipLaunchKernelGGL((rmsnorm_kernel<true, true, true>), grid, block, 0, s, x, gamma, y, N, eps);
+    else hipLaunchKernelGGL((rmsnorm_kernel<false, true, true>), grid, block, 0, s, x, gamma, y, N, eps);
+  } else if (bf16) {
+    if (x_f32) hipLaunchKernelGGL((rmsnorm_kernel<true, true, false>), grid, block, 0, s, x, gamma, y, N, eps);
+    else hipLaunchKernelGGL((rmsnorm_kernel<false, true, false>), grid, block, 0, s, x, gamma, y, N, eps);
   } else {
-    hipLaunchKernelGGL((rmsnorm_kernel<false, false>), grid, block, 0, s, x, gamma, y, N, eps);
+    if (x_f32) hipLaunchKernelGGL((rmsnorm_kernel<true, false, false>), grid, block, 0, s, x, gamma, y, N, eps);
+    else hipLaunchKernelGGL((rmsnorm_kernel<false, false, false>), grid, block, 0, s, x, gamma, y, N, eps);
   }
   TPL_LAUNCH_CHECK("rmsnorm");
   return TP_OK;
@@ -300,16 +355,37 @@ tp_status rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t 
 
 // ---- sum of rank partials + residual, then RMSNorm (fused) ------------------------
 
-// One 256-thread workgroup per row, bf16 storage, N % 8 == 0, 16-byte aligned
-// rows.  Pass 1 forms h = residual + sum_r partials[r] exactly as reduce_kernel
-// does (fp32, rank order, residual last, RNE to bf16), stores it and
-// accumulates the squares of the stored bf16 values in rmsnorm_kernel's order;
-// pass 2 re-reads this thread's own h values (still in L2) and normalises them
+// One 256-thread workgroup per row; gamma and yn bf16, y bf16 or float32
+// (YF32), N % 8 == 0, 16-byte aligned rows.  Pass 1 forms y = residual +
+// sum_r partials[r] exactly as reduce_kernel does (fp32, rank order, residual
+// last, one rounding to y's type), stores it and accumulates the squares of
+// the stored values in the order of rmsnorm_kernel's vector path; pass 2
+// re-reads this thread's own y values (still in L2) and normalises them
 // exactly as rmsnorm_kernel does.  So y and yn equal the two unfused calls bit
-// for bit, with one launch and one less pass over h in HBM.
+// for bit, with one launch and one less pass over y in HBM.
+template <int RES, bool YF32>
+__device__ __forceinline__ void sum_chunk(const PartialPtrs& P, int R, const void* residual,
+                                          int64_t o, float* h) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(P.p[0] + o + 4 * half);
+    for (int r = 1; r < R; ++r) acc += *reinterpret_cast<const f32x4*>(P.p[r] + o + 4 * half);
+    if constexpr (RES == kResBf16) {
+      const u32x2 rv = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(residual) + o + 4 * half);
+      acc[0] += bf_lo(rv[0]); acc[1] += bf_hi(rv[0]);
+      acc[2] += bf_lo(rv[1]); acc[3] += bf_hi(rv[1]);
+    } else if constexpr (RES == kResF32) {
+      acc += *reinterpret_cast<const f32x4*>(static_cast<const float*>(residual) + o + 4 * half);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[4 * half + i] = acc[i];
+  }
+}
+
+template <int RES, bool YF32>
 __global__ __launch_bounds__(256) void reduce_rmsnorm_kernel(PartialPtrs P, int R,
-                                                             const uint16_t* residual,
-                                                             uint16_t* y,   // may alias residual
+                                                             const void* residual,
+                                                             void* y,   // may alias residual
                                                              const uint16_t* __restrict__ gamma,
                                                              uint16_t* __restrict__ yn, int64_t N,
                                                              float eps) {
@@ -318,26 +394,11 @@ __global__ __launch_bounds__(256) void reduce_rmsnorm_kernel(PartialPtrs P, int 
   const int tid = threadIdx.x;
   float ss = 0.f;
   for (int64_t c = tid * 8; c < N; c += 256 * 8) {
-    const int64_t o = m * N + c;
     float h[8];
+    sum_chunk<RES, YF32>(P, R, residual, m * N + c, h);
+    store8<YF32>(y, m * N + c, h);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x4 acc = *reinterpret_cast<const f32x4*>(P.p[0] + o + 4 * half);
-      for (int r = 1; r < R; ++r) acc += *reinterpret_cast<const f32x4*>(P.p[r] + o + 4 * half);
-      if (residual) {
-        const u32x2 rv = *reinterpret_cast<const u32x2*>(residual + o + 4 * half);
-        acc[0] += bf_lo(rv[0]); acc[1] += bf_hi(rv[0]);
-        acc[2] += bf_lo(rv[1]); acc[3] += bf_hi(rv[1]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[4 * half + i] = acc[i];
-    }
-    const u32x4 hb = pack8(h);
-    *reinterpret_cast<u32x4*>(y + o) = hb;
-    float f[8];
-    unpack8(hb, f);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+    for (int i = 0; i < 8; ++i) ss = fmaf(h[i], h[i], ss);
   }
   ss = wave_sum(ss);
   if ((tid & 63) == 0) wsum[tid >> 6] = ss;
@@ -346,7 +407,7 @@ __global__ __launch_bounds__(256) void reduce_rmsnorm_kernel(PartialPtrs P, int 
   const float inv = rsqrtf(tot / (float)N + eps);
   for (int64_t c = tid * 8; c < N; c += 256 * 8) {
     float f[8], gm[8], o[8];
-    unpack8(*reinterpret_cast<const u32x4*>(y + m * N + c), f);
+    load8<YF32>(y, m * N + c, f);
     unpack8(*reinterpret_cast<const u32x4*>(gamma + c), gm);
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = f[i] * inv * gm[i];
@@ -355,12 +416,12 @@ __global__ __launch_bounds__(256) void reduce_rmsnorm_kernel(PartialPtrs P, int 
 }
 
 // Rows of at most 8 x 2048 elements: reduce_rmsnorm_kernel's arithmetic in the
-// same order, with each rank's loads for the whole row issued together and h
+// same order, with each rank's loads for the whole row issued together and y
 // kept in registers for the second pass.
-template <int CH>
+template <int CH, int RES, bool YF32>
 __global__ __launch_bounds__(256) void reduce_rmsnorm_reg_kernel(PartialPtrs P, int R,
-                                                                 const uint16_t* residual,
-                                                                 uint16_t* y,   // may alias residual
+                                                                 const void* residual,
+                                                                 void* y,   // may alias residual
                                                                  const uint16_t* __restrict__ gamma,
                                                                  uint16_t* __restrict__ yn, int64_t N,
                                                                  float eps) {
@@ -392,31 +453,29 @@ __global__ __launch_bounds__(256) void reduce_rmsnorm_reg_kernel(PartialPtrs P, 
       acc[k][1] += v[k][1];
     }
   }
-  u32x4 hb[CH];
+  float h[CH][8];
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < CH; ++k) {
     const int64_t c = tid * 8 + k * 2048;
     if (c < N) {
       const int64_t o = m * N + c;
-      float h[8];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         f32x4 a = acc[k][half];
-        if (residual) {
-          const u32x2 rv = *reinterpret_cast<const u32x2*>(residual + o + 4 * half);
+        if constexpr (RES == kResBf16) {
+          const u32x2 rv = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(residual) + o + 4 * half);
           a[0] += bf_lo(rv[0]); a[1] += bf_hi(rv[0]);
           a[2] += bf_lo(rv[1]); a[3] += bf_hi(rv[1]);
+        } else if constexpr (RES == kResF32) {
+          a += *reinterpret_cast<const f32x4*>(static_cast<const float*>(residual) + o + 4 * half);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[4 * half + i] = a[i];
+        for (int i = 0; i < 4; ++i) h[k][4 * half + i] = a[i];
       }
-      hb[k] = pack8(h);
-      *reinterpret_cast<u32x4*>(y + o) = hb[k];
-      float f[8];
-      unpack8(hb[k], f);
+      store8<YF32>(y, o, h[k]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+      for (int i = 0; i < 8; ++i) ss = fmaf(h[k][i], h[k][i], ss);
     }
   }
   ss = wave_sum(ss);
@@ -428,46 +487,56 @@ __global__ __launch_bounds__(256) void reduce_rmsnorm_reg_kernel(PartialPtrs P, 
   for (int k = 0; k < CH; ++k) {
     const int64_t c = tid * 8 + k * 2048;
     if (c < N) {
-      float f[8], gm[8], o[8];
-      unpack8(hb[k], f);
+      float gm[8], o[8];
       unpack8(*reinterpret_cast<const u32x4*>(gamma + c), gm);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = f[i] * inv * gm[i];
+      for (int i = 0; i < 8; ++i) o[i] = h[k][i] * inv * gm[i];
       *reinterpret_cast<u32x4*>(yn + m * N + c) = pack8(o);
     }
   }
 }
 
-tp_status reduce_rmsnorm(const float* const* partials, int R, const void* residual, void* y,
-                         const void* gamma, void* yn, int64_t M, int64_t N, float eps,
-                         hipStream_t s) {
+template <int RES, bool YF32>
+static void launch_reduce_rmsnorm(const PartialPtrs& P, int R, const void* residual, void* y,
+                                  const void* gamma, void* yn, int64_t M, int64_t N, float eps,
+                                  hipStream_t s) {
+  auto G = static_cast<const uint16_t*>(gamma);
+  auto YN = static_cast<uint16_t*>(yn);
+  const int ch = (int)((N + 2047) / 2048);
+  if (ch > 8) {
+    hipLaunchKernelGGL((reduce_rmsnorm_kernel<RES, YF32>), dim3((unsigned)M), dim3(256), 0, s, P, R,
+                       residual, y, G, YN, N, eps);
+    return;
+  }
+#define TPL_RRMS(C) hipLaunchKernelGGL((reduce_rmsnorm_reg_kernel<C, RES, YF32>), dim3((unsigned)M), \
+                                       dim3(256), 0, s, P, R, residual, y, G, YN, N, eps)
+  switch (ch) {
+    case 1: TPL_RRMS(1); break;
+    case 2: TPL_RRMS(2); break;
+    case 3: TPL_RRMS(3); break;
+    case 4: TPL_RRMS(4); break;
+    case 5: TPL_RRMS(5); break;
+    case 6: TPL_RRMS(6); break;
+    case 7: TPL_RRMS(7); break;
+    default: TPL_RRMS(8); break;
+  }
+#undef TPL_RRMS
+}
+
+// gamma and yn bf16; residual bf16 or float32 (res_f32) or none; y bf16 or
+// float32 (y_f32).
+tp_status reduce_rmsnorm(const float* const* partials, int R, const void* residual, bool res_f32,
+                         void* y, bool y_f32, const void* gamma, void* yn, int64_t M, int64_t N,
+                         float eps, hipStream_t s) {
   PartialPtrs P = {};
   for (int r = 0; r < R; ++r) P.p[r] = partials[r];
-  const int ch = (int)((N + 2047) / 2048);
-  if (ch <= 8) {
-    auto Rs = static_cast<const uint16_t*>(residual);
-    auto Y = static_cast<uint16_t*>(y);
-    auto G = static_cast<const uint16_t*>(gamma);
-    auto YN = static_cast<uint16_t*>(yn);
-#define TPL_RRMS(C) hipLaunchKernelGGL((reduce_rmsnorm_reg_kernel<C>), dim3((unsigned)M), dim3(256), 0, s, \
-                                       P, R, Rs, Y, G, YN, N, eps)
-    switch (ch) {
-      case 1: TPL_RRMS(1); break;
-      case 2: TPL_RRMS(2); break;
-      case 3: TPL_RRMS(3); break;
-      case 4: TPL_RRMS(4); break;
-      case 5: TPL_RRMS(5); break;
-      case 6: TPL_RRMS(6); break;
-      case 7: TPL_RRMS(7); break;
-      default: TPL_RRMS(8); break;
-    }
-#undef TPL_RRMS
-    TPL_LAUNCH_CHECK("reduce_rmsnorm");
-    return TP_OK;
-  }
-  hipLaunchKernelGGL(reduce_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, s, P, R,
-                     static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(y),
-                     static_cast<const uint16_t*>(gamma), static_cast<uint16_t*>(yn), N, eps);
+#define TPL_RR(RES) \
+  (y_f32 ? launch_reduce_rmsnorm<RES, true>(P, R, residual, y, gamma, yn, M, N, eps, s) \
+         : launch_reduce_rmsnorm<RES, false>(P, R, residual, y, gamma, yn, M, N, eps, s))
+  if (!residual) TPL_RR(kResNone);
+  else if (res_f32) TPL_RR(kResF32);
+  else TPL_RR(kResBf16);
+#undef TPL_RR
   TPL_LAUNCH_CHECK("reduce_rmsnorm");
   return TP_OK;
 }

@@ -73,8 +73,8 @@ __device__ __forceinline__ void sg_pairs() {
 // EPI: 0 = plain product; 1 = SwiGLU on a paired tile (W rows [0, I) gate,
 // [I, 2I) up; the tile's first BN/2 W rows are gate rows n0.., the rest the
 // matching up rows; output [M, I]); 2 = GELU on each output.  The fused
-// epilogues round the products to bf16 first, exactly as the unfused path
-// stores them before the activation kernel reads them.
+// epilogues apply the activation to the float32 accumulators, so the gate and
+// up products are never rounded; only the activation's result is stored bf16.
 template <class C, bool OUT_F32, bool VEC_OUT, int EPI>
 __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
@@ -283,9 +283,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float g = bf2f((uint16_t)f2bf_bits(acc[i][j][4 * q + e]));
-            const float u = bf2f((uint16_t)f2bf_bits(acc[i + C::FA / 2][j][4 * q + e]));
-            v[e] = act_fn<TP_ACT_SWIGLU>(g, u);
+            v[e] = act_fn<TP_ACT_SWIGLU>(acc[i][j][4 * q + e], acc[i + C::FA / 2][j][4 * q + e]);
           }
           if (VEC_OUT && n + 3 < N) {
             *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(Y) + (int64_t)m * N + n) =
@@ -330,10 +328,8 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float g = bf2f((uint16_t)f2bf_bits(acc[i][j][4 * q + e]));
-              const float u = bf2f((uint16_t)f2bf_bits(
-                  xch[pair * PER_WAVE + ((i * C::FB + j) * 16 + 4 * q + e) * 64 + lane]));
-              v[e] = act_fn<TP_ACT_SWIGLU>(g, u);
+              v[e] = act_fn<TP_ACT_SWIGLU>(
+                  acc[i][j][4 * q + e], xch[pair * PER_WAVE + ((i * C::FB + j) * 16 + 4 * q + e) * 64 + lane]);
             }
             if (VEC_OUT && n + 3 < N) {
               *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(Y) + (int64_t)m * N + n) =
@@ -362,7 +358,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
                       acc[i][j][4 * q + 3]};
         if constexpr (EPI == 2) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = act_fn<TP_ACT_GELU>(bf2f((uint16_t)f2bf_bits(v[e])), 0.f);
+          for (int e = 0; e < 4; ++e) v[e] = act_fn<TP_ACT_GELU>(v[e], 0.f);
         }
         if (VEC_OUT && n + 3 < N) {
           if constexpr (OUT_F32) {

@@ -34,8 +34,8 @@ __device__ __forceinline__ u32x4 bload(const __amdgpu_buffer_rsrc_t r, uint32_t 
 
 // EPI: 0 = plain product; 1 = SwiGLU (RT = 2: row tile 0 = gate rows n0..,
 // tile 1 = the matching up rows N + n0.. of a [2N, K] weight; output [M, N]);
-// 2 = GELU on each output.  Fused epilogues round the sums to bf16 before the
-// activation, exactly as the unfused path stores them.
+// 2 = GELU on each output.  Fused epilogues apply the activation to the
+// float32 sums; only the activation's result is rounded to bf16.
 template <int WAVES, int MT, int RT, bool OUT_F32, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
       const int nl = (l >> 4) * 4 + e, n = n0 + nl;
       if (m < M && nl < nrows)
         reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] = (uint16_t)f2bf_bits(
-            act_fn<TP_ACT_SWIGLU>(bf2f((uint16_t)f2bf_bits(sg)), bf2f((uint16_t)f2bf_bits(su))));
+            act_fn<TP_ACT_SWIGLU>(sg, su));
     }
     return;
   }
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_kernel(
     if (m < M && nl < nrows) {
       if constexpr (EPI == 2)
         reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] =
-            (uint16_t)f2bf_bits(act_fn<TP_ACT_GELU>(bf2f((uint16_t)f2bf_bits(s)), 0.f));
+            (uint16_t)f2bf_bits(act_fn<TP_ACT_GELU>(s, 0.f));
       else if constexpr (OUT_F32)
         reinterpret_cast<float*>(Y)[(int64_t)m * N + n] = s;
       else

@@ -41,8 +41,8 @@ constexpr uint32_t kSOob = 0x80000000u;   // offset past any buffer bound -> rea
 
 // EPI: 0 plain, 1 SwiGLU (RT = 2: row tile 0 = gate rows n0.., tile 1 = the
 // matching up rows N + n0.. of a [2N, K] weight; output [M, N]), 2 GELU.  The
-// fused epilogues round the sums to bf16 before the activation, as the
-// unfused path stores them.
+// fused epilogues apply the activation to the float32 sums; only its result is
+// rounded to bf16.
 template <int WAVES, int MT, int RT, int S, bool OUT_F32, int EPI, int TG>
 __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
       const int nl = (l >> 4) * 4 + e, n = n0 + nl;
       if (m < M && nl < nrows)
         reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] = (uint16_t)f2bf_bits(
-            act_fn<TP_ACT_SWIGLU>(bf2f((uint16_t)f2bf_bits(sg)), bf2f((uint16_t)f2bf_bits(su))));
+            act_fn<TP_ACT_SWIGLU>(sg, su));
     }
     return;
   }
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
     if (m < M && nl < nrows) {
       if constexpr (EPI == 2)
         reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] =
-            (uint16_t)f2bf_bits(act_fn<TP_ACT_GELU>(bf2f((uint16_t)f2bf_bits(s)), 0.f));
+            (uint16_t)f2bf_bits(act_fn<TP_ACT_GELU>(s, 0.f));
       else if constexpr (OUT_F32)
         reinterpret_cast<float*>(Y)[(int64_t)m * N + n] = s;
       else

@@ -16,19 +16,19 @@ tp_status gemm_bf16_dma_act(const void* x, const void* w, void* h, int64_t M, in
                             int act, bool vec_out, hipStream_t s);
 tp_status gemm_bf16_stream_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
                                int64_t K, int act, hipStream_t s);
-tp_status reduce_rmsnorm(const float* const* partials, int R, const void* residual, void* y,
-                         const void* gamma, void* yn, int64_t M, int64_t N, float eps,
-                         hipStream_t s);
+tp_status reduce_rmsnorm(const float* const* partials, int R, const void* residual, bool res_f32,
+                         void* y, bool y_f32, const void* gamma, void* yn, int64_t M, int64_t N,
+                         float eps, hipStream_t s);
 tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                            bool out_f32, hipStream_t s);
 tp_status gemm_f32(const float* x, const float* w, float* y, int64_t M, int64_t N, int64_t K,
                    hipStream_t s);
 tp_status act_local(const void* g, const void* u, void* h, int64_t M, int64_t I, int64_t ld,
                     int act, bool bf16, bool vec, hipStream_t s);
-tp_status reduce_partials(const float* const* partials, int R, const void* residual, void* y,
-                          int64_t total, bool bf16, bool vec, hipStream_t s);
-tp_status rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t N, float eps,
-                  bool bf16, bool vec, hipStream_t s);
+tp_status reduce_partials(const float* const* partials, int R, const void* residual, bool res_f32,
+                          void* y, int64_t total, bool bf16, bool vec, hipStream_t s);
+tp_status rmsnorm(const void* x, bool x_f32, const void* gamma, void* y, int64_t M, int64_t N,
+                  float eps, bool bf16, bool vec, hipStream_t s);
 tp_status kv_append(const void* kn, const void* vn, int64_t new_stride, void* kc, void* vc,
                     const int64_t cs[3], int64_t B, int64_t H, int64_t D, int64_t pos,
                     hipStream_t s);
@@ -76,6 +76,19 @@ namespace {
 constexpr int64_t kIntMax = 0x7fffffff;
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+// Do the byte ranges [a, a + na) and [b, b + nb) share a byte?
+inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+// A sum's output may be its residual buffer itself (the residual stream
+// updated in place) only when both have one storage type; any other overlap
+// would let one thread's store clobber another thread's residual load.
+inline bool bad_alias(const void* res, tp_dtype res_dt, const void* y, tp_dtype y_dt, int64_t n) {
+  if (!res) return false;
+  if (res == y && res_dt == y_dt) return false;
+  return overlap(res, (size_t)n * (res_dt == TP_BF16 ? 2 : 4), y, (size_t)n * (y_dt == TP_BF16 ? 2 : 4));
+}
 inline size_t esize(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
 inline bool dtype_ok(tp_dtype dt) { return dt == TP_F32 || dt == TP_BF16; }
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -245,36 +258,40 @@ tp_status tp_decode_attention_append(const void* q, const int64_t qs[2], const v
 }
 
 tp_status tp_reduce_partials(const float* const* partials, int64_t R, const void* residual,
-                             void* y, int64_t M, int64_t N, tp_dtype out_dt, void* stream) {
+                             tp_dtype res_dt, void* y, int64_t M, int64_t N, tp_dtype out_dt,
+                             void* stream) {
   if (!partials || !y) return TP_ERR_NULL;
   if (R < 1 || R > 16) return TP_ERR_SHAPE;
   for (int64_t r = 0; r < R; ++r)
     if (!partials[r]) return TP_ERR_NULL;
-  if (!dtype_ok(out_dt)) return TP_ERR_DTYPE;
+  if (!dtype_ok(out_dt) || (residual && !dtype_ok(res_dt))) return TP_ERR_DTYPE;
   if (M <= 0 || N <= 0) return TP_ERR_SHAPE;
-  const size_t es = esize(out_dt);
-  if (!aligned(y, es) || (residual && !aligned(residual, es))) return TP_ERR_ALIGN;
-  bool vec = ((M * N) % 4 == 0) && aligned(y, 4 * es) && (!residual || aligned(residual, 4 * es));
+  if (bad_alias(residual, res_dt, y, out_dt, M * N)) return TP_ERR_SHAPE;
+  const size_t es = esize(out_dt), rs = esize(res_dt);
+  if (!aligned(y, es) || (residual && !aligned(residual, rs))) return TP_ERR_ALIGN;
+  bool vec = ((M * N) % 4 == 0) && aligned(y, 4 * es) && (!residual || aligned(residual, 4 * rs));
   for (int64_t r = 0; r < R; ++r) {
     if (!aligned(partials[r], 4)) return TP_ERR_ALIGN;
     vec = vec && aligned(partials[r], 16);
   }
-  return tpl::reduce_partials(partials, (int)R, residual, y, M * N, out_dt == TP_BF16, vec,
-                              as_stream(stream));
+  return tpl::reduce_partials(partials, (int)R, residual, res_dt == TP_F32, y, M * N,
+                              out_dt == TP_BF16, vec, as_stream(stream));
 }
 
 tp_status tp_reduce_partials_rmsnorm(const float* const* partials, int64_t R, const void* residual,
-                                     void* y, const void* gamma, void* yn, int64_t M, int64_t N,
-                                     float eps, tp_dtype dt, void* stream) {
+                                     tp_dtype res_dt, void* y, tp_dtype y_dt, const void* gamma,
+                                     void* yn, int64_t M, int64_t N, float eps, tp_dtype dt,
+                                     void* stream) {
   if (!partials || !y || !gamma || !yn) return TP_ERR_NULL;
   if (R < 1 || R > 16) return TP_ERR_SHAPE;
   for (int64_t r = 0; r < R; ++r)
     if (!partials[r]) return TP_ERR_NULL;
-  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dtype_ok(dt) || !dtype_ok(y_dt) || (residual && !dtype_ok(res_dt))) return TP_ERR_DTYPE;
   if (M <= 0 || N <= 0 || !(eps >= 0.f) || !isfinite(eps)) return TP_ERR_SHAPE;
   if (M > kIntMax) return TP_ERR_UNSUPPORTED;
-  const size_t es = esize(dt);
-  if (!aligned(y, es) || !aligned(yn, es) || !aligned(gamma, es) || (residual && !aligned(residual, es)))
+  if (bad_alias(residual, res_dt, y, y_dt, M * N)) return TP_ERR_SHAPE;
+  const size_t es = esize(dt), ys = esize(y_dt), rs = esize(res_dt);
+  if (!aligned(y, ys) || !aligned(yn, es) || !aligned(gamma, es) || (residual && !aligned(residual, rs)))
     return TP_ERR_ALIGN;
   bool fused = dt == TP_BF16 && N % 8 == 0 && aligned(y, 16) && aligned(yn, 16) && aligned(gamma, 16) &&
                (!residual || aligned(residual, 16));
@@ -283,11 +300,12 @@ tp_status tp_reduce_partials_rmsnorm(const float* const* partials, int64_t R, co
     fused = fused && aligned(partials[r], 16);
   }
   if (fused)
-    return tpl::reduce_rmsnorm(partials, (int)R, residual, y, gamma, yn, M, N, eps, as_stream(stream));
+    return tpl::reduce_rmsnorm(partials, (int)R, residual, res_dt == TP_F32, y, y_dt == TP_F32, gamma,
+                               yn, M, N, eps, as_stream(stream));
   // other layouts: the two unfused calls (same results)
-  const tp_status st = tp_reduce_partials(partials, R, residual, y, M, N, dt, stream);
+  const tp_status st = tp_reduce_partials(partials, R, residual, res_dt, y, M, N, y_dt, stream);
   if (st != TP_OK) return st;
-  return tp_rmsnorm(y, gamma, yn, M, N, eps, dt, stream);
+  return tp_rmsnorm(y, y_dt, gamma, yn, M, N, eps, dt, stream);
 }
 
 size_t tp_paged_attention_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_context_len,
@@ -408,17 +426,17 @@ tp_status tp_vocab_argmax_reduce(const float* const* vals, const int64_t* const*
   return tpl::vocab_argmax_reduce(vals, idxs, (int)R, M, out_val, out_idx, as_stream(stream));
 }
 
-tp_status tp_rmsnorm(const void* x, const void* gamma, void* y, int64_t M, int64_t N, float eps,
-                     tp_dtype dt, void* stream) {
+tp_status tp_rmsnorm(const void* x, tp_dtype x_dt, const void* gamma, void* y, int64_t M, int64_t N,
+                     float eps, tp_dtype dt, void* stream) {
   if (!x || !gamma || !y) return TP_ERR_NULL;
-  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dtype_ok(dt) || !dtype_ok(x_dt)) return TP_ERR_DTYPE;
   if (M <= 0 || N <= 0 || !(eps >= 0.f) || !isfinite(eps)) return TP_ERR_SHAPE;
   if (M > kIntMax) return TP_ERR_UNSUPPORTED;
   const size_t es = esize(dt);
-  if (!aligned(x, es) || !aligned(gamma, es) || !aligned(y, es)) return TP_ERR_ALIGN;
+  if (!aligned(x, esize(x_dt)) || !aligned(gamma, es) || !aligned(y, es)) return TP_ERR_ALIGN;
   const bool vec = dt == TP_BF16 && (N % 8 == 0) && aligned(x, 16) && aligned(gamma, 16) &&
                    aligned(y, 16);
-  return tpl::rmsnorm(x, gamma, y, M, N, eps, dt == TP_BF16, vec, as_stream(stream));
+  return tpl::rmsnorm(x, x_dt == TP_F32, gamma, y, M, N, eps, dt == TP_BF16, vec, as_stream(stream));
 }
 
 const char* tp_status_string(tp_status s) {

@@ -9,6 +9,7 @@ parallel" / "MLP 里的 tensor parallel"; P2 sections 二 and 2.1):
     o = attention over the rank's heads               local
     P_attn_r = o Wo_r                                 row-parallel partial
     h = x + sum_r P_attn_r                            all-reduce arithmetic
+                                                      (h stays float32)
     hn = RMSNorm(h)                                   (fused with the sum)
     g|u = hn Wgu_r                                    column-parallel
     a = SiLU(g) * u   (or GELU(g))                    local (fused into g|u)
@@ -38,8 +39,9 @@ class MlpShard:
     row-parallel partial for one rank.  ``w_in`` is ``[2*I_l, H]`` (gate rows
     then up rows) for SwiGLU or ``[I_l, H]`` for GELU/none; ``w_out`` is
     ``[H, I_l]``.  With ``fused`` (the default) a bf16 shard takes the
-    activation in the projection's epilogue (``column_linear_act``); the
-    result is the same bit for bit."""
+    activation in the projection's epilogue (``column_linear_act``), on the
+    float32 sums; unfused, the projection is stored as bf16 before the
+    activation kernel reads it."""
 
     def __init__(self, w_in: torch.Tensor, w_out: torch.Tensor, act: str, max_tokens: int,
                  fused: bool = True):
@@ -159,7 +161,12 @@ class AttnShard:
 
 
 class LayerShard:
-    """One rank's share of a pre-norm decoder layer (prefill of one sequence)."""
+    """One rank's share of a pre-norm decoder layer (prefill of one sequence).
+
+    The residual stream ``h`` (the attention sub-block's sum plus the input)
+    is kept in float32: it is never a GEMM operand, only the residual of the
+    final sum and the input of the second pre-norm.  The layer input ``x``,
+    the normalised ``xn``/``hn`` and the output ``y`` are bf16."""
 
     def __init__(self, g1, g2, wqkv, wo, wgu, wd, n_q, n_kv, head_dim, eps, max_tokens,
                  act="swiglu", fused=True):
@@ -169,7 +176,7 @@ class LayerShard:
         H = wo.shape[0]
         dev, dt = wqkv.device, wqkv.dtype
         self.xn = torch.empty((max_tokens, H), dtype=dt, device=dev)
-        self.h = torch.empty((max_tokens, H), dtype=dt, device=dev)
+        self.h = torch.empty((max_tokens, H), dtype=torch.float32, device=dev)
         self.hn = torch.empty((max_tokens, H), dtype=dt, device=dev)
 
     def attn_partial(self, x, out):

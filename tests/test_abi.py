@@ -131,25 +131,33 @@ def test_attention_validation(lib):
 def test_reduce_validation(lib):
     f = lib.tp_reduce_partials
     arr = (ctypes.c_void_p * 2)(P, P)
-    assert f(None, 2, None, P, 4, 4, 0, S) == NULL
-    assert f(arr, 0, None, P, 4, 4, 0, S) == SHAPE
-    assert f(arr, 17, None, P, 4, 4, 0, S) == SHAPE
+    assert f(None, 2, None, 0, P, 4, 4, 0, S) == NULL
+    assert f(arr, 0, None, 0, P, 4, 4, 0, S) == SHAPE
+    assert f(arr, 17, None, 0, P, 4, 4, 0, S) == SHAPE
     bad = (ctypes.c_void_p * 2)(P, None)
-    assert f(bad, 2, None, P, 4, 4, 0, S) == NULL
-    assert f(arr, 2, None, P, 0, 4, 0, S) == SHAPE
-    assert f(arr, 2, None, P, 4, 4, 4, S) == DTYPE
-    assert f(arr, 2, P + 2, P, 4, 4, 0, S) == ALIGN
+    assert f(bad, 2, None, 0, P, 4, 4, 0, S) == NULL
+    assert f(arr, 2, None, 0, P, 0, 4, 0, S) == SHAPE
+    assert f(arr, 2, None, 0, P, 4, 4, 4, S) == DTYPE
+    assert f(arr, 2, P + 256, 7, P, 4, 4, 0, S) == DTYPE          # bad residual dtype
+    assert f(arr, 2, P + 258, 0, P, 4, 4, 0, S) == ALIGN
     odd = (ctypes.c_void_p * 2)(P, P + 2)
-    assert f(odd, 2, None, P, 4, 4, 0, S) == ALIGN
+    assert f(odd, 2, None, 0, P, 4, 4, 0, S) == ALIGN
+    # y may be the residual itself only with one storage type; other overlaps
+    # are rejected (a 4x4 fp32 residual and a bf16 y inside it)
+    assert f(arr, 2, P + 256, 0, P + 256, 4, 4, 1, S) == SHAPE
+    assert f(arr, 2, P + 256, 0, P + 272, 4, 4, 0, S) == SHAPE
+    assert f(arr, 2, P + 256, 1, P + 256, 4, 4, 0, S) == SHAPE
 
 
 @no_gpu
 def test_rmsnorm_and_append_validation(lib):
-    assert lib.tp_rmsnorm(None, P, P, 4, 8, 1e-5, 1, S) == NULL
-    assert lib.tp_rmsnorm(P, P, P, 4, 8, -1.0, 1, S) == SHAPE
-    assert lib.tp_rmsnorm(P, P, P, 4, 8, float("nan"), 1, S) == SHAPE
-    assert lib.tp_rmsnorm(P, P, P, 0, 8, 1e-5, 1, S) == SHAPE
-    assert lib.tp_rmsnorm(P, P, P + 1, 4, 8, 1e-5, 1, S) == ALIGN
+    assert lib.tp_rmsnorm(None, 1, P, P, 4, 8, 1e-5, 1, S) == NULL
+    assert lib.tp_rmsnorm(P, 1, P, P, 4, 8, -1.0, 1, S) == SHAPE
+    assert lib.tp_rmsnorm(P, 1, P, P, 4, 8, float("nan"), 1, S) == SHAPE
+    assert lib.tp_rmsnorm(P, 1, P, P, 0, 8, 1e-5, 1, S) == SHAPE
+    assert lib.tp_rmsnorm(P, 1, P, P + 1, 4, 8, 1e-5, 1, S) == ALIGN
+    assert lib.tp_rmsnorm(P + 2, 0, P, P, 4, 8, 1e-5, 1, S) == ALIGN   # fp32 x on a 2-byte boundary
+    assert lib.tp_rmsnorm(P, 3, P, P, 4, 8, 1e-5, 1, S) == DTYPE
     cs = _s3(2 * 64 * 128, 128, 64 * 128)
     f = lib.tp_kv_append
     assert f(None, P, 256, P, P, cs, 2, 2, 128, 64, 0, 1, S) == NULL
@@ -175,17 +183,21 @@ def test_fused_entry_validation(lib):
     assert f(P, P, P, 4, 1 << 20, 1 << 11, 1, 1, S) == UNSUPPORTED   # weight past 32-bit offsets
     g = lib.tp_reduce_partials_rmsnorm
     arr = (ctypes.c_void_p * 2)(P, P)
-    assert g(None, 2, None, P, P, P, 4, 8, 1e-5, 1, S) == NULL
-    assert g(arr, 2, None, P, None, P, 4, 8, 1e-5, 1, S) == NULL
-    assert g(arr, 2, None, P, P, None, 4, 8, 1e-5, 1, S) == NULL
-    assert g(arr, 0, None, P, P, P, 4, 8, 1e-5, 1, S) == SHAPE
-    assert g(arr, 17, None, P, P, P, 4, 8, 1e-5, 1, S) == SHAPE
-    assert g(arr, 2, None, P, P, P, 4, 8, -1.0, 1, S) == SHAPE
-    assert g(arr, 2, None, P, P, P, 0, 8, 1e-5, 1, S) == SHAPE
-    assert g(arr, 2, None, P, P, P, 4, 8, 1e-5, 4, S) == DTYPE
-    assert g(arr, 2, None, P + 1, P, P, 4, 8, 1e-5, 1, S) == ALIGN
+    assert g(None, 2, None, 1, P, 1, P, P, 4, 8, 1e-5, 1, S) == NULL
+    assert g(arr, 2, None, 1, P, 1, None, P, 4, 8, 1e-5, 1, S) == NULL
+    assert g(arr, 2, None, 1, P, 1, P, None, 4, 8, 1e-5, 1, S) == NULL
+    assert g(arr, 0, None, 1, P, 1, P, P, 4, 8, 1e-5, 1, S) == SHAPE
+    assert g(arr, 17, None, 1, P, 1, P, P, 4, 8, 1e-5, 1, S) == SHAPE
+    assert g(arr, 2, None, 1, P, 1, P, P, 4, 8, -1.0, 1, S) == SHAPE
+    assert g(arr, 2, None, 1, P, 1, P, P, 0, 8, 1e-5, 1, S) == SHAPE
+    assert g(arr, 2, None, 1, P, 1, P, P, 4, 8, 1e-5, 4, S) == DTYPE
+    assert g(arr, 2, None, 1, P, 4, P, P, 4, 8, 1e-5, 1, S) == DTYPE     # bad y dtype
+    assert g(arr, 2, None, 1, P + 1, 1, P, P, 4, 8, 1e-5, 1, S) == ALIGN
+    assert g(arr, 2, None, 1, P + 2, 0, P, P, 4, 8, 1e-5, 1, S) == ALIGN   # fp32 y
     odd = (ctypes.c_void_p * 2)(P, P + 2)
-    assert g(odd, 2, None, P, P, P, 4, 8, 1e-5, 1, S) == ALIGN
+    assert g(odd, 2, None, 1, P, 1, P, P, 4, 8, 1e-5, 1, S) == ALIGN
+    # a bf16 residual overlapping a float32 y (other than in place, same type)
+    assert g(arr, 2, P + 256, 1, P + 256, 0, P, P, 4, 8, 1e-5, 1, S) == SHAPE
 
 
 def _s2(*v):

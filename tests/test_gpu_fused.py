@@ -1,13 +1,19 @@
-"""The fused entry points against the oracle and, bit for bit, against the
-unfused calls they replace:
+"""The fused entry points against the oracle, and against the unfused calls
+they replace:
   * column_linear_act: the column-parallel gate|up (or fc1) projection with
     the rank-local activation in its epilogue (the activation needs no
-    exchange because gate_i and up_i live on the same rank);
+    exchange because gate_i and up_i live on the same rank).  The activation
+    is taken on the float32 sums, so the reference is the activation of the
+    EXACT projections; the unfused calls store g and u as bf16 first and are
+    checked against the activation of the rounded projections.
   * reduce_partials_rmsnorm: the all-reduce's sum of rank partials plus the
-    residual, followed by the next sub-block's pre-norm, in one pass.
+    residual, followed by the next sub-block's pre-norm, in one pass; equal
+    bit for bit to the two unfused calls, for every pair of residual and
+    output storage types.
 Shapes cover every dispatch of the fused linear (one and two 16-token tiles
-with 4, 8 and 16 waves splitting K, the 3-4 tile LDS-ring kernel, both tile
-sizes of the prefill kernel) with ragged token and feature counts."""
+with 4, 8 and 16 waves splitting K, the 3-4 tile LDS-ring kernel with one to
+four token row groups, both tile sizes of the prefill kernel) with ragged
+token and feature counts."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +21,7 @@ import torch
 import oracle.tp_oracle as O
 import tensor_transformer_layer_05_amd as tpl
 from tensor_transformer_layer_05_amd import inputs as I
-from util import assert_bitexact, assert_normwise, assert_within, U16, U32, log
+from util import assert_normwise, assert_within, U16, U32, log
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -39,6 +45,9 @@ ACT_SHAPES = [
     (5, 520, 130),       # ragged K range per wave, ragged rows
     (8, 8192, 3584),     # decode gate|up shard at 8 tokens: register kernel, 8 waves
     (13, 16384, 200),    # register kernel, 16 waves, ragged tokens
+    (4, 3584, 4096),     # LDS-ring kernel, one token tile, one 4-row token group (8192 rows)
+    (8, 3584, 4096),     # LDS-ring kernel, one token tile, two token row groups
+    (11, 3584, 4096),    # LDS-ring kernel, one token tile, three token row groups
     (17, 4096, 1000),    # two token tiles; the plain call (2000 rows) splits them over workgroups
     (32, 4096, 3584),    # two token tiles, two row tiles per wave
     (33, 1024, 300),     # LDS-ring kernel, three token tiles
@@ -55,6 +64,27 @@ ACT_SHAPES = [
 ]
 
 
+def _lip(act, g, u, ag, au):
+    """Bounds on |d act/d g| and |d act/d u| over the box g +- ag, u +- au:
+    SiLU' <= 1.0999 (its maximum, near g = 2.4), |SiLU(g)| <= |g| + 0.28,
+    and GELU' = Phi(g) + g phi(g) <= 1.1289 (its maximum, near g = 1.41)."""
+    if act == "swiglu":
+        return 1.0999 * (np.abs(u) + au), np.abs(g) + ag + 0.28
+    return 1.1289 + 0 * g, 0 * g
+
+
+def _act_bound(act, g, u, ref, ag, au):
+    """|h - act(g, u)| for h = RNE_bf16(fp32 act(g32, u32)), |g32 - g| <= ag,
+    |u32 - u| <= au: the perturbation of the arguments (mean value theorem in
+    each argument), the fp32 evaluation of the activation (relative error
+    below (8 + |g|^2 + |g|) fp32 units: the exponential or erfc argument's
+    rounding times its condition number), then one bf16 rounding."""
+    lg, lu = _lip(act, g, u, ag, au)
+    cond = 8 + np.abs(g) * np.abs(g) + np.abs(g)
+    e = (lg * ag + lu * au) * (1 + 1e-3) + cond * U32 * (np.abs(ref) + lg * ag + lu * au)
+    return U16 * (np.abs(ref) + e) + e + 1e-30
+
+
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
 @pytest.mark.parametrize("M,K,I_", ACT_SHAPES)
 def test_column_linear_act(act, M, K, I_):
@@ -64,30 +94,46 @@ def test_column_linear_act(act, M, K, I_):
     w = I.normal(40, "w", (rows, K), 1.5 / np.sqrt(K))   # activation arguments of O(1)
     X, W = dev(x), dev(w)
     h = tpl.column_linear_act(X, W, act)
-    assert_bitexact(h, _unfused(X, W, act, I_).double().cpu().numpy(), "fused == unfused")
+    ax = np.abs(x.ref)
     g = O.linear(x.ref, w.ref[:I_])
-    u = O.linear(x.ref, w.ref[I_:]) if act == "swiglu" else None
-    assert_normwise(h, O.local_activation(g, u, act), 1e-2, f"{act} vs oracle")
+    ag = 1.01 * K * U32 * (ax @ np.abs(w.ref[:I_]).T)     # fp32 accumulation of exact products
+    if act == "swiglu":
+        u = O.linear(x.ref, w.ref[I_:])
+        au = 1.01 * K * U32 * (ax @ np.abs(w.ref[I_:]).T)
+    else:
+        u, au = None, 0.0
+    ref = O.local_activation(g, u, act)
+    assert_within(h, ref, _act_bound(act, g, u if u is not None else 0 * g, ref, ag, au),
+                  f"fused {act} vs activation of the exact projections")
+    assert_normwise(h, ref, 1e-2, f"fused {act} vs oracle")
+    # the unfused calls round g and u to bf16 before the activation
+    hu = _unfused(X, W, act, I_)
+    agu = U16 * (np.abs(g) + ag) + ag
+    auu = U16 * (np.abs(u) + au) + au if act == "swiglu" else 0.0
+    assert_within(hu, ref, _act_bound(act, g, u if u is not None else 0 * g, ref, agu, auu),
+                  f"unfused {act} vs activation of the exact projections")
 
 
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
-@pytest.mark.parametrize("M,K,I_", [(1, 64, 40), (40, 136, 130), (200, 264, 300)])
+@pytest.mark.parametrize("M,K,I_", [(1, 64, 40), (40, 136, 130), (200, 264, 300), (11, 264, 4096)])
 def test_column_linear_act_integer(act, M, K, I_):
-    """Integer inputs: the projections are exact, so the only roundings are
-    the bf16 store of each projection and of the activation."""
+    """Integer inputs: every projection is an exact integer in float32, so the
+    fused route's only roundings are the fp32 activation and one bf16 store;
+    the unfused route first stores g and u as bf16 (integers above 256 round)."""
     log(f"column_linear_act int {act} M={M} K={K} I={I_}")
     rows = 2 * I_ if act == "swiglu" else I_
     x = I.uniform_int(41, "x", (M, K), -2, 2, dtype=torch.bfloat16)
     w = I.uniform_int(41, "w", (rows, K), -1, 1, dtype=torch.bfloat16)
     X, W = dev(x), dev(w)
-    h = tpl.column_linear_act(X, W, act)
-    assert_bitexact(h, _unfused(X, W, act, I_).double().cpu().numpy(), "fused == unfused")
-    g = O.round_bf16(O.linear(x.ref, w.ref[:I_]))
-    u = O.round_bf16(O.linear(x.ref, w.ref[I_:])) if act == "swiglu" else None
-    ref = O.local_activation(g, u, act)
-    # fp32 evaluation of the activation on exact bf16 arguments, then one bf16 rounding
-    cond = 8 + np.abs(g) * np.abs(g) + np.abs(g)
-    assert_within(h, ref, (U16 * (1 + 1e-5) + cond * U32) * np.abs(ref) + 1e-30, act)
+    g = O.linear(x.ref, w.ref[:I_])
+    u = O.linear(x.ref, w.ref[I_:]) if act == "swiglu" else None
+    for name, h, gg, uu in (
+            ("fused", tpl.column_linear_act(X, W, act), g, u),
+            ("unfused", _unfused(X, W, act, I_), O.round_bf16(g),
+             O.round_bf16(u) if u is not None else None)):
+        ref = O.local_activation(gg, uu, act)
+        cond = 8 + np.abs(gg) * np.abs(gg) + np.abs(gg)
+        assert_within(h, ref, (U16 * (1 + 1e-5) + cond * U32) * np.abs(ref) + 1e-30, f"{name} {act}")
 
 
 def test_column_linear_act_none_is_column_linear():
@@ -107,35 +153,47 @@ def test_column_linear_act_rejects_unsupported():
         tpl.column_linear_act(xf, wf, "gelu")
 
 
+_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
 @pytest.mark.parametrize("R", [1, 2, 8])
 @pytest.mark.parametrize("M,N", [(1, 8192), (7, 4096), (300, 1024), (3, 8), (5, 100), (2, 14344), (2, 20480)])
-@pytest.mark.parametrize("residual", [True, False])
-def test_reduce_partials_rmsnorm(R, M, N, residual):
-    log(f"reduce_partials_rmsnorm R={R} M={M} N={N} residual={residual}")
+@pytest.mark.parametrize("res,ydt", [(None, "bf16"), ("bf16", "bf16"), ("bf16", "f32"),
+                                     ("f32", "f32"), ("f32", "bf16"), (None, "f32")])
+def test_reduce_partials_rmsnorm(R, M, N, res, ydt):
+    """The layer's step after the attention partials: a bf16 input x plus the
+    partials into a float32 residual stream h, and h normalised to bf16 (the
+    ("bf16", "f32") case); the other storage pairs take the same kernels."""
+    log(f"reduce_partials_rmsnorm R={R} M={M} N={N} residual={res} y={ydt}")
     parts = [I.normal(43, "p", (M, N), 1.0, dtype=torch.float32, rank=r) for r in range(R)]
-    res = I.normal(43, "res", (M, N), 2.0) if residual else None
+    resid = I.normal(43, "res", (M, N), 2.0, dtype=_DT[res]) if res else None
     gam = I.normal(43, "gamma", (N,), 1.0)
     P = [dev(p) for p in parts]
-    RES = dev(res) if residual else None
+    RES = dev(resid) if res else None
     G = dev(gam)
-    y, yn = tpl.reduce_partials_rmsnorm(P, G, residual=RES, eps=1e-5)
-    y2 = tpl.reduce_partials(P, residual=RES, out_dtype=torch.bfloat16)
+    y, yn = tpl.reduce_partials_rmsnorm(P, G, residual=RES, eps=1e-5, out_dtype=_DT[ydt])
+    assert y.dtype == _DT[ydt] and yn.dtype == torch.bfloat16
+    y2 = tpl.reduce_partials(P, residual=RES, out_dtype=_DT[ydt])
     yn2 = tpl.rmsnorm(y2, G, 1e-5)
     assert torch.equal(y, y2), "sum differs from tp_reduce_partials"
     assert torch.equal(yn, yn2), "norm differs from tp_rmsnorm"
-    ref_y = O.reduce_partials([p.ref for p in parts], residual=res.ref if residual else None)
-    assert_normwise(y, ref_y, 1e-2, "sum vs oracle")
+    ref_y = O.reduce_partials([p.ref for p in parts], residual=resid.ref if res else None)
+    ay = sum(np.abs(p.ref) for p in parts) + (np.abs(resid.ref) if res else 0)
+    uy = U16 if ydt == "bf16" else U32
+    bound_y = uy * (np.abs(ref_y) + R * U32 * ay) + (R + 1) * U32 * ay + 1e-30
+    assert_within(y, ref_y, bound_y, "sum vs oracle")
     assert_normwise(yn, O.rmsnorm(ref_y, gam.ref, 1e-5), 1e-2, "norm vs oracle")
 
 
-def test_reduce_partials_rmsnorm_in_place_residual():
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_reduce_partials_rmsnorm_in_place_residual(dt):
     """y may be the residual buffer itself (the residual stream updated in
-    place)."""
+    place) when the two share a storage type."""
     M, N = 33, 2048
     P = [dev(I.normal(44, "p", (M, N), 1.0, dtype=torch.float32, rank=r)) for r in range(4)]
-    res = dev(I.normal(44, "res", (M, N)))
+    res = dev(I.normal(44, "res", (M, N), dtype=dt))
     G = dev(I.normal(44, "gamma", (N,)))
-    y, yn = tpl.reduce_partials_rmsnorm(P, G, residual=res.clone())
+    y, yn = tpl.reduce_partials_rmsnorm(P, G, residual=res.clone(), out_dtype=dt)
     buf = res.clone()
     y2, yn2 = tpl.reduce_partials_rmsnorm(P, G, residual=buf, out=buf)
     assert y2.data_ptr() == buf.data_ptr()

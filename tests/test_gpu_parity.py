@@ -64,7 +64,8 @@ INT_SHAPES = [
     # 4..16 tokens on short weights (fewer than 64 ring workgroups): register kernel
     (4, 1000, 300), (8, 4096, 1536), (13, 3584, 700),
     # LDS-ring kernel, one token tile: only the 4-token groups that hold tokens are loaded
-    (6, 3584, 8192), (13, 1000, 2500),
+    # (one, two and three of them)
+    (4, 3584, 8192), (6, 3584, 8192), (11, 3584, 8192), (13, 1000, 2500),
     # MFMA tile path: ragged M/N/K, each tile shape
     (65, 64, 16), (200, 136, 130), (300, 520, 300), (512, 264, 640), (4000, 264, 4000),
     (4096, 200, 2048), (4000, 136, 5100),   # the last picks 256x320 tiles
@@ -181,6 +182,19 @@ def test_rmsnorm(M, N, dtype):
     assert_within(y, ref, rt * np.abs(ref) + 1e-30, "rmsnorm")
 
 
+@pytest.mark.parametrize("M,N", [(1, 8), (7, 8192), (300, 4096), (3, 100), (2, 16392), (2, 20000)])
+def test_rmsnorm_f32_stream(M, N):
+    """A float32 residual stream normalised into bf16 (the second pre-norm of
+    a layer whose residual stream is kept in float32)."""
+    log(f"rmsnorm f32 -> bf16 M={M} N={N}")
+    x = I.normal(14, "x32", (M, N), 2.0, dtype=torch.float32)
+    g = I.normal(14, "g", (N,), 1.0)
+    ref = O.rmsnorm(x.ref, g.ref, 1e-5)
+    y = tpl.rmsnorm(dev(x), dev(g), 1e-5)
+    assert y.dtype == torch.bfloat16
+    assert_within(y, ref, U16 * (1 + 1e-4) * np.abs(ref) + 1e-30, "rmsnorm f32 -> bf16")
+
+
 @pytest.mark.parametrize("R", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("M,N", [(4, 64), (33, 130), (2048, 1536)])
 def test_reduce_integer_exact(R, M, N):
@@ -196,6 +210,25 @@ def test_reduce_integer_exact(R, M, N):
     y = tpl.reduce_partials(P, residual=dev(res16))
     assert_bitexact(y, O.round_bf16(O.reduce_partials([p.ref for p in parts], residual=res16.ref)),
                     "sum + residual bf16")
+    # mixed storage: a bf16 layer input summed into a float32 residual stream,
+    # and a float32 residual stream summed into a bf16 layer output
+    y = tpl.reduce_partials(P, residual=dev(res16), out_dtype=torch.float32)
+    assert y.dtype == torch.float32
+    assert_bitexact(y, O.reduce_partials([p.ref for p in parts], residual=res16.ref),
+                    "sum + residual bf16 -> fp32")
+    y = tpl.reduce_partials(P, residual=dev(res32), out_dtype=torch.bfloat16)
+    assert y.dtype == torch.bfloat16
+    assert_bitexact(y, O.round_bf16(ref_r), "sum + residual fp32 -> bf16")
+
+
+def test_reduce_rejects_mixed_alias():
+    """A bf16 output written over a float32 residual would clobber residual
+    values other threads still read: rejected before any launch."""
+    P = [torch.ones((8, 64), device=DEV)]
+    res = torch.ones((8, 64), device=DEV)
+    out = res.view(-1).view(torch.bfloat16)[:512].view(8, 64)   # contiguous, inside res
+    with pytest.raises(tpl.TPError):
+        tpl.reduce_partials(P, residual=res, out=out)
 
 
 def test_reduce_rank_order():
@@ -238,7 +271,9 @@ def test_attention_decode(B, Skv, Hq, Hkv):
 @pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,causal", [
     (1, 300, 300, 4, 2, True), (2, 70, 200, 8, 1, True), (1, 100, 130, 4, 4, False),
     (1, 513, 513, 2, 1, True), (1, 64, 64, 8, 8, True), (2, 1, 200, 16, 1, True),
-    (1, 1024, 1024, 8, 2, True)])
+    (1, 1024, 1024, 8, 2, True),
+    # one query row with more than 32 q heads per KV head: the prefill kernel
+    (3, 1, 300, 64, 1, True), (2, 1, 2048, 48, 1, True), (1, 1, 77, 40, 1, False)])
 def test_attention_prefill(B, Sq, Skv, Hq, Hkv, causal):
     log(f"attention prefill B={B} Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv} causal={causal}")
     D = 128
@@ -249,6 +284,66 @@ def test_attention_prefill(B, Sq, Skv, Hq, Hkv, causal):
     o = tpl.local_attention(dev(q), dev(k), dev(v), causal=causal)
     assert_within(o, ref, _attn_bound(ref, v.ref), "prefill attention")
     assert_normwise(o, ref, 1e-2, "prefill attention")
+
+
+def _kv_view(t2, strides, numel=None):
+    """The [B, Skv, Hkv, D] values of ``t2`` placed at element strides
+    ``strides`` (b, t, j) of a flat device buffer, as a strided view.  With a
+    key stride below D consecutive keys share elements: the view is then
+    filled from a flat random buffer instead and the oracle gets its values."""
+    B, Skv, Hkv, D = t2.dev.shape
+    s0, s1, s2 = strides
+    n = numel or ((B - 1) * s0 + (Skv - 1) * s1 + (Hkv - 1) * s2 + D)
+    buf = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    view = buf.as_strided((B, Skv, Hkv, D), (s0, s1, s2, 1))
+    view.copy_(t2.dev.to(DEV))
+    return buf, view
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,causal", [
+    (1, 300, 300, 4, 2, True), (2, 70, 200, 8, 1, True), (1, 100, 130, 4, 4, False)])
+def test_attention_prefill_overlapping_keys(B, Sq, Skv, Hq, Hkv, causal):
+    """Key rows closer together than D elements (each key shares half its
+    elements with the next): a valid read-only view that the transposed-score
+    kernel cannot stage, so the call takes the register-staged prefill kernel."""
+    log(f"attention prefill, key stride < D: B={B} Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv}")
+    D = 128
+    s1, s2 = 64, 24
+    s0 = (Skv - 1) * s1 + (Hkv - 1) * s2 + D + 40
+    q = I.normal(18, "q", (B, Sq, Hq, D))
+    n = (B - 1) * s0 + (Skv - 1) * s1 + (Hkv - 1) * s2 + D
+    kf = I.normal(18, "kflat", (n,))
+    vf = I.normal(18, "vflat", (n,))
+    kv = [t.dev.as_strided((B, Skv, Hkv, D), (s0, s1, s2, 1)) for t in (kf, vf)]
+    kref, vref = (t.to(torch.float64).numpy() for t in kv)
+    K, V = kf.dev.to(DEV), vf.dev.to(DEV)
+    k = K.as_strided((B, Skv, Hkv, D), (s0, s1, s2, 1))
+    v = V.as_strided((B, Skv, Hkv, D), (s0, s1, s2, 1))
+    ref = O.attention(q.ref, kref, vref, causal=causal)
+    o = tpl.local_attention(dev(q), k, v, causal=causal)
+    assert_within(o, ref, _attn_bound(ref, vref), "prefill attention, overlapping keys")
+    assert_normwise(o, ref, 1e-2, "prefill attention, overlapping keys")
+
+
+def test_attention_prefill_long_key_span():
+    """A key span past 2^31 bytes (4 MiB between consecutive keys, as in a
+    very long sequence read through a wide fused-QKV view): 64-bit addressing
+    in the register-staged prefill kernel."""
+    B, S, Hq, Hkv, D = 1, 600, 4, 2, 128
+    s1 = (1 << 21) + 8
+    log(f"attention prefill, key span {(S - 1) * s1 * 2 / 2**30:.2f} GiB")
+    q = I.normal(20, "q", (B, S, Hq, D))
+    k = I.normal(20, "k", (B, S, Hkv, D))
+    v = I.normal(20, "v", (B, S, Hkv, D))
+    strides = ((S - 1) * s1 + Hkv * D, s1, D)
+    kb, kview = _kv_view(k, strides)
+    vb, vview = _kv_view(v, strides)
+    assert (S - 1) * s1 * 2 >= 2 ** 31
+    ref = O.attention(q.ref, k.ref, v.ref, causal=True)
+    o = tpl.local_attention(dev(q), kview, vview, causal=True)
+    del kb, vb, kview, vview
+    assert_within(o, ref, _attn_bound(ref, v.ref), "prefill attention, long key span")
+    assert_normwise(o, ref, 1e-2, "prefill attention, long key span")
 
 
 @pytest.mark.parametrize("scale", [0.2, -0.05, 0.0])

@@ -169,6 +169,13 @@ def check_activations():
     g = np.array([1.0, -2.0]); u = np.array([3.0, 5.0])
     assert np.allclose(O.local_activation(g, u, "swiglu"), O.silu(g) * u)
     assert np.array_equal(O.local_activation(g, None, "none"), g)
+    # the GELU dispatch against textbook normal-CDF values (independent of gelu())
+    got = O.local_activation(np.array([1.0, 2.0, -1.0, -10.0, 0.0]), None, "gelu")
+    want = np.array([PHI_1, 2 * PHI_2, -(1 - PHI_1), -10.0 * PHI_M10, 0.0])
+    assert np.allclose(got, want, rtol=1e-10, atol=0.0)
+    # and the SwiGLU dispatch against sigma(ln 3) = 3/4
+    assert math.isclose(float(O.local_activation(np.array([math.log(3.0)]), np.array([2.0]),
+                                                 "swiglu")[0]), 1.5 * math.log(3.0), rel_tol=1e-15)
 
 
 def test_activations():
@@ -514,6 +521,32 @@ def test_vocab_argmax():
 # bf16 rounding used by the storage-faithful mode
 # ---------------------------------------------------------------------------
 
+def test_bf16_storage_policy():
+    """The diagnostic storage policy rounds exactly the named intermediates."""
+    a = np.array([1.0 + 2.0 ** -8 + 2.0 ** -20, -3.0000001])
+    everything = O.bf16_storage()
+    only_a = O.bf16_storage("a")
+    for name in O.STORED:
+        assert np.array_equal(everything(name, a), O.round_bf16(a))
+        assert np.array_equal(only_a(name, a), O.round_bf16(a) if name == "a" else a)
+    with pytest.raises(ValueError):
+        O.bf16_storage("g")
+    with pytest.raises(ValueError):
+        only_a("u", a)
+    # in a layer, rounding nothing equals the exact default; rounding the
+    # activation changes the MLP partial by at most its bf16 rounding through Wd
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 16)); wg = rng.standard_normal((8, 16)) / 4
+    wu = rng.standard_normal((8, 16)) / 4; wd = rng.standard_normal((16, 8)) / 4
+    exact = O.mlp_rank_partial(x, wg, wd, "swiglu", 0, 1, w_up=wu)
+    assert np.array_equal(O.mlp_rank_partial(x, wg, wd, "swiglu", 0, 1, w_up=wu,
+                                             store=O.bf16_storage("xn")), exact)
+    a_exact = O.local_activation(x @ wg.T, x @ wu.T, "swiglu")
+    stored = O.mlp_rank_partial(x, wg, wd, "swiglu", 0, 1, w_up=wu, store=O.bf16_storage("a"))
+    assert np.allclose(stored, O.round_bf16(a_exact) @ wd.T, rtol=0, atol=1e-12)
+    assert not np.array_equal(stored, exact)
+
+
 def test_round_bf16():
     assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0                      # tie -> even
     assert O.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6      # tie -> even (up)
@@ -645,7 +678,16 @@ def _mut_paged_swapped(pool, table_row, length, block_size):
     return np.stack(rows, axis=0)
 
 
+_orig_local_activation = O.local_activation
+
+
+def _mut_activation_gelu_as_silu(g, u=None, act="swiglu"):
+    # the GELU branch dispatching to SiLU
+    return O.silu(g) if act == "gelu" else _orig_local_activation(g, u, act)
+
+
 MUTATIONS = [
+    ("local_activation", _mut_activation_gelu_as_silu),
     ("paged_gather", _mut_paged_swapped),
     ("kv_heads_of_rank", _mut_kv_heads_modulo),
     ("vocab_argmax_local", _mut_argmax_last),
