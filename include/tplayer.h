@@ -199,6 +199,30 @@ tp_status tp_decode_attention_append(const void* q, const int64_t qs[2],
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * tp_decode_attention_append without the workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The chunk partials go to a buffer
+ * the library owns: a static device array of 8,486,400 bytes on each GPU the
+ * call runs on, kept until the process ends.  That size covers every call this
+ * entry point accepts (a key span is split only for at most 255 (sequence, KV
+ * head) pairs); a request needing more returns TP_ERR_WORKSPACE.  The call
+ * allocates nothing, and needs no clearing between calls (every partial it
+ * reads was written earlier in the same call).
+ * All calls on one GPU share that buffer: calls that overlap in time on one
+ * GPU (e.g. on two streams) race and give undefined results; serialise them.
+ * Results equal tp_decode_attention_append's bit for bit.  Every other
+ * argument, limit and error as tp_decode_attention_append; TP_ERR_HIP if the
+ * buffer's device address cannot be obtained.
+ */
+tp_status tp_decode_attention_append_noalloc(const void* q, const int64_t qs[2],
+                                             const void* k_new, const void* v_new,
+                                             int64_t new_stride, void* k_cache, void* v_cache,
+                                             const int64_t cs[3], int64_t T, int64_t pos, void* o,
+                                             const int64_t os[2], int64_t B, int64_t Hq,
+                                             int64_t Hkv, int64_t D, float scale, tp_dtype dt,
+                                             void* stream);
+
+/*
  * The arithmetic of the all-reduce after a row-parallel linear (P1 "Row
  * Parallel Linear": the partial outputs are summed; P2 section 二
  * all_reduce(output); P3: partials must be summed, not concatenated),

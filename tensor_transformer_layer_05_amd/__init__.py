@@ -11,7 +11,8 @@ Entry points (same names as the C ABI, without the ``tp_`` prefix):
 ``column_linear``, ``column_linear_act``, ``row_linear_partial``,
 ``swiglu_local``, ``local_attention``, ``kv_append``, ``reduce_partials``,
 ``reduce_partials_rmsnorm``, ``rmsnorm``, ``paged_attention_decode``,
-``paged_kv_append``, ``decode_attention_append``, ``paged_decode_attention_append``,
+``paged_kv_append``, ``decode_attention_append``, ``decode_attention_append_noalloc``,
+``paged_decode_attention_append``,
 ``vocab_argmax_local``, ``vocab_argmax_reduce``.
 Weights use the nn.Linear layout ``[out_features, in_features]``.
 """
@@ -28,7 +29,7 @@ __all__ = [
     "local_attention", "local_attention_workspace", "kv_append", "reduce_partials",
     "reduce_partials_rmsnorm", "rmsnorm", "vocab_argmax_local", "vocab_argmax_reduce",
     "paged_attention_decode", "paged_attention_workspace", "paged_kv_append",
-    "decode_attention_append", "paged_decode_attention_append",
+    "decode_attention_append", "decode_attention_append_noalloc", "paged_decode_attention_append",
     "shard_column", "shard_row", "shard_qkv", "kv_heads_of_rank", "kv_cache_bytes_per_rank",
     "F32", "BF16", "ACT_NONE", "ACT_SWIGLU", "ACT_GELU",
 ]
@@ -77,6 +78,10 @@ _SIGS = {
                                                   _i64, _vp, _i64p, _i64, _i64, _i64, _i64,
                                                   ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t,
                                                   _vp]),
+    "tp_decode_attention_append_noalloc": (ctypes.c_int, [_vp, _i64p, _vp, _vp, _i64, _vp, _vp,
+                                                          _i64p, _i64, _i64, _vp, _i64p, _i64, _i64,
+                                                          _i64, _i64, ctypes.c_float, ctypes.c_int,
+                                                          _vp]),
     "tp_paged_decode_attention_append": (ctypes.c_int, [_vp, _i64p, _vp, _vp, _i64, _vp, _vp, _i64p,
                                                         _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64p,
                                                         _i64, _i64, _i64, _i64, ctypes.c_float,
@@ -350,6 +355,21 @@ def decode_attention_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check("tp_decode_attention_append", lib().tp_decode_attention_append(
         *args, workspace.data_ptr() if need else None, need, _stream(q)))
+    return out
+
+
+def decode_attention_append_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                    k_cache: torch.Tensor, v_cache: torch.Tensor, pos: int,
+                                    out: torch.Tensor, scale: float | None = None):
+    """``decode_attention_append`` with no workspace: the library keeps the
+    split-key partials in its own static device buffer, so the call allocates
+    nothing (``out`` must be given).  Calls overlapping in time on one GPU
+    share that buffer and must not be issued."""
+    if out is None:
+        raise ValueError("out must be given (the call allocates nothing)")
+    out, args, _ = _decode_append_args(q, k_new, v_new, k_cache, v_cache, pos, scale, out)
+    _check("tp_decode_attention_append_noalloc",
+           lib().tp_decode_attention_append_noalloc(*args, _stream(q)))
     return out
 
 

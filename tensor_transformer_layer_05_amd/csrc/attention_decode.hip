@@ -42,6 +42,8 @@
 // the attention depending on the store.
 #include <algorithm>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace tpl {
@@ -501,6 +503,62 @@ tp_status attn_decode_paged(const void* q, const int64_t qs[2], const void* kp, 
   hipLaunchKernelGGL(attn_decode_kernel<true>, dim3(a.nsplit, a.Hkv, B), dim3(256), 0, s, a);
   if (a.ws) hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.Hq, B), dim3(128), 0, s, a, (int)B);
   TPL_LAUNCH_CHECK("attn_decode_paged");
+  return TP_OK;
+}
+
+// ---- a library-owned partials buffer for callers that cannot allocate ----------
+
+// attn_decode_workspace over every call the contiguous decode entry points
+// accept is at most this: a call splits its key span only when it has at most
+// 255 (sequence, KV head) pairs, into at most ceil(256 / pairs) chunks each,
+// so B * Hkv * nsplit <= 510 and B * Hq * nsplit <= 32 * 510 partial rows of
+// (2 + 128) floats (8,486,400 bytes).
+constexpr size_t kDecScratchBytes = size_t(kDecMaxG) * 510 * (2 + kDecD) * sizeof(float);
+
+// Every call of the allocation-free entry point on a GPU uses that GPU's copy
+// of this array (held until the process ends).  The chunk partials are fully
+// written by the attention kernel before the combine kernel reads them, so
+// nothing in it needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[kDecScratchBytes];
+
+// Device address of `scratch` on the device of stream s (the current device
+// for the null stream).  The address is looked up once per device, with that
+// device current, and kept; host code never passes the array's name itself.
+tp_status attn_decode_scratch(hipStream_t s, void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) { set_hip_error("hipGetDevice", e); return TP_ERR_HIP; }
+  int dev = cur;
+  if (s != nullptr) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(s, &d);
+    if (e != hipSuccess) { set_hip_error("hipStreamGetDevice", e); return TP_ERR_HIP; }
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return TP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) {
+      set_hip_error("hipSetDevice", e);
+      return TP_ERR_HIP;
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || p == nullptr) {
+      set_hip_error("hipGetSymbolAddress(scratch)", e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return TP_ERR_HIP;
+    }
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kDecScratchBytes;
   return TP_OK;
 }
 

@@ -42,6 +42,7 @@ tp_status attn_prefill_tr(const void* q, const int64_t qs[3], const void* k, con
                           hipStream_t s);
 bool attn_prefill_tr_ok(const int64_t kvs[3], int64_t Skv, int64_t D);
 size_t attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv);
+tp_status attn_decode_scratch(hipStream_t s, void** ptr, size_t* bytes);
 tp_status attn_prefill(const void* q, const int64_t qs[3], const void* k, const void* v,
                        const int64_t kvs[3], void* o, const int64_t os[3], int64_t B, int64_t Sq,
                        int64_t Skv, int64_t Hq, int64_t Hkv, int causal, float scale,
@@ -220,12 +221,15 @@ tp_status tp_kv_append(const void* k_new, const void* v_new, int64_t new_stride,
                         as_stream(stream));
 }
 
-tp_status tp_decode_attention_append(const void* q, const int64_t qs[2], const void* k_new,
-                                     const void* v_new, int64_t new_stride, void* k_cache,
-                                     void* v_cache, const int64_t cs[3], int64_t T, int64_t pos,
-                                     void* o, const int64_t os[2], int64_t B, int64_t Hq,
-                                     int64_t Hkv, int64_t D, float scale, tp_dtype dt,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+// The decode step's append + attention; `own_scratch` takes the partials
+// buffer from the library's static array instead of `workspace`.
+static tp_status decode_append_common(const void* q, const int64_t qs[2], const void* k_new,
+                                      const void* v_new, int64_t new_stride, void* k_cache,
+                                      void* v_cache, const int64_t cs[3], int64_t T, int64_t pos,
+                                      void* o, const int64_t os[2], int64_t B, int64_t Hq,
+                                      int64_t Hkv, int64_t D, float scale, tp_dtype dt,
+                                      void* workspace, size_t workspace_bytes, bool own_scratch,
+                                      void* stream) {
   if (!q || !qs || !k_new || !v_new || !k_cache || !v_cache || !cs || !o || !os) return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return TP_ERR_SHAPE;
@@ -249,12 +253,36 @@ tp_status tp_decode_attention_append(const void* q, const int64_t qs[2], const v
   // the kernel addresses one sequence's key span with 32-bit offsets
   if ((pos * cs[1] + D) * 2 >= (int64_t{1} << 31)) return TP_ERR_UNSUPPORTED;
   const size_t need = tpl::attn_decode_workspace(B, Hq, Hkv, Skv);
+  if (own_scratch && need > 0) {
+    const tp_status st = tpl::attn_decode_scratch(as_stream(stream), &workspace, &workspace_bytes);
+    if (st != TP_OK) return st;
+  }
   if (need > 0 && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return TP_ERR_ALIGN;
   const int64_t q3[3] = {qs[0], 0, qs[1]}, o3[3] = {os[0], 0, os[1]};
   return tpl::attn_decode(q, q3, k_cache, v_cache, cs, o, o3, B, Skv, Hq, Hkv, scale,
                           need > 0 ? workspace : nullptr, as_stream(stream), k_new, v_new,
                           new_stride);
+}
+
+tp_status tp_decode_attention_append(const void* q, const int64_t qs[2], const void* k_new,
+                                     const void* v_new, int64_t new_stride, void* k_cache,
+                                     void* v_cache, const int64_t cs[3], int64_t T, int64_t pos,
+                                     void* o, const int64_t os[2], int64_t B, int64_t Hq,
+                                     int64_t Hkv, int64_t D, float scale, tp_dtype dt,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_append_common(q, qs, k_new, v_new, new_stride, k_cache, v_cache, cs, T, pos, o, os,
+                              B, Hq, Hkv, D, scale, dt, workspace, workspace_bytes, false, stream);
+}
+
+tp_status tp_decode_attention_append_noalloc(const void* q, const int64_t qs[2], const void* k_new,
+                                             const void* v_new, int64_t new_stride, void* k_cache,
+                                             void* v_cache, const int64_t cs[3], int64_t T,
+                                             int64_t pos, void* o, const int64_t os[2], int64_t B,
+                                             int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                                             tp_dtype dt, void* stream) {
+  return decode_append_common(q, qs, k_new, v_new, new_stride, k_cache, v_cache, cs, T, pos, o, os,
+                              B, Hq, Hkv, D, scale, dt, nullptr, 0, true, stream);
 }
 
 tp_status tp_reduce_partials(const float* const* partials, int64_t R, const void* residual,

@@ -336,6 +336,23 @@ def test_decode_attention_append_validation(lib):
     assert call(B=1, T=4096, pos=4095, cs=big) == WORKSPACE
     assert call(B=1, T=4096, pos=4095, cs=big, ws=P, wsb=need - 1) == WORKSPACE
 
+    # the allocation-free form: the same host validation (these cases all fail
+    # before the library's buffer is looked up or anything is launched)
+    h = lib.tp_decode_attention_append_noalloc
+
+    def ncall(q=P, kn=P, cs=cs, pos=10, Hq=8, Hkv=2, D=128, dt=1, ns=1536):
+        return h(q, _s2(1536, 128), kn, P, ns, P, P, cs, 64, pos, P, _s2(1024, 128), 2, Hq, Hkv, D,
+                 0.088, dt, S)
+
+    assert ncall(q=None) == NULL
+    assert ncall(dt=7) == DTYPE
+    assert ncall(Hq=6, Hkv=4) == SHAPE
+    assert ncall(pos=64) == SHAPE
+    assert ncall(ns=128) == SHAPE
+    assert ncall(Hq=66, Hkv=1) == UNSUPPORTED
+    assert ncall(D=64) == UNSUPPORTED
+    assert ncall(kn=P + 2) == ALIGN
+
     g = lib.tp_paged_decode_attention_append
     ps = _s3(16 * 2 * 128, 2 * 128, 128)
 
