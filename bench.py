@@ -16,7 +16,10 @@ Secondary figures (same line, key "decode"): the decode MLP shard at TP=8
 cache), the same attention at TP=16 with replicated KV heads and the vocab-parallel lm_head shard with its
 greedy argmax (TP=8), timed over rotating
 copies of the weights/caches so that the 256 MB Infinity Cache cannot hold
-the working set between steps (also as HIP-graph replays, "graph_ms").
+the working set between steps (also as HIP-graph replays, "graph_ms"), with the
+HBM bytes the same steps moved by the FETCH_SIZE/WRITE_SIZE counters
+(profiles/decode_traffic.md) and their rate relative to the attainable read
+rate of a plain read-only stream ("hbm_read_ceiling").
 Key "ffn_tp8": rank 0's shard of the GELU FFN at TP=8 (2048 tokens, hidden
 12288): fc1 with GELU in its epilogue, fc2, and the sum of 8 partials.
 """
@@ -36,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 import tensor_transformer_layer_05_amd as tpl  # noqa: E402
 from tensor_transformer_layer_05_amd import inputs as I  # noqa: E402
-from tensor_transformer_layer_05_amd.shard import AttnShard, LayerShard, MlpShard  # noqa: E402
+from tensor_transformer_layer_05_amd.shard import LayerShard  # noqa: E402
 
 METRIC = "TFLOP/s + HBM GB/s per TP-rank layer shard (decode M=1..64, prefill M=4096)"
 PEAK_BF16_TFLOPS = 2500.0
@@ -315,57 +318,68 @@ def _decode_entry(ms_eager, ms_graph, byts, fl):
             "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9, "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS}
 
 
-def decode_figures(steps=30, warmup=5, copies=4):
+# the kernels (and their dispatch) a decode shard runs: the counter summary
+# of their HBM bytes is used only while these sources still hash as recorded
+DECODE_SRCS = ["tensor_transformer_layer_05_amd/csrc/gemm_stream.hip",
+               "tensor_transformer_layer_05_amd/csrc/gemm_stream_dma.hip",
+               "tensor_transformer_layer_05_amd/csrc/attention_decode.hip",
+               "tensor_transformer_layer_05_amd/csrc/argmax.hip",
+               "tensor_transformer_layer_05_amd/csrc/tplayer_api.hip",
+               "tensor_transformer_layer_05_amd/csrc/common.h"]
+
+
+def read_ceiling(steps=10, warmup=3, nbytes=1 << 30):
+    """Attainable HBM read rate on this GPU: the hand-written read-only
+    stream of libtpref (16-byte loads per lane, chunks of 4-16 KB per wave with
+    the next chunk in flight, like the decode weight streams) over 1 GiB, for
+    several grid shapes; the best median rate is the ceiling the decode shards
+    are also compared with."""
+    from tensor_transformer_layer_05_amd import ref
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=DEV)
+    out = torch.empty(4096 * 16 * 64, dtype=torch.int32, device=DEV)
+    best, rows = None, []
+    for wg, waves, u in ((256, 8, 8), (512, 8, 8), (1024, 8, 4), (256, 16, 8), (512, 16, 4),
+                         (256, 8, 16), (2048, 4, 4)):
+        ms = _median_ms(lambda i: ref.stream_read(buf, out, wg, waves, u), steps, warmup)
+        gbs = nbytes / ms / 1e6
+        rows.append({"workgroups": wg, "waves": waves, "loads_per_lane": u, "GB/s": round(gbs, 1)})
+        if best is None or gbs > best["GB/s"]:
+            best = rows[-1]
+    del buf
+    return {"GB/s": best["GB/s"], "frac_of_peak": best["GB/s"] / PEAK_HBM_GBPS, "best": best,
+            "configs": rows, "bytes": nbytes}
+
+
+def decode_figures(steps=30, warmup=5, copies=4, ceiling=None):
     """Decode shards timed over ``copies`` rotating copies of the weights and
     caches (together larger than the 256 MB Infinity Cache).  ``eager_ms`` is
     the step issued call by call, ``graph_ms`` the same step replayed from a
-    captured HIP graph; ``ms`` and the rates use the faster of the two."""
+    captured HIP graph; ``ms`` and the rates use the faster of the two.
+    ``hbm_frac`` is algorithmic bytes over time; ``counter_hbm_frac`` the HBM
+    bytes the same step moved by the FETCH_SIZE/WRITE_SIZE counters (profiles/
+    decode_traffic.md, while the decode kernels' sources match) over time;
+    ``frac_of_read_ceiling`` algorithmic bytes over time relative to the
+    attainable read rate measured by ``read_ceiling``."""
+    from tensor_transformer_layer_05_amd.decode_workloads import all_decode
+    counted = recorded_profile("decode_traffic.md")
     out = {}
-    c = I.config("decode_mlp_tp8")
-    H, il = c.hidden, c.inter // c.tp
-    wg = I.normal(c.seed, "wg", (il, H), c.w_std).dev
-    wu = I.normal(c.seed, "wu", (il, H), c.w_std).dev
-    wd = I.normal(c.seed, "wd", (H, il), c.w_std).dev
-    wgu = torch.cat([wg, wu], 0)
-    mlps = [MlpShard(wgu.to(DEV).clone(), wd.to(DEV).clone(), "swiglu", 64) for _ in range(copies)]
-    wbytes = (wgu.numel() + wd.numel()) * 2
-    for M in c.tokens:
-        X = I.normal(c.seed, "x", (M, H)).dev.to(DEV)
-        Ps = [torch.empty((M, H), dtype=torch.float32, device=DEV) for _ in range(copies)]
-        fns = [(lambda j=j: mlps[j].partial(X, Ps[j])) for j in range(copies)]
-        gms = _graph_ms(fns, steps, warmup)
-        ms = _median_ms(lambda i: fns[i % copies](), steps, warmup)
-        # weights once, x read, act(g)*u written and read back, fp32 partial written
-        byts = wbytes + M * H * 2 + M * il * 2 * 2 + M * H * 4
-        fl = 2.0 * M * (H * 2 * il + il * H)
-        out[f"mlp_tp8_M{M}"] = _decode_entry(ms, gms, byts, fl)
-    del mlps
-    c = I.config("decode_attn_tp4")
-    H, R, D, B, L = c.hidden, c.tp, c.head_dim, c.batch, c.kv_len
-    hq, hkv = c.n_q // R, c.n_kv // R
-    x = I.normal(c.seed, "x", (B, H)).dev.to(DEV)
-    wqkv = I.normal(c.seed, "wqkv", ((hq + 2 * hkv) * D, H), c.w_std).dev
-    wo = I.normal(c.seed, "wo", (H, hq * D), c.w_std).dev
-    kc = I.normal(c.seed, "kcache", (B, hkv, L, D)).dev
-    vc = I.normal(c.seed, "vcache", (B, hkv, L, D)).dev
-    sets = []
-    for _ in range(copies):
-        sets.append((AttnShard(wqkv.to(DEV), wo.to(DEV), hq, hkv, D, B),
-                     kc.to(DEV), vc.to(DEV), torch.empty((B, H), dtype=torch.float32, device=DEV)))
-
-    def step(j):
-        a, k_, v_, P = sets[j]
-        a.decode_partial(x, k_.transpose(1, 2), v_.transpose(1, 2), L - 1, P)
-
-    fns = [(lambda j=j: step(j)) for j in range(copies)]
-    gms = _graph_ms(fns, steps, warmup)
-    ms = _median_ms(lambda i: fns[i % copies](), steps, warmup)
-    byts = (wqkv.numel() + wo.numel() + kc.numel() + vc.numel()) * 2 + B * H * 2 + B * H * 4
-    fl = 2.0 * B * H * (hq + 2 * hkv) * D + 4.0 * B * hq * L * D + 2.0 * B * hq * D * H
-    out["attn_tp4_B32_L2048"] = _decode_entry(ms, gms, byts, fl)
-    out["attn_tp16_rep_B32_L2048"] = _replicated_attn_figure(steps, warmup, copies)
-    out["attn_tp4_paged_B32_L2048"] = _paged_attn_figure(steps, warmup, copies)
-    out.update(_lm_head_figures(steps, warmup))
+    for build in all_decode(copies):
+        w = build()
+        n = len(w.steps)
+        gms = _graph_ms(w.steps, steps, warmup)
+        ms = _median_ms(lambda i: w.steps[i % n](), steps, warmup)
+        e = _decode_entry(ms, gms, w.bytes, w.flops)
+        e.update(w.extra)
+        if counted and w.name in counted.get("shards", {}):
+            cb = counted["shards"][w.name]["bytes"]
+            e["counter_bytes"] = cb
+            e["counter_hbm_frac"] = cb / e["ms"] / 1e6 / PEAK_HBM_GBPS
+        else:
+            e["counter_bytes"] = e["counter_hbm_frac"] = None
+        if ceiling:
+            e["frac_of_read_ceiling"] = e["GB/s"] / ceiling["GB/s"]
+        out[w.name] = e
+        del w
     return out
 
 
@@ -400,90 +414,6 @@ def ffn_figures(steps=20, warmup=3):
     }
     del parts
     return out
-
-
-def _lm_head_figures(steps, warmup, copies=2):
-    """Rank 0's vocab-parallel lm_head shard with its local greedy argmax
-    (128256-token vocab at TP 8: 16032 x 8192 bf16 rows, 263 MB per copy)."""
-    from tensor_transformer_layer_05_amd.shard import VocabShard
-    c = I.config("lm_head_tp8")
-    H, R, V = c.hidden, c.tp, c.extra["vocab"]
-    b = V // R
-    w = I.normal(c.seed, "w", (b, H), c.w_std, rank=0).dev
-    shards = [VocabShard(w.to(DEV), 0, max(c.tokens)) for _ in range(copies)]
-    out = {}
-    for M in c.tokens:
-        h = I.normal(c.seed, "h", (M, H)).dev.to(DEV)
-        ms = _median_ms(lambda i: shards[i % copies].local_greedy(h), steps, warmup)
-        byts = b * H * 2 + M * H * 2 + M * b * 4 * 2 + M * 12
-        fl = 2.0 * M * H * b
-        out[f"lm_head_tp8_M{M}"] = {"ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9,
-                                    "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS}
-    return out
-
-
-def _paged_attn_figure(steps, warmup, copies, bs=16):
-    """Rank 0's decode attention shard of config decode_attn_tp4 with a paged
-    cache: block size 16, physical blocks shuffled, every sequence at the full
-    2048 keys (the contiguous figure's byte count)."""
-    c = I.config("decode_attn_tp4")
-    H, R, D, B, L = c.hidden, c.tp, c.head_dim, c.batch, c.kv_len
-    hq, hkv = c.n_q // R, c.n_kv // R
-    nblk = L // bs
-    x = I.normal(c.seed, "x", (B, H)).dev.to(DEV)
-    wqkv = I.normal(c.seed, "wqkv", ((hq + 2 * hkv) * D, H), c.w_std).dev
-    wo = I.normal(c.seed, "wo", (H, hq * D), c.w_std).dev
-    kc = I.normal(c.seed, "kcache", (B * nblk, bs, hkv, D)).dev
-    vc = I.normal(c.seed, "vcache", (B * nblk, bs, hkv, D)).dev
-    table = torch.from_numpy(np.random.default_rng(c.seed).permutation(B * nblk).astype(np.int32))
-    table = table.reshape(B, nblk).to(DEV)
-    lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
-    sets = [(AttnShard(wqkv.to(DEV), wo.to(DEV), hq, hkv, D, B), kc.to(DEV), vc.to(DEV),
-             torch.empty((B, H), dtype=torch.float32, device=DEV)) for _ in range(copies)]
-
-    def step(j):
-        a, k_, v_, P = sets[j]
-        a.decode_partial_paged(x, k_, v_, table, lens, L, P)
-
-    fns = [(lambda j=j: step(j)) for j in range(copies)]
-    gms = _graph_ms(fns, steps, warmup)
-    ms = _median_ms(lambda i: fns[i % copies](), steps, warmup)
-    byts = (wqkv.numel() + wo.numel() + kc.numel() + vc.numel()) * 2 + B * H * 2 + B * H * 4
-    fl = 2.0 * B * H * (hq + 2 * hkv) * D + 4.0 * B * hq * L * D + 2.0 * B * hq * D * H
-    return _decode_entry(ms, gms, byts, fl)
-
-
-def _replicated_attn_figure(steps, warmup, copies):
-    """Rank 0's decode attention shard when KV heads are replicated (32 q / 8
-    KV heads at TP 16: 2 q heads and one KV head per rank)."""
-    c = I.config("decode_attn_tp16_rep")
-    H, R, D, B, L = c.hidden, c.tp, c.head_dim, c.batch, c.kv_len
-    hq = c.n_q // R
-    heads = tpl.kv_heads_of_rank(c.n_q, c.n_kv, 0, R)
-    x = I.normal(c.seed, "x", (B, H)).dev.to(DEV)
-    wq = I.normal(c.seed, "wq", (c.n_q * D, H), c.w_std).dev
-    wk = I.normal(c.seed, "wk", (c.n_kv * D, H), c.w_std).dev
-    wv = I.normal(c.seed, "wv", (c.n_kv * D, H), c.w_std).dev
-    wo = I.normal(c.seed, "wo", (H, c.n_q * D), c.w_std).dev
-    wqkv = tpl.shard_qkv(wq, wk, wv, 0, R, D)
-    wo0 = tpl.shard_row(wo, 0, R)
-    kc = I.normal(c.seed, "kcache", (B, c.n_kv, L, D)).dev[:, heads[0]:heads[0] + 1].contiguous()
-    vc = I.normal(c.seed, "vcache", (B, c.n_kv, L, D)).dev[:, heads[0]:heads[0] + 1].contiguous()
-    sets = [(AttnShard(wqkv.to(DEV), wo0.to(DEV), hq, len(heads), D, B), kc.to(DEV), vc.to(DEV),
-             torch.empty((B, H), dtype=torch.float32, device=DEV)) for _ in range(copies)]
-
-    def step(j):
-        a, k_, v_, P = sets[j]
-        a.decode_partial(x, k_.transpose(1, 2), v_.transpose(1, 2), L - 1, P)
-
-    fns = [(lambda j=j: step(j)) for j in range(copies)]
-    gms = _graph_ms(fns, steps, warmup)
-    ms = _median_ms(lambda i: fns[i % copies](), steps, warmup)
-    byts = (wqkv.numel() + wo0.numel() + kc.numel() + vc.numel()) * 2 + B * H * 2 + B * H * 4
-    fl = 2.0 * B * H * wqkv.shape[0] + 4.0 * B * hq * L * D + 2.0 * B * hq * D * H
-    e = _decode_entry(ms, gms, byts, fl)
-    e["kv_cache_bytes_per_rank"] = tpl.kv_cache_bytes_per_rank(c.n_q, c.n_kv, R, B, L, D)
-    return e
 
 
 # ---------------------------------------------------------------------------
@@ -549,8 +479,11 @@ def main(argv=None):
         "roofline": dom, "kernels": kernels,
     }
     if not a.no_decode:
+        log("measuring the attainable HBM read rate (reference stream)")
+        ceil_ = read_ceiling()
+        res["hbm_read_ceiling"] = ceil_
         log("timing decode shards")
-        res["decode"] = decode_figures()
+        res["decode"] = decode_figures(ceiling=ceil_)
     if not a.no_ffn:
         log("timing the GELU FFN shard at TP=8")
         res["ffn_tp8"] = ffn_figures()

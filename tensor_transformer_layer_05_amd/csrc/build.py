@@ -1,9 +1,12 @@
-"""Build libtplayer.so (HIP kernels + C ABI) for gfx950, in-tree.
+"""Build libtplayer.so (HIP kernels + C ABI) for gfx950, in-tree, and the
+measurement reference library libtpref.so (``ref/``: plain streaming kernels
+the layer's kernels are compared with).
 
     python -m tensor_transformer_layer_05_amd.csrc.build [--force] [--jobs N]
 
-Each .hip source is compiled to an object with hipcc, then all objects are
-linked into ``tensor_transformer_layer_05_amd/libtplayer.so``.  Objects live in
+Each .hip source is compiled to an object with hipcc, then the objects are
+linked into ``tensor_transformer_layer_05_amd/libtplayer.so`` (sources in this
+directory) and ``libtpref.so`` (sources in ``ref/``).  Objects live in
 ``_build/`` next to this file.  ``build(force=True)`` always recompiles.
 """
 from __future__ import annotations
@@ -20,6 +23,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libtplayer.so")
+REF_OUT = os.path.join(PKG, "libtpref.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
@@ -39,6 +43,10 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "*.hip")))
 
 
+def ref_sources():
+    return sorted(glob.glob(os.path.join(HERE, "ref", "*.hip")))
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
     cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
@@ -48,30 +56,35 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _link(objs, out):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
 def build(force: bool = True, jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library; returns its path."""
+    """Compile every HIP source and link both shared libraries; returns the
+    path of libtplayer.so."""
     os.makedirs(OBJDIR, exist_ok=True)
-    srcs = sources()
+    srcs, refs = sources(), ref_sources()
     headers = glob.glob(os.path.join(HERE, "*.h")) + glob.glob(os.path.join(ROOT, "include", "*.h"))
     newest_hdr = max((os.path.getmtime(h) for h in headers), default=0.0)
     todo = []
-    for s in srcs:
+    for s in srcs + refs:
         obj = os.path.join(OBJDIR, os.path.basename(s) + ".o")
         if force or not os.path.exists(obj) or os.path.getmtime(obj) < max(os.path.getmtime(s), newest_hdr):
             todo.append(s)
-    jobs = jobs or min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
+    jobs = jobs or min(len(srcs) + len(refs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
     if todo:
         with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
             for obj in ex.map(_compile, todo):
                 if verbose:
                     print("compiled", os.path.basename(obj))
-    objs = [os.path.join(OBJDIR, os.path.basename(s) + ".o") for s in srcs]
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    _link([os.path.join(OBJDIR, os.path.basename(s) + ".o") for s in srcs], OUT)
+    _link([os.path.join(OBJDIR, os.path.basename(s) + ".o") for s in refs], REF_OUT)
     return OUT
 
 

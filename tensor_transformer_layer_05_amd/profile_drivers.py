@@ -15,6 +15,19 @@ GEMM on the same operands (output [4096, 28672]).  Run it under
 rotating cache copies, for ``rocprofv3 --kernel-trace``: the kernel durations
 per span separate the fixed cost of a launch from the streaming rate.
 
+``decode_traffic``: the HBM bytes of each decode shard's step.  One plain
+256 MiB device-to-device copy (calibration), then for every decode shard of
+the benchmark, in its order (``decode_workloads.DECODE_NAMES``): its setup, a
+1 GiB read-only stream (``libtpref``; it evicts the caches and marks where the
+step's dispatches start), one step of the shard, and a 4 KiB read by the same
+stream kernel that marks where they end.  Run it under ``rocprofv3 --pmc
+FETCH_SIZE`` and, separately, ``--pmc WRITE_SIZE``; a shard's bytes are the
+sums over the dispatches between its two markers.
+
+``stream_ref``: 20 reads of 1 GiB by the reference stream kernel of
+``libtpref`` in the configuration the benchmark finds fastest, for
+``rocprofv3 --kernel-trace``.
+
 ``hbm_reference``: what plain streaming reaches on this GPU, next to the
 library's own decode weight stream: 20 device-to-device copies of 1 GiB, 20
 full sums of a 1 GiB float32 tensor (read only), then 20 one-token decode
@@ -100,7 +113,47 @@ def hbm_reference() -> None:
     print("hbm_reference done", flush=True)
 
 
-DRIVERS = {"gemm_traffic": gemm_traffic, "decode_attn_span": decode_attn_span, "hbm_reference": hbm_reference}
+def decode_traffic() -> None:
+    from . import ref
+    from .decode_workloads import all_decode
+    lib()
+    ref.lib()
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    words = torch.empty(256 * 8 * 64, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    for build in all_decode(copies=1):
+        w = build()
+        torch.cuda.synchronize()
+        ref.stream_read(flush, words)
+        torch.cuda.synchronize()
+        w.steps[0]()
+        torch.cuda.synchronize()
+        ref.stream_read(flush[:4096], words)
+        torch.cuda.synchronize()
+        print(f"decode_traffic {w.name} done", flush=True)
+        del w
+
+
+def stream_ref(workgroups: int = 256, waves: int = 8, loads: int = 8) -> None:
+    from . import ref
+    ref.lib()
+    buf = torch.ones(HBM_REF_BYTES, dtype=torch.uint8, device="cuda")
+    words = torch.empty(workgroups * waves * 64, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(HBM_REF_CALLS):
+        ref.stream_read(buf, words, workgroups, waves, loads)
+    torch.cuda.synchronize()
+    print("stream_ref done", flush=True)
+
+
+DRIVERS = {"gemm_traffic": gemm_traffic, "decode_attn_span": decode_attn_span, "hbm_reference": hbm_reference,
+           "decode_traffic": decode_traffic, "stream_ref": stream_ref}
 
 if __name__ == "__main__":
-    DRIVERS[sys.argv[1] if len(sys.argv) > 1 else "gemm_traffic"]()
+    name = sys.argv[1] if len(sys.argv) > 1 else "gemm_traffic"
+    DRIVERS[name](*[int(v) for v in sys.argv[2:]])

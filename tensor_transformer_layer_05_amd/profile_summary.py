@@ -284,19 +284,131 @@ python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
 """ + "\n".join(lines) + "\n"
 
 
+DECODE_SRCS = ["tensor_transformer_layer_05_amd/csrc/gemm_stream.hip",
+               "tensor_transformer_layer_05_amd/csrc/gemm_stream_dma.hip",
+               "tensor_transformer_layer_05_amd/csrc/attention_decode.hip",
+               "tensor_transformer_layer_05_amd/csrc/argmax.hip",
+               "tensor_transformer_layer_05_amd/csrc/tplayer_api.hip",
+               "tensor_transformer_layer_05_amd/csrc/common.h"]
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "").replace("tpl::", "")[:90]
+
+
+def decode_traffic(out):
+    from .decode_workloads import DECODE_NAMES
+    fetch, write = _counters(os.path.join(out, "pmc_dfetch")), _counters(os.path.join(out, "pmc_dwrite"))
+    fk, wk = sorted(fetch), sorted(write)
+    if [n for _, n in fk] != [n for _, n in wk]:
+        raise ValueError("the FETCH_SIZE and WRITE_SIZE runs dispatched different kernels")
+    cf = [fetch[k] for k in fk if "copyBuffer" in k[1]][0]
+    cw = [write[k] for k in wk if "copyBuffer" in k[1]][0]
+    fs, ws = 262144.0 / cf, 262144.0 / cw
+    # markers come in pairs around each measured step; what lies between an
+    # end marker and the next start marker is the next shard's setup
+    segs, cur, nmark = [], None, 0
+    for kf, kw in zip(fk, wk):
+        if "stream_read_kernel" in kf[1]:
+            nmark += 1
+            cur = [] if nmark % 2 == 1 else None
+            if cur is not None:
+                segs.append(cur)
+        elif cur is not None:
+            cur.append((_short(kf[1]), fetch[kf], write[kw]))
+    if len(segs) != len(DECODE_NAMES) or nmark != 2 * len(DECODE_NAMES):
+        raise ValueError(f"{len(segs)} marked segments for {len(DECODE_NAMES)} decode shards")
+    shards, rows = {}, []
+    for name, seg in zip(DECODE_NAMES, segs):
+        f = sum(v for _, v, _ in seg)
+        w = sum(v for _, _, v in seg)
+        byts = int((f * fs + w * ws) * 1024)
+        shards[name] = {"fetch_kib": round(f, 1), "write_kib": round(w, 1), "bytes": byts,
+                        "kernels": [k for k, _, _ in seg]}
+        for i, (k, a, b) in enumerate(seg):
+            rows.append(f"| {name if i == 0 else ''} | `{k}` | {a:.1f} | {b:.1f} |")
+        rows.append(f"| **{name} total** | | **{f:.1f}** | **{w:.1f}** |  -> {byts / 1e6:.2f} MB |")
+    h = hashlib.sha256()
+    for fn in DECODE_SRCS:
+        h.update(open(os.path.join(ROOT, fn), "rb").read())
+    data = {"sources": DECODE_SRCS, "sources_sha256_16": h.hexdigest()[:16],
+            "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "shards": shards}
+    stream = ""
+    tr = glob.glob(os.path.join(out, "prof_stream", "**", "*kernel_trace.csv"), recursive=True)
+    if tr:
+        t = [r for r in csv.DictReader(open(tr[0])) if "stream_read_kernel" in r["Kernel_Name"]]
+        d = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in t)
+        med = d[len(d) // 2]
+        stream = f"""
+## The read ceiling: the reference stream under the kernel trace
+
+```
+rocprofv3 --kernel-trace --output-format csv -d gpurun_out/prof_stream -o s -- python3 -m tensor_transformer_layer_05_amd.profile_drivers stream_ref 256 8 8
+```
+
+{len(d)} reads of 1 GiB by `stream_read_kernel<8>` (256 workgroups x 8 waves, 8 KB per wave per chunk, the next chunk
+in flight: the register GEMV's load width and bytes in flight): median {med:.1f} us = {2 ** 30 / med / 1e3:.0f} GB/s
+({2 ** 30 / med / 1e3 / 8000:.3f} of 8 TB/s); min {d[0]:.1f} us, max {d[-1]:.1f} us.
+"""
+        data["stream_ref_median_us"] = round(med, 2)
+        data["stream_ref_gbps"] = round(2 ** 30 / med / 1e3, 1)
+    return f"""# HBM bytes of each decode shard's step (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)
+
+Commands (from the repository root):
+
+```
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_dfetch -o f -- python3 -m tensor_transformer_layer_05_amd.profile_drivers decode_traffic
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_dwrite -o w -- python3 -m tensor_transformer_layer_05_amd.profile_drivers decode_traffic
+python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
+```
+
+The driver runs one plain 256 MiB copy (calibration: {cf:.1f} KiB fetched, {cw:.1f} KiB written for 262144 KiB
+each way, so FETCH_SIZE is scaled by {fs:.4f} and WRITE_SIZE by {ws:.4f}), then for each decode shard of the
+benchmark its setup, a 1 GiB read-only stream (evicts the caches, marks the step's start), one step of the
+shard, and a 4 KiB read by the same kernel (marks its end); the table lists the dispatches between the markers.
+FETCH_SIZE counts reads that leave an XCD's L2 (the Infinity Cache may still serve them): data read by
+workgroups on several XCDs (the activations, the token rows) is counted once per XCD.
+
+| shard | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB |
+|---|---|---:|---:|
+{chr(10).join(rows)}
+
+bench.py divides each shard's bytes by its measured step time (`counter_hbm_frac`) only while the decode
+kernels' sources still have the hash below.
+{stream}
+DATA {json.dumps(data)}
+"""
+
+
 def main(argv=None):
+    """``profile_summary <out_dir> [summary ...]``: write the named summaries
+    (gate_up_gemm_traffic, bench_kernel_stats, decode_traffic,
+    gate_up_gemm_counters, decode_attention_span, hbm_reference; default: all
+    whose raw outputs are present)."""
     argv = argv or sys.argv[1:]
     out = argv[0] if argv else "gpurun_out"
-    open(os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.md"), "w").write(traffic(out))
-    open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w").write(kernel_stats(out))
-    print("wrote profiles/gate_up_gemm_traffic.md and profiles/bench_kernel_stats.md")
-    if glob.glob(os.path.join(out, "pmc_mfma", "**", "*counter_collection.csv"), recursive=True):
+    only = set(argv[1:])
+    raw = lambda d, pat: glob.glob(os.path.join(out, d, "**", pat), recursive=True)
+    has = lambda name, d, pat: (not only or name in only) and raw(d, pat)
+    if has("gate_up_gemm_traffic", "pmc_fetch", "*counter_collection.csv") and \
+            raw("pmc_write", "*counter_collection.csv"):
+        open(os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.md"), "w").write(traffic(out))
+        print("wrote profiles/gate_up_gemm_traffic.md")
+    if has("bench_kernel_stats", "prof_bench", "*kernel_stats.csv"):
+        open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w").write(kernel_stats(out))
+        print("wrote profiles/bench_kernel_stats.md")
+    if has("decode_traffic", "pmc_dfetch", "*counter_collection.csv") and \
+            raw("pmc_dwrite", "*counter_collection.csv"):
+        open(os.path.join(ROOT, "profiles", "decode_traffic.md"), "w").write(decode_traffic(out))
+        print("wrote profiles/decode_traffic.md")
+    if has("gate_up_gemm_counters", "pmc_mfma", "*counter_collection.csv"):
         open(os.path.join(ROOT, "profiles", "gate_up_gemm_counters.md"), "w").write(counters(out))
         print("wrote profiles/gate_up_gemm_counters.md")
-    if glob.glob(os.path.join(out, "prof_span", "**", "*kernel_trace.csv"), recursive=True):
+    if has("decode_attention_span", "prof_span", "*kernel_trace.csv"):
         open(os.path.join(ROOT, "profiles", "decode_attention_span.md"), "w").write(decode_span(out))
         print("wrote profiles/decode_attention_span.md")
-    if glob.glob(os.path.join(out, "prof_hbm", "**", "*kernel_trace.csv"), recursive=True):
+    if has("hbm_reference", "prof_hbm", "*kernel_trace.csv"):
         open(os.path.join(ROOT, "profiles", "hbm_reference.md"), "w").write(hbm_reference(out))
         print("wrote profiles/hbm_reference.md")
 

@@ -50,6 +50,22 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(_declared()) == set(tpl.EXPORTED)
 
 
+def test_reference_library_exports_its_header():
+    """libtpref.so (the measurement reference stream, not part of the layer)
+    exports what include/tpref.h declares."""
+    import ctypes as C
+    from tensor_transformer_layer_05_amd import ref
+    if not os.path.exists(ref.library_path):
+        from tensor_transformer_layer_05_amd.csrc import build
+        build.build(force=False)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tpref.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(tpref_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["tpref_stream_read"]
+    l = C.CDLL(ref.library_path)
+    for n in names:
+        assert hasattr(l, n)
+
+
 def test_status_strings(lib):
     for s in range(8):
         assert lib.tp_status_string(s)
