@@ -119,25 +119,36 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   // Load i of this wave fills LDS rows (wave*L + i)*8 .. +7; lane -> row lane/8,
   // LDS chunk lane%8, which holds global chunk dswz(row, lane%8).
   const int lrow = lane >> 3, lpos = lane & 7;
-  uint32_t xoff[C::XL], woff[C::WL];
-  int xk[C::XL], wk[C::WL];
+  // 4-wave tiles: one offset register per load (their scheduling groups pair
+  // each load with an MFMA, and measured faster so).  8-wave tiles: the
+  // swizzle (row/2) % 8 depends only on the parity of wave*L + i, so two base
+  // offsets per operand plus a multiple of 16 rows address every load (fewer
+  // registers and VALU instructions; the same addresses).
+  constexpr bool kParity = C::NW == 8;
+  uint32_t xoff[kParity ? 2 : C::XL], woff[kParity ? 2 : C::WL];
+  int xk[kParity ? 2 : C::XL], wk[kParity ? 2 : C::WL];
 #pragma unroll
-  for (int i = 0; i < C::XL; ++i) {
+  for (int i = 0; i < (kParity ? 2 : C::XL); ++i) {
     const int row = (wave * C::XL + i) * 8 + lrow;
     xk[i] = 8 * dswz(row, lpos);
     xoff[i] = (uint32_t)(row * K + xk[i]) * 2u;
   }
 #pragma unroll
-  for (int i = 0; i < C::WL; ++i) {
+  for (int i = 0; i < (kParity ? 2 : C::WL); ++i) {
     const int row = (wave * C::WL + i) * 8 + lrow;
     wk[i] = 8 * dswz(row, lpos);
     woff[i] = (uint32_t)((row - wrow_shift) * K + wk[i]) * 2u;
   }
+  const uint32_t rows16 = (uint32_t)K * 32u;   // bytes of 16 rows
+  // Load i at k0: byte offset from the resource base, or past the bound when
+  // its k is past K.
   auto load_x = [&](int k0, int stage) {
     TPL_LDS uint16_t* base = (TPL_LDS uint16_t*)lds + stage * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::XL; ++i) {
-      const uint32_t off = (k0 + xk[i] < K) ? xoff[i] + (uint32_t)k0 * 2u : 0x80000000u;
+      const int e = kParity ? (i & 1) : i;
+      const uint32_t rows = kParity ? (uint32_t)(i >> 1) * rows16 : 0u;
+      const uint32_t off = (k0 + xk[e] < K) ? xoff[e] + rows + (uint32_t)k0 * 2u : 0x80000000u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xr, (TPL_LDS void*)(base + (wave * C::XL + i) * 8 * C::BK), 16, off, 0, 0, 0);
     }
@@ -146,7 +157,9 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
     TPL_LDS uint16_t* base = (TPL_LDS uint16_t*)lds + stage * C::STAGE + C::BM * C::BK;
 #pragma unroll
     for (int i = 0; i < C::WL; ++i) {
-      const uint32_t off = (k0 + wk[i] < K) ? woff[i] + (uint32_t)k0 * 2u : 0x80000000u;
+      const int e = kParity ? (i & 1) : i;
+      const uint32_t rows = kParity ? (uint32_t)(i >> 1) * rows16 : 0u;
+      const uint32_t off = (k0 + wk[e] < K) ? woff[e] + rows + (uint32_t)k0 * 2u : 0x80000000u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wr, (TPL_LDS void*)(base + (wave * C::WL + i) * 8 * C::BK), 16, off, 0, 0, 0);
     }
@@ -164,23 +177,47 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   // 16-byte chunk 2*kk + lane/32.
   const int frow = lane & 31, fh = lane >> 5;
   bf16x8 fa[2][C::FA], fb[2][C::FB];
+  // Every fragment row is frow plus a multiple of 16, so the chunk swizzle
+  // (row/2) % 8 is the lane's (frow/2) % 8 for all of them: one chunk offset
+  // per sub-step addresses every read (8-wave tiles; the 4-wave tile keeps
+  // per-row addressing, which its scheduling groups were tuned with).
+  static_assert(C::TM % 16 == 0 && C::TN % 32 == 0 && C::BN % 32 == 0 && C::BM % 16 == 0,
+                "fragment rows keep the lane's swizzle");
+  const int fsw = (frow >> 1) & 7;
+  const int a_row0 = kPairInWave ? wn * (C::TN / 2) : wn * C::TN;
+  const int b_row0 = wm * C::TM;
   auto read_frags = [&](int stage, int kk, int buf) {
-    const uint16_t* base = lds + stage * C::STAGE;
     const int kc = 2 * kk + fh;
+    if constexpr (kParity) {
+      const char* sbase = reinterpret_cast<const char*>(lds) + stage * C::STAGE * 2;
+      const char* abase = sbase + (C::BM + a_row0 + frow) * C::BK * 2;
+      const char* bbase = sbase + (b_row0 + frow) * C::BK * 2;
+      const int cofs = (kc ^ fsw) * 16;
 #pragma unroll
-    for (int i = 0; i < C::FA; ++i) {
-      // In-wave SwiGLU pairing: fragments i < FA/2 are gate rows and i + FA/2
-      // the up rows of the same outputs, so the epilogue pairs them in registers.
-      const int row = !kPairInWave ? wn * C::TN + i * 32 + frow
-                      : i < C::FA / 2 ? wn * (C::TN / 2) + i * 32 + frow
-                                      : C::BN / 2 + wn * (C::TN / 2) + (i - C::FA / 2) * 32 + frow;
-      fa[buf][i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-          base + C::BM * C::BK + row * C::BK + dswz(row, kc) * 8));
-    }
+      for (int i = 0; i < C::FA; ++i) {
+        // In-wave SwiGLU pairing: fragments i < FA/2 are gate rows and i + FA/2
+        // the up rows of the same outputs, so the epilogue pairs them in registers.
+        const int r = !kPairInWave ? i * 32 : i < C::FA / 2 ? i * 32 : C::BN / 2 + (i - C::FA / 2) * 32;
+        fa[buf][i] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + r * C::BK * 2 + cofs));
+      }
 #pragma unroll
-    for (int j = 0; j < C::FB; ++j) {
-      const int row = wm * C::TM + j * 32 + frow;
-      fb[buf][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + row * C::BK + dswz(row, kc) * 8));
+      for (int j = 0; j < C::FB; ++j)
+        fb[buf][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbase + j * 32 * C::BK * 2 + cofs));
+    } else {
+      const uint16_t* base = lds + stage * C::STAGE;
+#pragma unroll
+      for (int i = 0; i < C::FA; ++i) {
+        const int row = !kPairInWave ? wn * C::TN + i * 32 + frow
+                        : i < C::FA / 2 ? wn * (C::TN / 2) + i * 32 + frow
+                                        : C::BN / 2 + wn * (C::TN / 2) + (i - C::FA / 2) * 32 + frow;
+        fa[buf][i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            base + C::BM * C::BK + row * C::BK + dswz(row, kc) * 8));
+      }
+#pragma unroll
+      for (int j = 0; j < C::FB; ++j) {
+        const int row = wm * C::TM + j * 32 + frow;
+        fb[buf][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + row * C::BK + dswz(row, kc) * 8));
+      }
     }
   };
   auto mfmas = [&](int buf, int i0, int i1) {
