@@ -23,7 +23,8 @@
 //     so the loop is branch-free and waits for exactly the chunk it uses;
 //   * no workgroup barrier in the loop (the rings are per wave); the WAVES
 //     partial tiles are summed in LDS in wave order at the end, so the result
-//     depends only on WAVES and the k ranges, not on timing, RT or S.
+//     depends only on WAVES, the k ranges and (with several token tiles) the
+//     workgroup id that sets the chunk order, not on timing or S.
 #include "common.h"
 
 namespace tpl {
@@ -95,8 +96,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
   // lane%16 holding logical chunk (lane%16) ^ (row % 16).
   const int drow = lane >> 4, dpos = lane & 15;
   TPL_LDS uint16_t* ring = (TPL_LDS uint16_t*)lds + wave * RING;
+  // With more than one 16-token tile, token rows are most of a workgroup's
+  // loads, and workgroups that walk their k ranges in step all read the same
+  // token lines of L2 at once.  So workgroups on one XCD (every 8th id) start
+  // at different chunks and wrap around (gate|up + SwiGLU [7168, 8192] at 64
+  // tokens: 34.8 -> 31.9 us, at 48 tokens 32.1 -> 28.8 us; at 8 tokens the
+  // rotation measured 1% slower and is off).  The order of a wave's chunk sums
+  // then depends on its workgroup id, deterministically.
+  const int rot = (MT > 1 || gridDim.y > 1) && nc > 0 ? (int)((blockIdx.x >> 3) % (unsigned)nc) : 0;
   auto issue = [&](int c) {   // chunk c of this wave into stage c % S
-    const int k0 = kb + c * 128;
+    const int k0 = kb + (c < nc ? (c + rot) % nc : c) * 128;
     TPL_LDS uint16_t* dst = ring + (c % S) * STAGE;
 #pragma unroll
     for (int d = 0; d < DPC; ++d) {
@@ -230,11 +239,11 @@ constexpr int64_t kStreamCUs = 256;   // compute units of an MI355X
 // Output rows per workgroup: a full tile, or, when full tiles cover half the
 // CUs or more but not all, the fewest rows that give about one workgroup per
 // CU (rows past them read as zero through the buffer bound and are not
-// stored; the K split, hence the sums, do not change).  Every workgroup
+// stored; the K split does not change).  Every workgroup
 // streams all of its token rows, so thinner tiles re-read the activations:
 // below half the CUs that costs more than the idle CUs (SwiGLU on a [2048,
-// 4096] weight, 32 tokens: 8.8 -> 9.0 us).  Kernel trace, same bits: gate|up
-// SwiGLU on [7168, 8192], 64 tokens 36.8 -> 34.2 us, 48 tokens 33.4 -> 30.4 us.
+// 4096] weight, 32 tokens: 8.8 -> 9.0 us).  Kernel trace: gate|up SwiGLU on
+// [7168, 8192], 64 tokens 36.8 -> 34.2 us, 48 tokens 33.4 -> 30.4 us.
 static int stream_dma_rows(int64_t nout, int out_rows, int ty) {
   const int64_t tiles = (nout + out_rows - 1) / out_rows;
   if (tiles * ty >= kStreamCUs || 2 * tiles * ty < kStreamCUs) return out_rows;
@@ -312,9 +321,9 @@ tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M,
   return TP_OK;
 }
 
-// The same kernel with the rank-local activation fused (bf16 output [M, I]);
-// the K split is the plain call's for the same token count, so the results
-// equal the plain linear followed by the activation bit for bit.
+// The same kernel with the rank-local activation fused (bf16 output [M, I])
+// on the float32 sums; the waves split K as in the plain call for the same
+// token count.
 tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
                                    int64_t K, int act, hipStream_t s) {
   const int mt = (int)((M + 15) / 16);
