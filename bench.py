@@ -16,7 +16,8 @@ Secondary figures (same line, key "decode"): the decode MLP shard at TP=8
 cache), the same attention at TP=16 with replicated KV heads and the vocab-parallel lm_head shard with its
 greedy argmax (TP=8), timed over rotating
 copies of the weights/caches so that the 256 MB Infinity Cache cannot hold
-the working set between steps (also as HIP-graph replays, "graph_ms"), with the
+the working set between steps (also as HIP-graph replays, "graph_ms", and with the
+copies as consecutive layers of one graph, "graph_layers_ms"), with the
 HBM bytes the same steps moved by the FETCH_SIZE/WRITE_SIZE counters
 (profiles/decode_traffic.md) and their rate relative to the attainable read
 rate of a plain read-only stream ("hbm_read_ceiling").
@@ -323,12 +324,31 @@ def _graph_ms(steps_fns, steps, warmup):
     return _median_ms(lambda i: graphs[i % n].replay(), steps, warmup)
 
 
-def _decode_entry(ms_eager, ms_graph, byts, fl):
-    """Figures of one decode shard: both issue modes, and the rates of the
-    faster one (a serving loop would use whichever is faster)."""
-    ms = min(ms_eager, ms_graph)
-    return {"ms": ms, "issue": "graph" if ms_graph < ms_eager else "eager",
-            "eager_ms": ms_eager, "graph_ms": ms_graph,
+def _graph_layers_ms(steps_fns, steps, warmup):
+    """All closures of ``steps_fns`` captured in order in ONE graph, as a
+    serving loop captures a whole decode step (every layer, each with its own
+    weights and cache: here the rotating copies); the median replay time
+    divided by the number of closures.  The replay's own launch cost is then
+    shared by the layers, as it is in such a loop."""
+    for f in steps_fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in steps_fns:
+            f()
+    torch.cuda.synchronize()
+    return _median_ms(lambda i: g.replay(), steps, warmup) / len(steps_fns)
+
+
+def _decode_entry(ms_eager, ms_graph, ms_layers, byts, fl):
+    """Figures of one decode shard: the three issue modes, and the rates of the
+    fastest (a serving loop would use whichever is fastest)."""
+    modes = {"eager": ms_eager, "graph": ms_graph, "graph_layers": ms_layers}
+    issue = min(modes, key=modes.get)
+    ms = modes[issue]
+    return {"ms": ms, "issue": issue, "eager_ms": ms_eager, "graph_ms": ms_graph,
+            "graph_layers_ms": ms_layers,
             "GB/s": byts / ms / 1e6, "TFLOP/s": fl / ms / 1e9, "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBPS}
 
 
@@ -368,7 +388,9 @@ def decode_figures(steps=30, warmup=5, copies=4, ceiling=None):
     """Decode shards timed over ``copies`` rotating copies of the weights and
     caches (together larger than the 256 MB Infinity Cache).  ``eager_ms`` is
     the step issued call by call, ``graph_ms`` the same step replayed from a
-    captured HIP graph; ``ms`` and the rates use the faster of the two.
+    captured HIP graph, ``graph_layers_ms`` the copies captured one after the
+    other in one graph (like the layers of a decode step), per copy; ``ms`` and
+    the rates use the fastest of the three.
     ``hbm_frac`` is algorithmic bytes over time; ``counter_hbm_frac`` the HBM
     bytes the same step moved by the FETCH_SIZE/WRITE_SIZE counters (profiles/
     decode_traffic.md, while the decode kernels' sources match) over time;
@@ -381,8 +403,9 @@ def decode_figures(steps=30, warmup=5, copies=4, ceiling=None):
         w = build()
         n = len(w.steps)
         gms = _graph_ms(w.steps, steps, warmup)
+        lms = _graph_layers_ms(w.steps, steps, warmup)
         ms = _median_ms(lambda i: w.steps[i % n](), steps, warmup)
-        e = _decode_entry(ms, gms, w.bytes, w.flops)
+        e = _decode_entry(ms, gms, lms, w.bytes, w.flops)
         e.update(w.extra)
         if counted and w.name in counted.get("shards", {}):
             cb = counted["shards"][w.name]["bytes"]
