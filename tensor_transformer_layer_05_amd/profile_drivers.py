@@ -28,6 +28,11 @@ sums over the dispatches between its two markers.
 ``libtpref`` in the configuration the benchmark finds fastest, for
 ``rocprofv3 --kernel-trace``.
 
+``vendor_gemm``: the plain gate|up GEMM (M=4096, K=8192, N=28672, bf16
+output) three times through ``torch.matmul`` (the vendor library's GEMM) and
+three times through the library, on the same operands, for ``rocprofv3
+--pmc`` runs that compare the two kernels' instruction mix and stalls.
+
 ``hbm_reference``: what plain streaming reaches on this GPU, next to the
 library's own decode weight stream: 20 device-to-device copies of 1 GiB, 20
 full sums of a 1 GiB float32 tensor (read only), then 20 one-token decode
@@ -93,6 +98,22 @@ HBM_REF_BYTES = 1 << 30
 HBM_REF_CALLS = 20
 
 
+def vendor_gemm() -> None:
+    lib()
+    M, K, N = 4096, 8192, 28672
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    y = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(x, w.t(), out=y)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        column_linear(x, w, out=y)
+    torch.cuda.synchronize()
+
+
 def hbm_reference() -> None:
     lib()
     a = torch.ones(HBM_REF_BYTES, dtype=torch.uint8, device="cuda")
@@ -151,7 +172,7 @@ def stream_ref(workgroups: int = 256, waves: int = 8, loads: int = 8) -> None:
     print("stream_ref done", flush=True)
 
 
-DRIVERS = {"gemm_traffic": gemm_traffic, "decode_attn_span": decode_attn_span, "hbm_reference": hbm_reference,
+DRIVERS = {"gemm_traffic": gemm_traffic, "vendor_gemm": vendor_gemm, "decode_attn_span": decode_attn_span, "hbm_reference": hbm_reference,
            "decode_traffic": decode_traffic, "stream_ref": stream_ref}
 
 if __name__ == "__main__":

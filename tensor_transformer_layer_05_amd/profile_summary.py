@@ -214,6 +214,112 @@ DATA {json.dumps(data)}
 """
 
 
+VENDOR_PASSES = [
+    "SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD SQ_INSTS_MFMA SQ_INSTS_SMEM SQ_INSTS_BRANCH "
+    "SQ_WAVES TA_BUFFER_READ_LDS_WAVEFRONTS TA_BUFFER_READ_WAVEFRONTS GRBM_GUI_ACTIVE",
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY SQ_WAVE_CYCLES "
+    "SQ_INST_LEVEL_VMEM SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE TA_TA_BUSY "
+    "TA_ADDR_STALLED_BY_TC_CYCLES",
+    "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_LDS_DATA_FIFO_FULL "
+    "SQ_LDS_CMD_FIFO_FULL SQ_VMEM_TA_ADDR_FIFO_FULL SQ_VMEM_TA_CMD_FIFO_FULL SQ_ACTIVE_INST_VALU "
+    "GRBM_GUI_ACTIVE TA_DATA_STALLED_BY_TC_CYCLES TA_BUFFER_TOTAL_CYCLES TCP_PENDING_STALL_CYCLES "
+    "TCP_READ_TAGCONFLICT_STALL_CYCLES",
+]
+
+
+def vendor_counters(out):
+    """The vendor GEMM (torch.matmul) against the library's plain gate|up GEMM
+    on the same operands, from three --pmc runs of the vendor_gemm driver.
+    Every ratio is formed within one dispatch (each run counts
+    GRBM_GUI_ACTIVE, summed over the 8 XCDs); the tables give the median over
+    the kernel's launches."""
+    import statistics
+    xcd, simds, cus = 8, 1024, 256
+    ratios = {   # label -> (counter, denominator: "simd" | "cu" | "ghz" | "lds" | None, format)
+        "engine clock (GUI_ACTIVE per XCD / launch duration)": ("GRBM_GUI_ACTIVE", "ghz", "{:.2f} GHz"),
+        "MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GUI_ACTIVE per XCD x 1024 SIMDs))":
+            ("SQ_VALU_MFMA_BUSY_CYCLES", "simd", "{:.1f}%"),
+        "LDS index-active (SQ_LDS_IDX_ACTIVE / (GUI_ACTIVE per XCD x 256 CUs))": ("SQ_LDS_IDX_ACTIVE", "cu", "{:.1f}%"),
+        "LDS bank-conflict cycles / LDS index-active cycles": ("SQ_LDS_BANK_CONFLICT", "lds", "{:.2f}"),
+        "LDS command FIFO full (SQ_LDS_CMD_FIFO_FULL / (GUI_ACTIVE per XCD x 256 CUs))":
+            ("SQ_LDS_CMD_FIFO_FULL", "cu", "{:.2f}%"),
+        "TA busy (TA_TA_BUSY / (GUI_ACTIVE per XCD x 256 CUs))": ("TA_TA_BUSY", "cu", "{:.1f}%"),
+        "TA address stalled by the L1 (TA_ADDR_STALLED_BY_TC_CYCLES, same)":
+            ("TA_ADDR_STALLED_BY_TC_CYCLES", "cu", "{:.1f}%"),
+        "waves per launch (SQ_WAVES)": ("SQ_WAVES", None, "{:.0f}"),
+        "direct-to-LDS buffer loads (TA_BUFFER_READ_LDS_WAVEFRONTS)": ("TA_BUFFER_READ_LDS_WAVEFRONTS", None, "{:.4g}"),
+        "LDS bytes read (SQ_INSTS_LDS_LOAD_BANDWIDTH x 64)": ("SQ_INSTS_LDS_LOAD_BANDWIDTH", 64e-9, "{:.1f} GB"),
+        "MFMA instructions (SQ_INSTS_MFMA)": ("SQ_INSTS_MFMA", None, "{:.4g}"),
+    }
+    vals = {"vendor": collections.defaultdict(list), "library": collections.defaultdict(list)}
+    raw = {"vendor": collections.defaultdict(list), "library": collections.defaultdict(list)}
+    names = {}
+    for i in range(len(VENDOR_PASSES)):
+        for name, us, cs in _dispatches(os.path.join(out, f"pmc_vendor{i + 1}")).values():
+            k = "vendor" if "Cijk" in name else "library" if "gemm_bf16_dma" in name else None
+            if k is None:
+                continue
+            names[k] = name
+            raw[k]["duration_us"].append(us)
+            for c, v in cs.items():
+                raw[k][c].append(v)
+            gui = cs.get("GRBM_GUI_ACTIVE", 0.0) / xcd
+            for label, (c, den, _) in ratios.items():
+                if c not in cs or (den in ("simd", "cu", "ghz") and not gui):
+                    continue
+                v = cs[c]
+                if den == "simd":
+                    v = 100 * v / (gui * simds)
+                elif den == "cu":
+                    v = 100 * v / (gui * cus)
+                elif den == "ghz":
+                    v = gui / us / 1e3
+                elif den == "lds":
+                    v = v / cs["SQ_LDS_IDX_ACTIVE"]
+                elif den is not None:
+                    v = v * den
+                vals[k][label].append(v)
+    med = {k: {c: statistics.median(v) for c, v in d.items()} for k, d in vals.items()}
+    rmed = {k: {c: statistics.median(v) for c, v in d.items()} for k, d in raw.items()}
+    rows = "\n".join(f"| {q} | {f.format(med['vendor'][q])} | {f.format(med['library'][q])} |"
+                     for q, (_, _, f) in ratios.items())
+    craw = sorted(set(rmed["vendor"]) | set(rmed["library"]))
+    raw_rows = "\n".join(f"| `{c}` | {rmed['vendor'].get(c, 0):.4g} | {rmed['library'].get(c, 0):.4g} |" for c in craw)
+    cmds = "\n".join(f"rocprofv3 --pmc {p} --output-format csv -d $REPO/gpurun_out/pmc_vendor{i + 1} -o v -- "
+                      f"python3 -m tensor_transformer_layer_05_amd.profile_drivers vendor_gemm"
+                      for i, p in enumerate(VENDOR_PASSES))
+    data = {"vendor_kernel": names.get("vendor"), "library_kernel": names.get("library"),
+            "ratios": med, "counters": rmed}
+    return f"""# The plain gate|up GEMM: vendor library against this library (rocprofv3 --pmc, three runs)
+
+Commands (from /tmp with TMPDIR=/tmp and PYTHONPATH=$REPO, REPO = repository root; each under
+`timeout -s KILL 90`), then the summary script (from the repository root):
+
+```
+{cmds}
+python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out gate_up_vendor_counters
+```
+
+M=4096, K=8192, N=28672, bf16 in and out, the same operands for both. Three launches of each kernel per
+run; ratios are formed within a dispatch, then the median is taken over the kernel's nine dispatches.
+Vendor kernel (torch.matmul): `{names.get("vendor")}`.
+Library kernel: `{names.get("library")}`.
+
+| quantity | vendor | library |
+|---|---:|---:|
+| launch duration, as profiled (counters slow both) | {rmed['vendor']['duration_us']:.1f} us | {rmed['library']['duration_us']:.1f} us |
+{rows}
+
+All counters, medians over the kernel's launches (sums over the XCDs, shader engines and CUs):
+
+| counter | vendor | library |
+|---|---:|---:|
+{raw_rows}
+
+DATA {json.dumps(data)}
+"""
+
+
 def decode_span(out):
     from .profile_drivers import SPANS
     trace = _csv(os.path.join(out, "prof_span", "**", "*kernel_trace.csv"))
@@ -384,7 +490,8 @@ DATA {json.dumps(data)}
 def main(argv=None):
     """``profile_summary <out_dir> [summary ...]``: write the named summaries
     (gate_up_gemm_traffic, bench_kernel_stats, decode_traffic,
-    gate_up_gemm_counters, decode_attention_span, hbm_reference; default: all
+    gate_up_gemm_counters, gate_up_vendor_counters, decode_attention_span,
+    hbm_reference; default: all
     whose raw outputs are present)."""
     argv = argv or sys.argv[1:]
     out = argv[0] if argv else "gpurun_out"
@@ -405,6 +512,10 @@ def main(argv=None):
     if has("gate_up_gemm_counters", "pmc_mfma", "*counter_collection.csv"):
         open(os.path.join(ROOT, "profiles", "gate_up_gemm_counters.md"), "w").write(counters(out))
         print("wrote profiles/gate_up_gemm_counters.md")
+    if has("gate_up_vendor_counters", "pmc_vendor1", "*counter_collection.csv") and \
+            raw("pmc_vendor3", "*counter_collection.csv"):
+        open(os.path.join(ROOT, "profiles", "gate_up_vendor_counters.md"), "w").write(vendor_counters(out))
+        print("wrote profiles/gate_up_vendor_counters.md")
     if has("decode_attention_span", "prof_span", "*kernel_trace.csv"):
         open(os.path.join(ROOT, "profiles", "decode_attention_span.md"), "w").write(decode_span(out))
         print("wrote profiles/decode_attention_span.md")
