@@ -33,6 +33,11 @@ output) three times through ``torch.matmul`` (the vendor library's GEMM) and
 three times through the library, on the same operands, for ``rocprofv3
 --pmc`` runs that compare the two kernels' instruction mix and stalls.
 
+``prefill_attention``: the prefill attention of the TP=2 layer shard (one
+sequence of 4096 tokens, causal, 32 q / 4 KV heads of 128 on strided views of
+the fused QKV output, as the layer shard issues it), three launches, for
+``rocprofv3 --pmc`` runs of its instruction mix and MFMA utilisation.
+
 ``hbm_reference``: what plain streaming reaches on this GPU, next to the
 library's own decode weight stream: 20 device-to-device copies of 1 GiB, 20
 full sums of a 1 GiB float32 tensor (read only), then 20 one-token decode
@@ -114,6 +119,22 @@ def vendor_gemm() -> None:
     torch.cuda.synchronize()
 
 
+def prefill_attention() -> None:
+    lib()
+    S, hq, hkv, D = 4096, 32, 4, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    qkv = torch.randn(S, (hq + 2 * hkv) * D, device="cuda", generator=g).to(torch.bfloat16)
+    base = qkv.view(1, S, -1)
+    q = base[:, :, :hq * D].unflatten(2, (hq, D))
+    k = base[:, :, hq * D:(hq + hkv) * D].unflatten(2, (hkv, D))
+    v = base[:, :, (hq + hkv) * D:].unflatten(2, (hkv, D))
+    o = torch.empty(1, S, hq, D, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        local_attention(q, k, v, causal=True, out=o)
+    torch.cuda.synchronize()
+
+
 def hbm_reference() -> None:
     lib()
     a = torch.ones(HBM_REF_BYTES, dtype=torch.uint8, device="cuda")
@@ -172,7 +193,7 @@ def stream_ref(workgroups: int = 256, waves: int = 8, loads: int = 8) -> None:
     print("stream_ref done", flush=True)
 
 
-DRIVERS = {"gemm_traffic": gemm_traffic, "vendor_gemm": vendor_gemm, "decode_attn_span": decode_attn_span, "hbm_reference": hbm_reference,
+DRIVERS = {"gemm_traffic": gemm_traffic, "vendor_gemm": vendor_gemm, "prefill_attention": prefill_attention, "decode_attn_span": decode_attn_span, "hbm_reference": hbm_reference,
            "decode_traffic": decode_traffic, "stream_ref": stream_ref}
 
 if __name__ == "__main__":

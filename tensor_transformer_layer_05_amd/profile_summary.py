@@ -320,6 +320,64 @@ DATA {json.dumps(data)}
 """
 
 
+ATTN_PASS = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS "
+             "SQ_INSTS_SALU SQ_WAVES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE")
+
+
+def attention_counters(out):
+    """Instruction mix and MFMA utilisation of the prefill attention launch
+    (one --pmc run of the prefill_attention driver; medians over its three
+    launches, every ratio formed within a dispatch)."""
+    import statistics
+    xcd, simds = 8, 1024
+    S, hq, D = 4096, 32, 128
+    vals = collections.defaultdict(list)
+    name = None
+    for nm, us, cs in _dispatches(os.path.join(out, "pmc_attn")).values():
+        if "attn_prefill" not in nm:
+            continue
+        name = nm
+        gui = cs["GRBM_GUI_ACTIVE"] / xcd
+        vals["duration_us"].append(us)
+        vals["clock"].append(gui / us / 1e3)
+        vals["mfma_busy"].append(cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simds))
+        vals["valu_per_mfma"].append(cs["SQ_INSTS_VALU"] / cs["SQ_INSTS_MFMA"])
+        vals["trans_per_mfma"].append(cs["SQ_INSTS_VALU_TRANS_F32"] / cs["SQ_INSTS_MFMA"])
+        vals["lds_per_mfma"].append(cs["SQ_INSTS_LDS"] / cs["SQ_INSTS_MFMA"])
+        vals["mfma"].append(cs["SQ_INSTS_MFMA"])
+        vals["valu"].append(cs["SQ_INSTS_VALU"])
+        vals["waves"].append(cs["SQ_WAVES"])
+    m = {k: statistics.median(v) for k, v in vals.items()}
+    fl = 4.0 * S * S / 2 * hq * D   # QK^T and PV over the causal half of the score matrix
+    data = {"kernel": name, "medians": m, "pass": ATTN_PASS}
+    return f"""# Prefill attention of the TP=2 layer shard: instruction mix (rocprofv3 --pmc)
+
+Command (from /tmp with TMPDIR=/tmp and PYTHONPATH=$REPO, REPO = repository root), then the summary script
+(from the repository root):
+
+```
+timeout -s KILL 90 rocprofv3 --pmc {ATTN_PASS} --output-format csv -d $REPO/gpurun_out/pmc_attn -o a -- python3 -m tensor_transformer_layer_05_amd.profile_drivers prefill_attention
+python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out prefill_attention_counters
+```
+
+One sequence of 4096 tokens, causal, 32 q / 4 KV heads of 128 on strided views of the fused QKV output;
+medians over three launches of `{name}`.
+
+| quantity | value |
+|---|---:|
+| launch duration, as profiled | {m['duration_us']:.1f} us ({fl / m['duration_us'] / 1e6:.0f} TFLOP/s on the causal half, {fl / 1e12:.3f} TFLOP) |
+| engine clock (GUI_ACTIVE per XCD / duration) | {m['clock']:.2f} GHz |
+| MFMA busy (`SQ_VALU_MFMA_BUSY_CYCLES` / (GUI_ACTIVE per XCD x 1024 SIMDs)) | {100 * m['mfma_busy']:.1f}% |
+| MFMA instructions (`SQ_INSTS_MFMA`) | {m['mfma']:.4g} |
+| VALU instructions per MFMA (`SQ_INSTS_VALU` / `SQ_INSTS_MFMA`; the VALU count includes the MFMAs) | {m['valu_per_mfma']:.2f} |
+| fp32 transcendental instructions per MFMA (`SQ_INSTS_VALU_TRANS_F32`) | {m['trans_per_mfma']:.3f} |
+| LDS instructions per MFMA | {m['lds_per_mfma']:.3f} |
+| waves per launch | {m['waves']:.0f} |
+
+DATA {json.dumps(data)}
+"""
+
+
 def decode_span(out):
     from .profile_drivers import SPANS
     trace = _csv(os.path.join(out, "prof_span", "**", "*kernel_trace.csv"))
@@ -490,8 +548,8 @@ DATA {json.dumps(data)}
 def main(argv=None):
     """``profile_summary <out_dir> [summary ...]``: write the named summaries
     (gate_up_gemm_traffic, bench_kernel_stats, decode_traffic,
-    gate_up_gemm_counters, gate_up_vendor_counters, decode_attention_span,
-    hbm_reference; default: all
+    gate_up_gemm_counters, gate_up_vendor_counters, prefill_attention_counters,
+    decode_attention_span, hbm_reference; default: all
     whose raw outputs are present)."""
     argv = argv or sys.argv[1:]
     out = argv[0] if argv else "gpurun_out"
@@ -516,6 +574,9 @@ def main(argv=None):
             raw("pmc_vendor3", "*counter_collection.csv"):
         open(os.path.join(ROOT, "profiles", "gate_up_vendor_counters.md"), "w").write(vendor_counters(out))
         print("wrote profiles/gate_up_vendor_counters.md")
+    if has("prefill_attention_counters", "pmc_attn", "*counter_collection.csv"):
+        open(os.path.join(ROOT, "profiles", "prefill_attention_counters.md"), "w").write(attention_counters(out))
+        print("wrote profiles/prefill_attention_counters.md")
     if has("decode_attention_span", "prof_span", "*kernel_trace.csv"):
         open(os.path.join(ROOT, "profiles", "decode_attention_span.md"), "w").write(decode_span(out))
         print("wrote profiles/decode_attention_span.md")
