@@ -57,3 +57,13 @@ def test_multi_gpu_request_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_decode_entry_takes_the_fastest_issue_mode():
+    # 100 MB in 20 us (graph layers) = 5 TB/s; 1 GFLOP in the same time
+    e = bench._decode_entry(0.030, 0.025, 0.020, 100e6, 1e9)
+    assert e["issue"] == "graph_layers" and e["ms"] == 0.020
+    assert abs(e["GB/s"] - 5000.0) < 1e-6 and abs(e["TFLOP/s"] - 50.0) < 1e-9
+    assert abs(e["hbm_frac"] - 5000.0 / bench.PEAK_HBM_GBPS) < 1e-12
+    e = bench._decode_entry(0.010, 0.025, 0.020, 100e6, 1e9)
+    assert e["issue"] == "eager" and e["eager_ms"] == 0.010 and e["graph_layers_ms"] == 0.020
