@@ -384,6 +384,26 @@ def read_ceiling(steps=10, warmup=3, nbytes=1 << 30):
             "configs": rows, "bytes": nbytes}
 
 
+def stream_ms(nbytes, steps=30, warmup=5):
+    """The same read-only stream as ``read_ceiling``, over ``nbytes`` per call
+    (enough rotating buffers that the Infinity Cache cannot hold them), issued
+    and timed like a decode step: the fastest of four grid shapes.  A decode
+    shard moves at least its algorithmic bytes, so this is the time a single
+    plain read of that many bytes takes here, fixed launch and first-load
+    latency included."""
+    from tensor_transformer_layer_05_amd import ref
+    n = max(4096, int(nbytes) // 4096 * 4096)
+    copies = max(2, int(600e6 // n) + 1)
+    bufs = [torch.ones(n, dtype=torch.uint8, device=DEV) for _ in range(copies)]
+    out = torch.empty(4096 * 16 * 64, dtype=torch.int32, device=DEV)
+    best = None
+    for wg, waves, u in ((256, 8, 8), (512, 8, 8), (1024, 8, 4), (256, 16, 8)):
+        ms = _median_ms(lambda i: ref.stream_read(bufs[i % copies], out, wg, waves, u), steps, warmup)
+        best = ms if best is None else min(best, ms)
+    del bufs
+    return best
+
+
 def decode_figures(steps=30, warmup=5, copies=4, ceiling=None):
     """Decode shards timed over ``copies`` rotating copies of the weights and
     caches (together larger than the 256 MB Infinity Cache).  ``eager_ms`` is
@@ -395,13 +415,15 @@ def decode_figures(steps=30, warmup=5, copies=4, ceiling=None):
     bytes the same step moved by the FETCH_SIZE/WRITE_SIZE counters (profiles/
     decode_traffic.md, while the decode kernels' sources match) over time;
     ``frac_of_read_ceiling`` algorithmic bytes over time relative to the
-    attainable read rate measured by ``read_ceiling``."""
+    attainable read rate measured by ``read_ceiling``; ``size_stream_ms`` the
+    time of one plain read of the shard's algorithmic bytes (``stream_ms``) and
+    ``frac_of_size_stream`` that time over the shard's."""
     from tensor_transformer_layer_05_amd.decode_workloads import all_decode
     counted = recorded_profile("decode_traffic.md")
     out = {}
     for build in all_decode(copies):
         w = build()
-        n = len(w.steps)
+        n, name, byts = len(w.steps), w.name, w.bytes
         gms = _graph_ms(w.steps, steps, warmup)
         lms = _graph_layers_ms(w.steps, steps, warmup)
         ms = _median_ms(lambda i: w.steps[i % n](), steps, warmup)
@@ -415,8 +437,10 @@ def decode_figures(steps=30, warmup=5, copies=4, ceiling=None):
             e["counter_bytes"] = e["counter_hbm_frac"] = None
         if ceiling:
             e["frac_of_read_ceiling"] = e["GB/s"] / ceiling["GB/s"]
-        out[w.name] = e
         del w
+        e["size_stream_ms"] = stream_ms(byts, steps, warmup)
+        e["frac_of_size_stream"] = e["size_stream_ms"] / e["ms"]
+        out[name] = e
     return out
 
 
