@@ -434,6 +434,8 @@ using Dma320 = DmaTile<256, 320, 4, 2>;
 // partly, e.g. a 2048 x 6144 output: 8 x 32 tiles fill 256 CUs once where
 // 8 x 24 tiles of 256x256 would leave a quarter of them idle.
 using Dma192 = DmaTile<256, 192, 4, 2>;
+// 256x192 with 4 waves of 128x96 (192 accumulators each), for fp32 outputs.
+using Dma192w4 = DmaTile<256, 192, 2, 2>;
 
 template <class C, int EPI>
 static tp_status launch_dma(const void* x, const void* w, void* y, int M, int N, int K,
@@ -482,8 +484,10 @@ tp_status gemm_bf16_dma(const void* x, const void* w, void* y, int64_t M, int64_
                         bool out_f32, bool vec_out, hipStream_t s, int force_tile) {
   const int pick = force_tile >= 0 ? force_tile : gemm_dma_pick_tile((int)M, (int)N, true);
   // fp32 partials (the row-parallel products) run 2-3% faster on 4 waves of
-  // 128x128 than on 8 waves of 128x64; bf16 outputs run alike on both.
+  // 128x128 than on 8 waves of 128x64, and on 4 waves of 128x96 than on 8 of
+  // 64x96; bf16 outputs run alike (256x256) or faster on 8 waves (256x192).
   if (pick == 0 && out_f32) return launch_dma<Dma256w4, 0>(x, w, y, (int)M, (int)N, (int)K, true, vec_out, s);
+  if (pick == 3 && out_f32) return launch_dma<Dma192w4, 0>(x, w, y, (int)M, (int)N, (int)K, true, vec_out, s);
   if (pick == 0) return launch_dma<Dma256, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
   if (pick == 2) return launch_dma<Dma320, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
   if (pick == 3) return launch_dma<Dma192, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);

@@ -38,6 +38,12 @@ sequence of 4096 tokens, causal, 32 q / 4 KV heads of 128 on strided views of
 the fused QKV output, as the layer shard issues it), three launches, for
 ``rocprofv3 --pmc`` runs of its instruction mix and MFMA utilisation.
 
+``ffn_gemms``: the GELU FFN shard's two GEMMs at TP=8 (2048 tokens, hidden
+12288, local intermediate 6144): one plain 256 MiB device-to-device copy
+(calibration), then fc1 with GELU in its epilogue three times and fc2 to
+float32 partials three times, for ``rocprofv3 --pmc`` runs of their HBM bytes
+(FETCH_SIZE, WRITE_SIZE) and MFMA and LDS counters.
+
 ``hbm_reference``: what plain streaming reaches on this GPU, next to the
 library's own decode weight stream: 20 device-to-device copies of 1 GiB, 20
 full sums of a 1 GiB float32 tensor (read only), then 20 one-token decode
@@ -50,7 +56,8 @@ import sys
 
 import torch
 
-from . import column_linear, column_linear_act, lib, local_attention, local_attention_workspace
+from . import (column_linear, column_linear_act, lib, local_attention, local_attention_workspace,
+               row_linear_partial)
 
 
 def gemm_traffic() -> None:
@@ -135,6 +142,31 @@ def prefill_attention() -> None:
     torch.cuda.synchronize()
 
 
+def ffn_gemms() -> None:
+    lib()
+    M, H, F = 2048, 12288, 6144
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    x = torch.randn(M, H, device="cuda", generator=g).to(torch.bfloat16)
+    w1 = (torch.randn(F, H, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn(H, F, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    a = torch.empty(M, F, device="cuda", dtype=torch.bfloat16)
+    p = torch.empty(M, H, device="cuda", dtype=torch.float32)
+    n = 256 << 20
+    c0 = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    c1 = torch.empty_like(c0)
+    torch.cuda.synchronize()
+    c1.copy_(c0)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        column_linear_act(x, w1, "gelu", out=a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        row_linear_partial(a, w2, out=p)
+    torch.cuda.synchronize()
+    print("ffn_gemms done", flush=True)
+
+
 def hbm_reference() -> None:
     lib()
     a = torch.ones(HBM_REF_BYTES, dtype=torch.uint8, device="cuda")
@@ -193,7 +225,7 @@ def stream_ref(workgroups: int = 256, waves: int = 8, loads: int = 8) -> None:
     print("stream_ref done", flush=True)
 
 
-DRIVERS = {"gemm_traffic": gemm_traffic, "vendor_gemm": vendor_gemm, "prefill_attention": prefill_attention, "decode_attn_span": decode_attn_span, "hbm_reference": hbm_reference,
+DRIVERS = {"gemm_traffic": gemm_traffic, "vendor_gemm": vendor_gemm, "ffn_gemms": ffn_gemms, "prefill_attention": prefill_attention, "decode_attn_span": decode_attn_span, "hbm_reference": hbm_reference,
            "decode_traffic": decode_traffic, "stream_ref": stream_ref}
 
 if __name__ == "__main__":

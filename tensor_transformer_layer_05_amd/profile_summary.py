@@ -320,6 +320,99 @@ DATA {json.dumps(data)}
 """
 
 
+FFN_SQ_PASS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_LDS_IDX_ACTIVE "
+               "SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE")
+FFN_PASSES = [("pmc_ffn_fetch", "FETCH_SIZE"), ("pmc_ffn_write", "WRITE_SIZE"), ("pmc_ffn_sq", FFN_SQ_PASS)]
+
+
+def ffn_counters(out):
+    """HBM bytes, MFMA and LDS counters of the GELU FFN shard's fc1 (GELU
+    epilogue) and fc2 (float32 partials), three launches each, from three
+    --pmc runs of the ffn_gemms driver.  Traffic = FETCH_SIZE and WRITE_SIZE
+    scaled by what they read for the driver's 256 MiB copy; every other ratio
+    is formed within one dispatch; the table gives medians over the launches."""
+    import statistics
+    xcd, simds, cus = 8, 1024, 256
+    M, H, F = 2048, 12288, 6144
+    kinds = {"fc1": "false, true, 2>", "fc2": "true, true, 0>"}
+    alg = {"fc1": {"flop": 2.0 * M * H * F, "bytes": (M * H + F * H + M * F) * 2},
+           "fc2": {"flop": 2.0 * M * F * H, "bytes": (M * F + H * F) * 2 + M * H * 4}}
+    runs = {d: _dispatches(os.path.join(out, d)) for d, _ in FFN_PASSES}
+
+    def copy_of(d):
+        return [cs for n, us, cs in runs[d].values() if "copyBuffer" in n][0]
+    fs = 262144.0 / copy_of("pmc_ffn_fetch")["FETCH_SIZE"]
+    ws = 262144.0 / copy_of("pmc_ffn_write")["WRITE_SIZE"]
+    vals = {k: collections.defaultdict(list) for k in kinds}
+    names = {}
+    for d, _ in FFN_PASSES:
+        for name, us, cs in runs[d].values():
+            k = next((k for k, t in kinds.items() if "gemm_bf16_dma_kernel" in name and t in name), None)
+            if k is None:
+                continue
+            names[k] = name
+            v = vals[k]
+            if d == "pmc_ffn_sq":
+                v["duration_us"].append(us)
+                gui = cs["GRBM_GUI_ACTIVE"] / xcd
+                v["clock_ghz"].append(gui / us / 1e3)
+                v["mfma_busy"].append(cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simds))
+                v["lds_idx_active"].append(cs["SQ_LDS_IDX_ACTIVE"] / (gui * cus))
+                v["lds_bank_conflicts"].append(cs["SQ_LDS_BANK_CONFLICT"])
+                v["mfma_flop_counted"].append(cs["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512)
+            elif d == "pmc_ffn_fetch":
+                v["fetch_bytes"].append(cs["FETCH_SIZE"] * fs * 1024)
+            else:
+                v["write_bytes"].append(cs["WRITE_SIZE"] * ws * 1024)
+    med = {k: {c: statistics.median(x) for c, x in d.items()} for k, d in vals.items()}
+    for k in kinds:
+        m = med[k]
+        m["traffic_bytes"] = m["fetch_bytes"] + m["write_bytes"]
+        m["tflops_as_profiled"] = alg[k]["flop"] / m["duration_us"] / 1e6
+        m["algorithmic_bytes"] = alg[k]["bytes"]
+    cmds = "\n".join(f"timeout -s KILL 90 rocprofv3 --pmc {p} --output-format csv -d $REPO/gpurun_out/{d} -o f -- "
+                      f"python3 -m tensor_transformer_layer_05_amd.profile_drivers ffn_gemms"
+                      for d, p in FFN_PASSES)
+
+    def row(label, key, fmt):
+        return f"| {label} | {fmt.format(med['fc1'][key])} | {fmt.format(med['fc2'][key])} |"
+    rows = "\n".join([
+        row("launch duration, as profiled (counters slow it)", "duration_us", "{:.1f} us"),
+        row("rate as profiled", "tflops_as_profiled", "{:.0f} TFLOP/s"),
+        row("engine clock (GUI_ACTIVE per XCD / duration)", "clock_ghz", "{:.2f} GHz"),
+        row("MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GUI_ACTIVE per XCD x 1024 SIMDs))", "mfma_busy", "{:.1%}"),
+        row("bf16 MFMA FLOP counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)", "mfma_flop_counted", "{:.4g}"),
+        row("LDS index-active (SQ_LDS_IDX_ACTIVE / (GUI_ACTIVE per XCD x 256 CUs))", "lds_idx_active", "{:.1%}"),
+        row("LDS bank conflicts (SQ_LDS_BANK_CONFLICT)", "lds_bank_conflicts", "{:.0f}"),
+        row("HBM bytes read (FETCH_SIZE, scaled)", "fetch_bytes", "{:.4g}"),
+        row("HBM bytes written (WRITE_SIZE, scaled)", "write_bytes", "{:.4g}"),
+        row("algorithmic bytes (operands once, output once)", "algorithmic_bytes", "{:.4g}"),
+    ])
+    data = {"kernels": names, "fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "medians": med}
+    return f"""# The GELU FFN shard's GEMMs at TP=8: HBM bytes, MFMA and LDS counters (rocprofv3 --pmc, three runs)
+
+Commands (from /tmp with TMPDIR=/tmp and PYTHONPATH=$REPO, REPO = repository root), then the summary script
+(from the repository root):
+
+```
+{cmds}
+python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out ffn_gemm_counters
+```
+
+Rank 0 of the GELU FFN at TP=8: fc1 = [2048, 12288] x [6144, 12288]^T with GELU in the epilogue (bf16 out),
+fc2 = [2048, 6144] x [12288, 6144]^T to float32 partials; both on 256x192 tiles (fc1: 8 x 32 tiles, one
+round on 256 CUs; fc2: 8 x 64 tiles, two rounds). 309.2 GFLOP each. Three launches of each per run; the
+traffic is scaled by what the counters read for a 256 MiB copy in the same run (FETCH_SIZE x {fs:.4f},
+WRITE_SIZE x {ws:.4f}); the other ratios are formed within a dispatch; medians over the launches.
+
+| quantity | fc1 + GELU | fc2 |
+|---|---:|---:|
+{rows}
+
+DATA {json.dumps(data)}
+"""
+
+
 ATTN_PASS = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS "
              "SQ_INSTS_SALU SQ_WAVES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE")
 
@@ -548,7 +641,7 @@ DATA {json.dumps(data)}
 def main(argv=None):
     """``profile_summary <out_dir> [summary ...]``: write the named summaries
     (gate_up_gemm_traffic, bench_kernel_stats, decode_traffic,
-    gate_up_gemm_counters, gate_up_vendor_counters, prefill_attention_counters,
+    gate_up_gemm_counters, gate_up_vendor_counters, prefill_attention_counters, ffn_gemm_counters,
     decode_attention_span, hbm_reference; default: all
     whose raw outputs are present)."""
     argv = argv or sys.argv[1:]
@@ -577,6 +670,10 @@ def main(argv=None):
     if has("prefill_attention_counters", "pmc_attn", "*counter_collection.csv"):
         open(os.path.join(ROOT, "profiles", "prefill_attention_counters.md"), "w").write(attention_counters(out))
         print("wrote profiles/prefill_attention_counters.md")
+    if has("ffn_gemm_counters", "pmc_ffn_sq", "*counter_collection.csv") and \
+            raw("pmc_ffn_fetch", "*counter_collection.csv") and raw("pmc_ffn_write", "*counter_collection.csv"):
+        open(os.path.join(ROOT, "profiles", "ffn_gemm_counters.md"), "w").write(ffn_counters(out))
+        print("wrote profiles/ffn_gemm_counters.md")
     if has("decode_attention_span", "prof_span", "*kernel_trace.csv"):
         open(os.path.join(ROOT, "profiles", "decode_attention_span.md"), "w").write(decode_span(out))
         print("wrote profiles/decode_attention_span.md")

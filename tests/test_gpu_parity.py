@@ -117,8 +117,10 @@ def test_linear_bf16_normal(M, K, N):
 
 
 # Row-parallel partials (fp32 out) on each prefill tile shape: 4-wave 256x256,
-# 256x192, 256x320, 128x128; ragged M, N and K tails.
-ROW_SHAPES = [(4000, 1000, 4000), (2048, 1032, 6144), (4000, 136, 5100), (1000, 520, 1000), (65, 64, 16)]
+# 4-wave 256x192 (ragged K, then ragged M and N), 256x320, 128x128; ragged M, N
+# and K tails.
+ROW_SHAPES = [(4000, 1000, 4000), (2048, 1032, 6144), (2000, 520, 6100), (4000, 136, 5100), (1000, 520, 1000),
+              (65, 64, 16)]
 
 
 @pytest.mark.parametrize("M,K,N", ROW_SHAPES)
