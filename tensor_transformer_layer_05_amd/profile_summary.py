@@ -140,7 +140,8 @@ Mapping (prefill calls = 2 set-up passes over both ranks + 2 warm-up + 5 timed s
 - `attn_decode_kernel<false|true>` + `attn_decode_combine_kernel`: decode attention (contiguous / paged cache).
 - `vocab_argmax_kernel`: the lm_head shard's local greedy step.
 - `gemm_bf16_dma_kernel<DmaTile<256,192,4,2>, false, true, 2>`: the GELU FFN's fc1 with GELU in its epilogue
-  (M=2048 K=12288 N=6144, 8 x 32 tiles); `<..., true, true, 0>`: its fc2 to fp32 partials (N=12288).
+  (M=2048 K=12288 N=6144, 8 x 32 tiles); `<DmaTile<256,192,2,2>, true, true, 0>`: its fc2 to fp32
+  partials (N=12288, 4 waves of 128x96).
 - `reduce_kernel<true, true>` also runs the sum of the FFN's 8 partials.
 
 Decode calls come from the eager and graph-replayed decode figures; kernel durations are per launch.
