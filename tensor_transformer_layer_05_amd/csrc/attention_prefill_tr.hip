@@ -14,18 +14,29 @@
 //    V stored naturally ([key][d]) in LDS through ds_read_b64_tr_b16: within
 //    each 16-lane group, lane s addresses the 4 d of row k0 + s/4 starting at
 //    d0 + 4 (s % 4), and lane j receives V[k0 + e][d0 + j], e = 0..3.
+//  * Each wave alternates an MFMA step (the O product of tile t and the
+//    scores of tile t+1) and a VALU step (the softmax of tile t+1 and the
+//    rescale of O), with a workgroup barrier after each step.  The two waves
+//    of a SIMD (w and w + 4) run half a tile apart, so one wave's MFMAs run
+//    while the other works through its softmax: waves 4-7 pass one extra
+//    barrier before the loop and waves 0-3 one after it.
 //  * K and V tiles reach LDS through buffer_load_dwordx4 ... lds (1 KB = 4
-//    key rows per wave-level load), one barrier per tile.  K runs two tiles
-//    ahead of the O product and V one, in two slots each: while the scores
-//    of tile t+1 are turned into probabilities, the MFMAs of O += V P for
-//    tile t can run.  Rows past the key span read as zero through the buffer
-//    bound.  LDS rows are 256 bytes; K's 16-byte chunks are XOR-ed with
-//    (key % 16) so that the 16 rows of an A-fragment read hit distinct banks,
-//    V's with 4 (key % 4) so that the 4 rows x 4 chunks of a transposed read
-//    do.
+//    key rows per wave-level load), in two slots each; K runs two tiles ahead
+//    of the O product and V one.  Inside the loop only waves 0-3 load (in
+//    their MFMA step, after the O product) and they wait for the loads before
+//    the barrier that ends their next VALU step; the transposing V reads wait
+//    for every load their wave has in flight, so waves 4-7 issue none.  Rows
+//    past the key span read as zero through the buffer bound.  LDS rows are
+//    256 bytes; K's 16-byte chunks are XOR-ed with (key % 16) so that the 16
+//    rows of an A-fragment read hit distinct banks, V's with 4 (key % 4) so
+//    that the 4 rows x 4 chunks of a transposed read do.
+//  * A positive softmax scale is applied inside the exponent's FMA; the
+//    running maximum is kept on unscaled scores.
 //  * Causal masking is aligned to the end of the key span; tiles entirely
 //    above a wave's last query are skipped by that wave.  Workgroups are
 //    ordered longest first across all heads to balance the causal triangle.
+#include <type_traits>
+
 #include "common.h"
 
 namespace tpl {
@@ -57,6 +68,15 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// a ^ IMM in a VALU op the compiler does not hoist out of the loop (one op per
+// fragment address instead of a register held per address)
+template <uint32_t IMM>
+__device__ __forceinline__ uint32_t xor_late(uint32_t a) {
+  uint32_t r;
+  asm volatile("v_xor_b32_e32 %0, %1, %2" : "=v"(r) : "i"(IMM), "v"(a));
+  return r;
 }
 
 }  // namespace
@@ -109,29 +129,34 @@ __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
   const uint32_t row_bytes = (uint32_t)(a.ks1 * 2);
   // LDS: K slots 0,1 then V slots 0,1 (64 keys x 256 B each).  K runs two
   // tiles ahead of the O product, V one.
+  // Tile loads: one wave-level load = 4 key rows x 256 B.  Before the loop
+  // every wave loads rows (2 wave + i) * 4 + lr of a tile (i < 2); inside
+  // it, waves 0-3 load rows (4 wave + i) * 4 + lr (i < 4) and waves 4-7 none,
+  // so the latter never wait for loads in flight (the transposing V reads
+  // wait for every load the wave has in flight).
+  auto issue_rows = [&](const __amdgpu_buffer_rsrc_t& rs, int slot, int kt, int row, bool is_v) {
+    const int t = kt * kBK + row;
+    const int ch = is_v ? (lp ^ (4 * (row & 3))) : (lp ^ (row & 15));
+    const bool ok = t < a.Skv;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (TPL_LDS void*)((TPL_LDS uint16_t*)lds + slot * kTileE + (row - lr) * kD), 16,
+        ok ? (uint32_t)t * row_bytes + (uint32_t)ch * 16u : 0x80000000u, 0, 0, 0);
+  };
   auto issue_k = [&](int kt) {
-    TPL_LDS uint16_t* dst = (TPL_LDS uint16_t*)lds + (kt & 1) * kTileE;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = (wave * 2 + i) * 4 + lr;
-      const int t = kt * kBK + row;
-      const int kc = lp ^ (row & 15);
-      const bool ok = t < a.Skv;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TPL_LDS void*)(dst + (wave * 2 + i) * 4 * kD), 16,
-                                               ok ? (uint32_t)t * row_bytes + (uint32_t)kc * 16u : 0x80000000u, 0, 0, 0);
-    }
+    for (int i = 0; i < 2; ++i) issue_rows(kr, kt & 1, kt, (wave * 2 + i) * 4 + lr, false);
   };
   auto issue_v = [&](int kt) {
-    TPL_LDS uint16_t* dst = (TPL_LDS uint16_t*)lds + (2 + (kt & 1)) * kTileE;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = (wave * 2 + i) * 4 + lr;
-      const int t = kt * kBK + row;
-      const int vc = lp ^ (4 * (row & 3));
-      const bool ok = t < a.Skv;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TPL_LDS void*)(dst + (wave * 2 + i) * 4 * kD), 16,
-                                               ok ? (uint32_t)t * row_bytes + (uint32_t)vc * 16u : 0x80000000u, 0, 0, 0);
-    }
+    for (int i = 0; i < 2; ++i) issue_rows(vr, 2 + (kt & 1), kt, (wave * 2 + i) * 4 + lr, true);
+  };
+  auto issue_k4 = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_rows(kr, kt & 1, kt, (wave * 4 + i) * 4 + lr, false);
+  };
+  auto issue_v4 = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_rows(vr, 2 + (kt & 1), kt, (wave * 4 + i) * 4 + lr, true);
   };
 
   f32x16 oacc[4];
@@ -152,32 +177,54 @@ __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
 
   // S^T[key, query] of tile kt, 2 blocks of 32 keys (K from slot kt & 1)
   f32x16 st[2];
+  // chunk (2 kk + hl) ^ (row % 16) of K row `row` (row % 16 = c32 % 16) is the
+  // byte offset ((hl ^ row % 16) * 16) ^ (32 kk): one base address serves all kk
+  const uint32_t y16 = (uint32_t)((hl ^ (c32 & 15)) * 16);
   auto s_tile = [&](int kt) {
-    const uint16_t* ks = lds + (kt & 1) * kTileE;
+    const uint32_t kaddr0 =
+        (uint32_t)reinterpret_cast<uintptr_t>((TPL_LDS uint16_t*)lds + (kt & 1) * kTileE + c32 * kD) | y16;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    auto step = [&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      const uint32_t ka = xor_late<32u * kk>(kaddr0);
+      const bf16x8 qk = qf[kk];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + c32;
-        const int ch = (2 * kk + hl) ^ (row & 15);
-        const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + row * kD + ch * 8));
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], st[kb], 0, 0, 0);
+        const bf16x8 af = as_bf16x8(*reinterpret_cast<const TPL_LDS u32x4*>((TPL_LDS uint8_t*)(uintptr_t)ka + kb * 8192));
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qk, st[kb], 0, 0, 0);
       }
+    };
+    step(std::integral_constant<int, 0>{}); step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{}); step(std::integral_constant<int, 3>{});
+    step(std::integral_constant<int, 4>{}); step(std::integral_constant<int, 5>{});
+    step(std::integral_constant<int, 6>{}); step(std::integral_constant<int, 7>{});
+    // K reads three steps ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int g = 0; g < 5; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
   };
   // scores into the log2 domain, then the mask behind one wave-uniform branch
   // (only diagonal and ragged tiles need it): key t = t_first + 4 hl + 32 kb +
   // 8 (r / 4) + r % 4 is valid while t < lim
+  // A positive scale is folded into the exponent's FMA (the running max is
+  // kept on unscaled scores); otherwise the scores are scaled first.
+  const bool fold = a.scale_log2 > 0.f;
+  const float csc = fold ? a.scale_log2 : 1.f;
   auto softmax_a = [&](int kt) {
     const int t_first = kt * kBK;
+    if (!fold) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[kb][r] *= a.scale_log2;
+        for (int r = 0; r < 16; ++r) st[kb][r] *= a.scale_log2;
+    }
     const bool need_mask = (t_first + kBK > a.Skv) ||
                            (a.causal && t_first + kBK - 1 > qw0 + off);
     if (need_mask) {
@@ -196,30 +243,30 @@ __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
   // rescales the older O sums.  v_exp_f32 is called directly: its arguments
   // are <= 0, and results below 2^-126 may flush to zero.
   auto softmax_b = [&](bf16x8* pb) -> float {
-    float mx = -INFINITY;
+    // max over four independent chains, then across the pair of lanes
+    float m4[4] = {st[0][0], st[0][8], st[1][0], st[1][8]};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
+      for (int r = 1; r < 8; ++r) m4[g] = fmaxf(m4[g], st[g >> 1][(g & 1) * 8 + r]);
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     mx = pair_max(mx);
     const float mnew = fmaxf(mrun, mx);
-    const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(mrun - muse);
+    const float muse = (mnew == -INFINITY) ? 0.f : mnew * csc;
+    const float alpha = __builtin_amdgcn_exp2f(fmaf(mrun, csc, -muse));
     mrun = mnew;
-    float psum = 0.f;
+    float ps[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(st[kb][half * 8 + e] - muse);
-          psum += p[e];
-        }
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(st[kb][half * 8 + e], csc, -muse));
+        ps[kb * 2 + half] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         pb[kb * 2 + half] = as_bf16x8(pack8(p));
       }
-    lrun = lrun * alpha + psum;
+    lrun = lrun * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
     return alpha;
   };
   // O^T[d, query] += V^T[d, keys] P^T[keys, query], 16 keys per step (V from
@@ -251,6 +298,14 @@ __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[step], oacc[db], 0, 0, 0);
       }
     }
+    // transposing reads four MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int g = 0; g < 12; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   auto rescale = [&](float alpha) {
 #pragma unroll
@@ -259,36 +314,46 @@ __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
   };
 
-  bf16x8 pb[4], pn[4];
+  bf16x8 pb[4];
   if (nkt > 0) { issue_k(0); issue_v(0); }
   if (nkt > 1) issue_k(1);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  if (nw > 0) {
-    s_tile(0);
-    softmax_a(0);
-    softmax_b(pb);
-  }
-  // Iteration kt: scores and probabilities of tile kt+1, O product of tile kt
-  // (whose probabilities the previous iteration made); loads of V(kt+1) and
-  // K(kt+2) into the slots that V(kt-1) and K(kt) left.
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) issue_v(kt + 1);
-    if (kt + 2 < nkt) issue_k(kt + 2);
-    if (kt + 1 < nw) {
-      s_tile(kt + 1);
-      softmax_a(kt + 1);
-      o_tile(kt, pb);
-      const float alpha = softmax_b(pn);
-      rescale(alpha);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pb[i] = pn[i];
-    } else if (kt < nw) {
-      o_tile(kt, pb);
+  // Ping-pong: step M(j) is the MFMA work (O product of tile j, scores of
+  // tile j+1), step V(j) the VALU work (softmax of tile j+1, O rescale).
+  // Waves 4-7 (the second wave of each SIMD) run every step one phase after
+  // waves 0-3, so one wave's MFMAs run beside the other wave's softmax.
+  const int lag = wave >> 2;
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Every wave runs the same steps M(j), barrier, V(j), barrier for j = -1 ..
+  // nkt - 1; waves 4-7 pass one extra barrier first and waves 0-3 one at the
+  // end, so waves 4-7 run each step one phase after waves 0-3.  Waves 0-3
+  // issue the tile loads in their M step (K(j+2) and V(j+1) into the slots
+  // that K(j) and V(j-1) left; both groups finished reading those one phase
+  // earlier) and wait for them before the barrier after their V step, which
+  // precedes every read of those tiles.
+  if (lag) phase_barrier();
+  for (int j = -1; j < nkt; ++j) {
+    if (j >= 0 && j < nw) o_tile(j, pb);
+    if (lag == 0 && j >= 0) {
+      if (j + 2 < nkt) issue_k4(j + 2);
+      if (j + 1 < nkt) issue_v4(j + 1);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+    if (j + 1 < nw) s_tile(j + 1);
+    phase_barrier();
+    if (j + 1 < nw) {
+      softmax_a(j + 1);
+      const float alpha = softmax_b(pb);
+      rescale(alpha);
+    }
+    if (lag == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+    phase_barrier();
   }
+  if (!lag) phase_barrier();
 
   // normalise and store O[s, h, d]; lane holds query c32 and, per 32-d block,
   // d = 8 (r/4) + 4 hl + r%4
