@@ -19,11 +19,17 @@
 //    v_mfma_f32_32x32x16_bf16, so a lane's accumulators hold 4 consecutive
 //    output features of one token: the epilogue writes 16-byte (fp32) or
 //    8-byte (bf16) vectors.
-//  * Two LDS stages, one barrier per 64-k step.  The step's body is pinned
-//    with scheduling barriers: fragment reads for sub-step kk+1 are issued
-//    before the MFMAs of sub-step kk, the next step's tile loads go out in the
-//    first two sub-steps, and the last sub-step's MFMAs are split around the
-//    barrier so that the next step's first fragment reads overlap them.
+//  * Two LDS stages.  8-wave tiles of at most 256 columns run a ping-pong
+//    loop: each wave alternates a phase that reads a whole stage's fragments
+//    (and issues tile loads) with a phase that issues the stage's MFMAs, and
+//    the two waves of a SIMD run half a step apart, so one wave's MFMAs run
+//    while the other reads.  The 256x320 tile (too many fragment registers
+//    for that) and the 4-wave tiles run one barrier per 64-k step with the
+//    step's body pinned by scheduling barriers: fragment reads for sub-step
+//    kk+1 are issued before the MFMAs of sub-step kk, the next step's tile
+//    loads go out in the first two sub-steps, and the last sub-step's MFMAs
+//    are split around the barrier so that the next step's first fragment
+//    reads overlap them.
 //  * 256x256 tiles run 8 waves (2 per SIMD, 128x64 per wave, accumulators in
 //    128 VGPRs), or for fp32 partials 4 waves of 128x128 (one per SIMD, 256
 //    accumulators, tile loads and fragment reads paired with MFMAs by
@@ -230,6 +236,115 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   auto pin = []() { __builtin_amdgcn_sched_barrier(0); };
 
   const int nk = (K + C::BK - 1) / C::BK;
+  // Ping-pong loop (8 waves, 256 rows, at most 256 columns; wider tiles have
+  // no registers for a whole stage of fragments): each wave reads all of a
+  // stage's fragments in one phase and issues the stage's MFMAs in the next,
+  // with a workgroup barrier after each phase.  Waves 4-7, the second wave of
+  // each SIMD, pass one extra barrier first (waves 0-3 one at the end), so
+  // they run one phase later: one wave's MFMAs run while the other wave of
+  // its SIMD reads fragments and issues tile loads.  Waves 0-3 load the X
+  // tiles (at the start of their read phase, into the slot the stage before
+  // left), waves 4-7 the W tiles (at the end of their read phase, two stages
+  // ahead, into the slot they have just read); each group waits for its own
+  // loads before the barrier that precedes the first read of them.  The
+  // accumulation order is the in-step loop's, so the results are the same.
+  constexpr bool kPP = C::NW == 8 && C::BM == 256 && C::BN <= 256;
+  if constexpr (kPP) {
+    const int lag = wave >> 2, q = wave & 3;
+    constexpr int LX = C::BM / 32, LW = C::BN / 32;   // loads per wave per stage (rows / 4 waves / 8 rows)
+    const int L8 = lag ? LW : LX;
+    uint32_t o8[2];
+    int k8[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int row = (q * L8 + e) * 8 + lrow;
+      k8[e] = 8 * dswz(row, lpos);
+      o8[e] = (uint32_t)(row * K + k8[e]) * 2u;
+    }
+    // Rows of this wave's loads: X rows (q LX + i) * 8 + lrow for waves 0-3,
+    // W rows (q LW + i) * 8 + lrow for waves 4-7 (SwiGLU up rows when they
+    // lie in [BN/2, BN): the resource then starts at row N + n0).
+    const bool up8 = EPI == 1 && q * LW * 8 >= C::BN / 2;
+    const uint32_t wrows8 = (uint32_t)min(OUT_BN, N - n0);
+    const __amdgpu_buffer_rsrc_t wr8 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(W + (int64_t)(up8 ? N + n0 : n0) * K), 0, wrows8 * (uint32_t)K * 2u, 0x00020000);
+    const uint32_t shift8 = up8 ? (uint32_t)(C::BN / 2) * (uint32_t)K * 2u : 0u;
+    auto load8 = [&](int k0, int stage) {
+      TPL_LDS uint16_t* base = (TPL_LDS uint16_t*)lds + stage * C::STAGE;
+      if (lag) {
+#pragma unroll
+        for (int i = 0; i < LW; ++i) {
+          const int e = i & 1;
+          const uint32_t off = (k0 + k8[e] < K) ? o8[e] + (uint32_t)(i >> 1) * rows16 + (uint32_t)k0 * 2u - shift8
+                                                : 0x80000000u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              wr8, (TPL_LDS void*)(base + C::BM * C::BK + (q * LW + i) * 8 * C::BK), 16, off, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < LX; ++i) {
+          const int e = i & 1;
+          const uint32_t off = (k0 + k8[e] < K) ? o8[e] + (uint32_t)(i >> 1) * rows16 + (uint32_t)k0 * 2u
+                                                : 0x80000000u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              xr, (TPL_LDS void*)(base + (q * LX + i) * 8 * C::BK), 16, off, 0, 0, 0);
+        }
+      }
+    };
+    bf16x8 fa4[4][C::FA], fb4[4][C::FB];
+    auto read4 = [&](int stage) {
+      const char* sbase = reinterpret_cast<const char*>(lds) + stage * C::STAGE * 2;
+      const char* abase = sbase + (C::BM + a_row0 + frow) * C::BK * 2;
+      const char* bbase = sbase + (b_row0 + frow) * C::BK * 2;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int cofs = ((2 * kk + fh) ^ fsw) * 16;
+#pragma unroll
+        for (int i = 0; i < C::FA; ++i) {
+          const int r = !kPairInWave ? i * 32 : i < C::FA / 2 ? i * 32 : C::BN / 2 + (i - C::FA / 2) * 32;
+          fa4[kk][i] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + r * C::BK * 2 + cofs));
+        }
+#pragma unroll
+        for (int j = 0; j < C::FB; ++j)
+          fb4[kk][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbase + j * 32 * C::BK * 2 + cofs));
+      }
+    };
+    auto phase_barrier = [&]() {
+      pin();
+      __builtin_amdgcn_s_barrier();
+      pin();
+    };
+    load8(0, 0);
+    if (lag && nk > 1) load8(C::BK, 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (lag) phase_barrier();
+    for (int t = 0; t < nk; ++t) {
+      const int st = t & 1;
+      // read phase: waves 0-3 first load X of stage t+1 (the slot stage t-1
+      // left, read by waves 4-7 one phase ago); waves 4-7 load W of stage t+2
+      // after their own reads of stage t (read by waves 0-3 one phase ago)
+      if (lag == 0 && t + 1 < nk) load8((t + 1) * C::BK, st ^ 1);
+      read4(st);
+      if (lag) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this stage's fragments are in registers
+        __builtin_amdgcn_s_waitcnt(kWaitVm0); // W of stage t+1 has landed
+        if (t + 2 < nk) load8((t + 2) * C::BK, st);
+      }
+      phase_barrier();
+      // MFMA phase
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i = 0; i < C::FA; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa4[kk][i], fb4[kk][j], acc[i][j], 0, 0, 0);
+      if (lag == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);   // X of stage t+1 has landed
+      phase_barrier();
+    }
+    if (!lag) phase_barrier();
+  } else {
   load_x(0, 0);
   load_w(0, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -301,6 +416,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
     if (more) read_frags(st ^ 1, 0, 0);
     mfmas(1, C::FA / 2, C::FA);
     pin();
+  }
   }
 
   // Epilogue.  acc[i][j] lane holds token m = wm*TM + 32j + (lane&31) and
