@@ -24,18 +24,16 @@
 //    (and issues tile loads) with a phase that issues the stage's MFMAs, and
 //    the two waves of a SIMD run half a step apart, so one wave's MFMAs run
 //    while the other reads.  The 256x320 tile (too many fragment registers
-//    for that) and the 4-wave tiles run one barrier per 64-k step with the
-//    step's body pinned by scheduling barriers: fragment reads for sub-step
-//    kk+1 are issued before the MFMAs of sub-step kk, the next step's tile
-//    loads go out in the first two sub-steps, and the last sub-step's MFMAs
-//    are split around the barrier so that the next step's first fragment
-//    reads overlap them.
+//    for that) and the 4-wave 128x128 tile run one barrier per 64-k step,
+//    the step's body pinned by scheduling barriers: fragment reads for
+//    sub-step kk+1 are issued before the MFMAs of sub-step kk, the next
+//    step's tile loads go out in the first two sub-steps, and the last
+//    sub-step's MFMAs are split around the barrier so that the next step's
+//    first fragment reads overlap them.
 //  * 256x256 tiles run 8 waves (2 per SIMD, 128x64 per wave, accumulators in
-//    128 VGPRs), or for fp32 partials 4 waves of 128x128 (one per SIMD, 256
-//    accumulators, tile loads and fragment reads paired with MFMAs by
-//    scheduling groups); 128x128 tiles run 4 waves with 2 workgroups per CU,
-//    and 256x320 and 256x192 tiles 8 waves of 64x160 and 64x96, for grids
-//    that 256x256 tiles would leave with a partly empty last round.
+//    128 VGPRs); 128x128 tiles run 4 waves with 2 workgroups per CU, and
+//    256x320 and 256x192 tiles 8 waves of 64x160 and 64x96, for grids that
+//    256x256 tiles would leave with a partly empty last round.
 //  * SwiGLU: the W tile holds BN/2 gate rows then the matching BN/2 up rows.
 //    With an even number of W fragments per wave, each wave reads gate and up
 //    fragments of the same outputs and applies the activation in registers.
@@ -64,17 +62,6 @@ struct DmaTile {
 };
 
 __device__ __forceinline__ int dswz(int row, int kc) { return kc ^ ((row >> 1) & 7); }
-
-// Scheduling groups: N times (one instruction of class MASK, then one MFMA).
-constexpr int kSgMfma = 0x008, kSgVmem = 0x010, kSgDsRead = 0x100;
-template <int MASK, int N>
-__device__ __forceinline__ void sg_pairs() {
-#pragma unroll
-  for (int g = 0; g < N; ++g) {
-    __builtin_amdgcn_sched_group_barrier(MASK, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-  }
-}
 
 // EPI: 0 = plain product; 1 = SwiGLU on a paired tile (W rows [0, I) gate,
 // [I, 2I) up; the tile's first BN/2 W rows are gate rows n0.., the rest the
@@ -351,45 +338,6 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   __syncthreads();
   read_frags(0, 0, 0);
   pin();
-  if constexpr (C::NW == 4 && C::BM == 256) {
-    // One wave per SIMD: nothing else hides this wave's load issue or LDS
-    // latency, so each tile load and fragment read is paired with one MFMA
-    // (scheduling groups).  Loads past K use out-of-range offsets (zeros) so
-    // that every step has the same instruction mix.
-    for (int t = 0; t < nk; ++t) {
-      const int st = t & 1;
-      const int k1 = (t + 1) * C::BK;
-      // sub-step 0: X loads of the next step, fragments of sub-step 1
-      load_x(k1, st ^ 1);
-      read_frags(st, 1, 1);
-      mfmas(0, 0, C::FA);
-      sg_pairs<kSgVmem, C::XL>();
-      sg_pairs<kSgDsRead, C::FA + C::FB>();
-      pin();
-      // sub-step 1: W loads of the next step, fragments of sub-step 2
-      load_w(k1, st ^ 1);
-      read_frags(st, 2, 0);
-      mfmas(1, 0, C::FA);
-      sg_pairs<kSgVmem, C::WL>();
-      sg_pairs<kSgDsRead, C::FA + C::FB>();
-      pin();
-      // sub-step 2
-      read_frags(st, 3, 1);
-      mfmas(0, 0, C::FA);
-      sg_pairs<kSgDsRead, C::FA + C::FB>();
-      pin();
-      // sub-step 3, split around the barrier that publishes the next stage
-      mfmas(1, 0, C::FA / 2);
-      pin();
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      __builtin_amdgcn_s_barrier();
-      pin();
-      read_frags(st ^ 1, 0, 0);   // unused after the last step
-      mfmas(1, C::FA / 2, C::FA);
-      sg_pairs<kSgDsRead, C::FA + C::FB>();
-      pin();
-    }
-  } else
   for (int t = 0; t < nk; ++t) {
     const int st = t & 1;
     const bool more = t + 1 < nk;
@@ -539,9 +487,6 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
 
 using Dma256 = DmaTile<256, 256, 2, 4>;   // 8 waves, one workgroup per CU
 using Dma128 = DmaTile<128, 128, 2, 2>;   // 4 waves, two workgroups per CU
-// 256x256 with 4 waves of 128x128 (one per SIMD, 256 accumulators each): a
-// third less LDS fragment traffic per MFMA than 8 waves of 128x64.
-using Dma256w4 = DmaTile<256, 256, 2, 2>;
 // 256x320: 8 waves of 64x160 (144 KB of LDS for two stages).  For N where
 // 256x256 tiles leave a mostly empty last round, e.g. the fused QKV at
 // N = 5120: 16 x 16 tiles fill 256 CUs exactly once.
@@ -550,8 +495,6 @@ using Dma320 = DmaTile<256, 320, 4, 2>;
 // partly, e.g. a 2048 x 6144 output: 8 x 32 tiles fill 256 CUs once where
 // 8 x 24 tiles of 256x256 would leave a quarter of them idle.
 using Dma192 = DmaTile<256, 192, 4, 2>;
-// 256x192 with 4 waves of 128x96 (192 accumulators each), for fp32 outputs.
-using Dma192w4 = DmaTile<256, 192, 2, 2>;
 
 template <class C, int EPI>
 static tp_status launch_dma(const void* x, const void* w, void* y, int M, int N, int K,
@@ -599,11 +542,6 @@ int gemm_dma_pick_tile(int M, int N, bool wide) {
 tp_status gemm_bf16_dma(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                         bool out_f32, bool vec_out, hipStream_t s, int force_tile) {
   const int pick = force_tile >= 0 ? force_tile : gemm_dma_pick_tile((int)M, (int)N, true);
-  // fp32 partials (the row-parallel products) run 2-3% faster on 4 waves of
-  // 128x128 than on 8 waves of 128x64, and on 4 waves of 128x96 than on 8 of
-  // 64x96; bf16 outputs run alike (256x256) or faster on 8 waves (256x192).
-  if (pick == 0 && out_f32) return launch_dma<Dma256w4, 0>(x, w, y, (int)M, (int)N, (int)K, true, vec_out, s);
-  if (pick == 3 && out_f32) return launch_dma<Dma192w4, 0>(x, w, y, (int)M, (int)N, (int)K, true, vec_out, s);
   if (pick == 0) return launch_dma<Dma256, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
   if (pick == 2) return launch_dma<Dma320, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);
   if (pick == 3) return launch_dma<Dma192, 0>(x, w, y, (int)M, (int)N, (int)K, out_f32, vec_out, s);

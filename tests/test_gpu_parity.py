@@ -116,9 +116,9 @@ def test_linear_bf16_normal(M, K, N):
     assert_within(p, ref, gemm_bound(x.ref, w.ref, ref, False), "row partial fp32")
 
 
-# Row-parallel partials (fp32 out) on each prefill tile shape: 4-wave 256x256,
-# 4-wave 256x192 (ragged K, then ragged M and N), 256x320, 128x128; ragged M, N
-# and K tails.
+# Row-parallel partials (fp32 out) on each prefill tile shape: 256x256,
+# 256x192 (ragged K, then ragged M and N), 256x320, 128x128; ragged M, N and K
+# tails.
 ROW_SHAPES = [(4000, 1000, 4000), (2048, 1032, 6144), (2000, 520, 6100), (4000, 136, 5100), (1000, 520, 1000),
               (65, 64, 16)]
 
