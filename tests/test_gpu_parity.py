@@ -70,6 +70,9 @@ INT_SHAPES = [
     (65, 64, 16), (200, 136, 130), (300, 520, 300), (512, 264, 640), (4000, 264, 4000),
     (4096, 200, 2048), (4000, 136, 5100),   # the last picks 256x320 tiles
     (1800, 136, 4700),                      # 256x192 tiles, ragged M and N
+    # the ping-pong loop with one k-step (256x256; 256x192 with ragged K, M
+    # and N) and with two (256x256, ragged K, M and N)
+    (4096, 64, 4096), (2000, 40, 4100), (4000, 72, 4000),
     # element path (K not a multiple of 8)
     (5, 13, 7), (70, 37, 50),
 ]
