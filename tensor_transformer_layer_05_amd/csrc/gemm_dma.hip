@@ -112,8 +112,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   // Load i of this wave fills LDS rows (wave*L + i)*8 .. +7; lane -> row lane/8,
   // LDS chunk lane%8, which holds global chunk dswz(row, lane%8).
   const int lrow = lane >> 3, lpos = lane & 7;
-  // 4-wave tiles: one offset register per load (their scheduling groups pair
-  // each load with an MFMA, and measured faster so).  8-wave tiles: the
+  // 4-wave (128x128) tiles: one offset register per load.  8-wave tiles: the
   // swizzle (row/2) % 8 depends only on the parity of wave*L + i, so two base
   // offsets per operand plus a multiple of 16 rows address every load (fewer
   // registers and VALU instructions; the same addresses).
@@ -173,7 +172,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   // Every fragment row is frow plus a multiple of 16, so the chunk swizzle
   // (row/2) % 8 is the lane's (frow/2) % 8 for all of them: one chunk offset
   // per sub-step addresses every read (8-wave tiles; the 4-wave tile keeps
-  // per-row addressing, which its scheduling groups were tuned with).
+  // per-row addressing).
   static_assert(C::TM % 16 == 0 && C::TN % 32 == 0 && C::BN % 32 == 0 && C::BM % 16 == 0,
                 "fragment rows keep the lane's swizzle");
   const int fsw = (frow >> 1) & 7;

@@ -129,8 +129,7 @@ include the set-up and warm-up launches.
 Mapping (prefill calls = 2 set-up passes over both ranks + 2 warm-up + 5 timed steps = 9 per rank-0 call):
 - `gemm_bf16_dma_kernel<DmaTile<256,256,2,4>, false, true, 1>`: gate|up with the SwiGLU epilogue, M=4096 K=8192
   2I=28672 -> [4096, 14336].
-- `gemm_bf16_dma_kernel<DmaTile<256,256,2,2>, true, true, 0>`: o_proj (K=4096) and down (K=14336), fp32 partials,
-  on 4 waves of 128x128.
+- `gemm_bf16_dma_kernel<DmaTile<256,256,2,4>, true, true, 0>`: o_proj (K=4096) and down (K=14336), fp32 partials.
 - `gemm_bf16_dma_kernel<DmaTile<256,320,4,2>, false, true, 0>`: fused QKV, N=5120 (16 x 16 tiles).
 - `attn_prefill_tr_kernel`: causal 4096-token attention over 32 local q heads / 4 KV heads.
 - `reduce_rmsnorm_reg_kernel<4>`: sum of the two ranks' attention partials + residual, then the MLP's RMSNorm.
@@ -140,8 +139,7 @@ Mapping (prefill calls = 2 set-up passes over both ranks + 2 warm-up + 5 timed s
 - `attn_decode_kernel<false|true>` + `attn_decode_combine_kernel`: decode attention (contiguous / paged cache).
 - `vocab_argmax_kernel`: the lm_head shard's local greedy step.
 - `gemm_bf16_dma_kernel<DmaTile<256,192,4,2>, false, true, 2>`: the GELU FFN's fc1 with GELU in its epilogue
-  (M=2048 K=12288 N=6144, 8 x 32 tiles); `<DmaTile<256,192,2,2>, true, true, 0>`: its fc2 to fp32
-  partials (N=12288, 4 waves of 128x96).
+  (M=2048 K=12288 N=6144, 8 x 32 tiles); `<..., true, true, 0>`: its fc2 to fp32 partials (N=12288).
 - `reduce_kernel<true, true>` also runs the sum of the FFN's 8 partials.
 
 Decode calls come from the eager and graph-replayed decode figures; kernel durations are per launch.
