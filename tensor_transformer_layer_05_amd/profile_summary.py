@@ -101,10 +101,13 @@ def kernel_stats(out):
     d = json.loads(bench)
     f = sorted((r for r in trace if FUSED in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in f]
-    timed = durs[-d["steps"]:]
+    # launch order: set-up, warm-up, the timed steps, then as many steps with
+    # an event pair around every call (the per-call breakdown)
+    timed = durs[-2 * d["steps"]:-d["steps"]]
     lines = []
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        name = r["Name"].split("(")[0].replace("void ", "")
+        name = r["Name"].replace("void ", "")
+        name = name[:name.rfind("(")] if name.endswith(")") else name   # drop the parameter list
         lines.append(f'| `{name[:100]}` | {r["Calls"]} | {float(r["AverageNs"]) / 1e3:.1f} | '
                      f'{float(r["MinNs"]) / 1e3:.1f} | {float(r["MaxNs"]) / 1e3:.1f} | {float(r["Percentage"]):.2f} |')
     return f"""# Kernel stats: bench.py (prefill layer shard + decode shards), rocprofv3 --kernel-trace --stats
@@ -118,15 +121,17 @@ python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
 
 The bench line of the same run (under the profiler): value {d['value']} TFLOP/s, {d['ms_per_step']} ms per step;
 the dominant kernel's event-timed average {d['roofline']['avg_launch_ms'] * 1e3:.1f} us. From the trace of the same
-run, the {len(timed)} timed-step launches of that kernel (`gemm_bf16_dma_kernel<..., 1>`, the last {len(timed)} of its
-{len(durs)}) average {sum(timed) / len(timed):.1f} us ({', '.join(f'{x:.1f}' for x in timed)}); the table's averages
-include the set-up and warm-up launches.
+run, the {len(timed)} timed-step launches of that kernel (`gemm_bf16_dma_kernel<..., 1>`, launches
+{len(durs) - 2 * len(timed) + 1}-{len(durs) - len(timed)} of its {len(durs)}; the last {len(timed)} are the per-call breakdown pass) average
+{sum(timed) / len(timed):.1f} us ({', '.join(f'{x:.1f}' for x in timed)}); the table's averages include the set-up and
+warm-up launches.
 
 | kernel | calls | avg us | min us | max us | % time |
 |---|---:|---:|---:|---:|---:|
 """ + "\n".join(lines) + """
 
-Mapping (prefill calls = 2 set-up passes over both ranks + 2 warm-up + 5 timed steps = 9 per rank-0 call):
+Mapping (prefill calls = 2 set-up passes over both ranks + 2 warm-up + 5 timed steps + 5 breakdown steps = 14
+per rank-0 call):
 - `gemm_bf16_dma_kernel<DmaTile<256,256,2,4>, false, true, 1>`: gate|up with the SwiGLU epilogue, M=4096 K=8192
   2I=28672 -> [4096, 14336].
 - `gemm_bf16_dma_kernel<DmaTile<256,256,2,4>, true, true, 0>`: o_proj (K=4096) and down (K=14336), fp32 partials.
@@ -141,6 +146,8 @@ Mapping (prefill calls = 2 set-up passes over both ranks + 2 warm-up + 5 timed s
 - `gemm_bf16_dma_kernel<DmaTile<256,192,4,2>, false, true, 2>`: the GELU FFN's fc1 with GELU in its epilogue
   (M=2048 K=12288 N=6144, 8 x 32 tiles); `<..., true, true, 0>`: its fc2 to fp32 partials (N=12288).
 - `reduce_kernel<true, true>` also runs the sum of the FFN's 8 partials.
+- `stream_read_kernel<...>` (libtpref, measurement only): the plain read-only stream behind `hbm_read_ceiling`
+  and each decode shard's `size_stream_ms` (every configuration warmed with 100 ms of back-to-back calls).
 
 Decode calls come from the eager and graph-replayed decode figures; kernel durations are per launch.
 """
