@@ -22,8 +22,8 @@
 //    barrier before the loop and waves 0-3 one after it.
 //  * K and V tiles reach LDS through buffer_load_dwordx4 ... lds (1 KB = 4
 //    key rows per wave-level load), in two slots each; K runs two tiles ahead
-//    of the O product and V one.  Inside the loop only waves 0-3 load (in
-//    their MFMA step, after the O product) and they wait for the loads before
+//    of the O product and V one.  Inside the loop only waves 0-3 load (at the
+//    end of their MFMA step) and they wait for the loads before
 //    the barrier that ends their next VALU step; the transposing V reads wait
 //    for every load their wave has in flight, so waves 4-7 issue none.  Rows
 //    past the key span read as zero through the buffer bound.  LDS rows are
@@ -332,18 +332,18 @@ __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
   // Every wave runs the same steps M(j), barrier, V(j), barrier for j = -1 ..
   // nkt - 1; waves 4-7 pass one extra barrier first and waves 0-3 one at the
   // end, so waves 4-7 run each step one phase after waves 0-3.  Waves 0-3
-  // issue the tile loads in their M step (K(j+2) and V(j+1) into the slots
-  // that K(j) and V(j-1) left; both groups finished reading those one phase
-  // earlier) and wait for them before the barrier after their V step, which
-  // precedes every read of those tiles.
+  // issue the tile loads at the end of their M step (K(j+2) and V(j+1) into
+  // the slots that K(j) and V(j-1) left; both groups finished reading those
+  // one phase earlier) and wait for them before the barrier after their V
+  // step, which precedes every read of those tiles.
   if (lag) phase_barrier();
   for (int j = -1; j < nkt; ++j) {
     if (j >= 0 && j < nw) o_tile(j, pb);
+    if (j + 1 < nw) s_tile(j + 1);
     if (lag == 0 && j >= 0) {
       if (j + 2 < nkt) issue_k4(j + 2);
       if (j + 1 < nkt) issue_v4(j + 1);
     }
-    if (j + 1 < nw) s_tile(j + 1);
     phase_barrier();
     if (j + 1 < nw) {
       softmax_a(j + 1);
