@@ -228,12 +228,13 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
   // with a workgroup barrier after each phase.  Waves 4-7, the second wave of
   // each SIMD, pass one extra barrier first (waves 0-3 one at the end), so
   // they run one phase later: one wave's MFMAs run while the other wave of
-  // its SIMD reads fragments and issues tile loads.  Waves 0-3 load the X
-  // tiles (at the start of their read phase, into the slot the stage before
-  // left), waves 4-7 the W tiles (at the end of their read phase, two stages
-  // ahead, into the slot they have just read); each group waits for its own
-  // loads before the barrier that precedes the first read of them.  The
-  // accumulation order is the in-step loop's, so the results are the same.
+  // its SIMD reads fragments and issues tile loads.  At the end of its read
+  // phase, each wave of 0-3 loads its share of the next stage's X tile (into
+  // the slot the stage before left) and each wave of 4-7 its share of the W
+  // tile two stages ahead (into the slot it has just read); each group waits
+  // for its own loads before the barrier that precedes the first read of
+  // them.  The accumulation order is the in-step loop's, so the results are
+  // the same.
   constexpr bool kPP = C::NW == 8 && C::BM == 256 && C::BN <= 256;
   if constexpr (kPP) {
     const int lag = wave >> 2, q = wave & 3;
@@ -307,11 +308,12 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
     if (lag) phase_barrier();
     for (int t = 0; t < nk; ++t) {
       const int st = t & 1;
-      // read phase: waves 0-3 first load X of stage t+1 (the slot stage t-1
-      // left, read by waves 4-7 one phase ago); waves 4-7 load W of stage t+2
-      // after their own reads of stage t (read by waves 0-3 one phase ago)
-      if (lag == 0 && t + 1 < nk) load8((t + 1) * C::BK, st ^ 1);
+      // read phase: after their reads of stage t, waves 0-3 load X of stage
+      // t+1 (into the slot stage t-1 left, read by waves 4-7 one phase ago)
+      // and waves 4-7 load W of stage t+2 (into the slot of stage t, read by
+      // waves 0-3 one phase ago)
       read4(st);
+      if (lag == 0 && t + 1 < nk) load8((t + 1) * C::BK, st ^ 1);
       if (lag) {
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this stage's fragments are in registers
         __builtin_amdgcn_s_waitcnt(kWaitVm0); // W of stage t+1 has landed
