@@ -27,6 +27,7 @@ Key "ffn_tp8": rank 0's shard of the GELU FFN at TP=8 (2048 tokens, hidden
 from __future__ import annotations
 
 import argparse
+import itertools
 import json
 import os
 import sys
@@ -370,6 +371,7 @@ def _decode_entry(ms_eager, ms_graph, ms_layers, byts, fl):
 # of their HBM bytes is used only while these sources still hash as recorded
 DECODE_SRCS = ["tensor_transformer_layer_05_amd/csrc/gemm_stream.hip",
                "tensor_transformer_layer_05_amd/csrc/gemm_stream_dma.hip",
+               "tensor_transformer_layer_05_amd/csrc/gemv_dot.hip",
                "tensor_transformer_layer_05_amd/csrc/attention_decode.hip",
                "tensor_transformer_layer_05_amd/csrc/argmax.hip",
                "tensor_transformer_layer_05_amd/csrc/tplayer_api.hip",
@@ -380,17 +382,21 @@ def read_ceiling(steps=10, warmup=3, nbytes=1 << 30):
     """Attainable HBM read rate on this GPU: the hand-written read-only
     stream of libtpref (16-byte loads per lane, chunks of 4-16 KB per wave with
     the next chunk in flight, like the decode weight streams) over 1 GiB, for
-    several grid shapes; the best median rate is the ceiling the decode shards
-    are also compared with."""
+    several grid shapes, with and without non-temporal loads and with a slice
+    per wave or chunks interleaved over all waves; the best median rate is the
+    ceiling the decode shards are also compared with."""
     from tensor_transformer_layer_05_amd import ref
     buf = torch.ones(nbytes, dtype=torch.uint8, device=DEV)
     out = torch.empty(4096 * 16 * 64, dtype=torch.int32, device=DEV)
     best, rows = None, []
-    for wg, waves, u in ((256, 8, 8), (512, 8, 8), (1024, 8, 4), (256, 16, 8), (512, 16, 4),
-                         (256, 8, 16), (2048, 4, 4)):
-        ms = _median_ms(lambda i: ref.stream_read(buf, out, wg, waves, u), steps, warmup)
+    for (wg, waves, u), fl in itertools.product(
+            ((256, 8, 8), (512, 8, 8), (1024, 8, 4), (256, 16, 8), (512, 16, 4), (256, 8, 16),
+             (2048, 4, 4)), (0, ref.NONTEMPORAL, ref.SPREAD, ref.NONTEMPORAL | ref.SPREAD)):
+        ms = _median_ms(lambda i: ref.stream_read(buf, out, wg, waves, u, fl), steps, warmup)
         gbs = nbytes / ms / 1e6
-        rows.append({"workgroups": wg, "waves": waves, "loads_per_lane": u, "GB/s": round(gbs, 1)})
+        rows.append({"workgroups": wg, "waves": waves, "loads_per_lane": u,
+                     "nontemporal": bool(fl & ref.NONTEMPORAL), "spread": bool(fl & ref.SPREAD),
+                     "GB/s": round(gbs, 1)})
         if best is None or gbs > best["GB/s"]:
             best = rows[-1]
     del buf
@@ -404,15 +410,18 @@ def stream_ms(nbytes, steps=30, warmup=5):
     and timed like a decode step: the fastest of four grid shapes.  A decode
     shard moves at least its algorithmic bytes, so this is the time a single
     plain read of that many bytes takes here, fixed launch and first-load
-    latency included."""
+    latency included (the fastest of the stream's load options too)."""
     from tensor_transformer_layer_05_amd import ref
     n = max(4096, int(nbytes) // 4096 * 4096)
     copies = max(2, int(600e6 // n) + 1)
     bufs = [torch.ones(n, dtype=torch.uint8, device=DEV) for _ in range(copies)]
     out = torch.empty(4096 * 16 * 64, dtype=torch.int32, device=DEV)
     best = None
-    for wg, waves, u in ((256, 8, 8), (512, 8, 8), (1024, 8, 4), (256, 16, 8)):
-        ms = _median_ms(lambda i: ref.stream_read(bufs[i % copies], out, wg, waves, u), steps, warmup)
+    for (wg, waves, u), fl in itertools.product(
+            ((256, 8, 8), (512, 8, 8), (1024, 8, 4), (256, 16, 8)),
+            (0, ref.NONTEMPORAL, ref.SPREAD, ref.NONTEMPORAL | ref.SPREAD)):
+        ms = _median_ms(lambda i: ref.stream_read(bufs[i % copies], out, wg, waves, u, fl), steps,
+                        warmup)
         best = ms if best is None else min(best, ms)
     del bufs
     return best

@@ -19,7 +19,8 @@
 //
 // Each of the 4 waves streams its own contiguous run of 32-key tiles through
 // a private two-stage LDS ring with buffer_load_dwordx4 ... lds (1 KB = 4 key
-// rows per load, rows past the span reading as zero): the next tile's K and V
+// rows per load, rows past the span reading as zero, non-temporal since each
+// cached byte is read once per step): the next tile's K and V
 // are in flight while the current one is computed, with an online softmax
 // across tiles.  There is no barrier in the loop; the waves' (max, sum, O^T)
 // are merged through LDS at the end.
@@ -188,15 +189,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       if constexpr (PAGED) {
         const uint32_t rb = (uint32_t)((int64_t)(t % a.bs) * a.ks1 * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(pk[u >= 4], (TPL_DLDS void*)(kd + u * 4 * kDecD), 16,
-                                                 ok ? rb + (uint32_t)kc * 16u : 0x80000000u, 0, 0, 0);
+                                                 ok ? rb + (uint32_t)kc * 16u : 0x80000000u, 0, 0, kLoadStream);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(pv[u >= 4], (TPL_DLDS void*)(vd + u * 4 * kDecD), 16,
-                                                 ok ? rb + (uint32_t)vc * 16u : 0x80000000u, 0, 0, 0);
+                                                 ok ? rb + (uint32_t)vc * 16u : 0x80000000u, 0, 0, kLoadStream);
       } else {
         const uint32_t rb = (uint32_t)((int64_t)t * a.ks1 * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TPL_DLDS void*)(kd + u * 4 * kDecD), 16,
-                                                 ok ? rb + (uint32_t)kc * 16u : 0x80000000u, 0, 0, 0);
+                                                 ok ? rb + (uint32_t)kc * 16u : 0x80000000u, 0, 0, kLoadStream);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TPL_DLDS void*)(vd + u * 4 * kDecD), 16,
-                                                 ok ? rb + (uint32_t)vc * 16u : 0x80000000u, 0, 0, 0);
+                                                 ok ? rb + (uint32_t)vc * 16u : 0x80000000u, 0, 0, kLoadStream);
       }
     }
   };

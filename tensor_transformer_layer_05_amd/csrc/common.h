@@ -17,6 +17,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kNumXcd = 8;    // MI355X: 8 accelerator complex dies, 32 CUs each
 constexpr int kMaxArgmaxRanks = 64;   // ranks combined by one vocab argmax reduce call
+// Cache-policy operand of buffer loads: non-temporal (streaming).  For bytes
+// read once per call (decode weights, the KV cache) whose loads cover whole
+// 128-byte lines, a plain read of 1 GiB measured 6.7 TB/s with it against
+// 5.9 TB/s without; loads that take half a line per instruction slowed down.
+constexpr int kLoadStream = 2;
 
 // ---- bf16 <-> fp32 ---------------------------------------------------------
 

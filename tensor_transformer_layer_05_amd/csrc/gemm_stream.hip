@@ -204,6 +204,11 @@ static void launch_stream(const void* x, const void* w, void* y, int M, int N, i
 
 tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M, int64_t N,
                                int64_t K, bool out_f32, hipStream_t s);
+bool gemv_dot_fits(int64_t M, int64_t K);
+tp_status gemv_dot(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                   bool out_f32, hipStream_t s);
+tp_status gemv_dot_act(const void* x, const void* w, void* h, int64_t M, int64_t I, int64_t K,
+                       int act, hipStream_t s);
 
 // Waves per workgroup of the one-token-tile decode linear on an [N, K]
 // weight: 16 waves (1024 threads) when there are few row tiles to spread over
@@ -249,6 +254,7 @@ static bool stream_regs(int64_t M, int64_t N, int64_t K) {
 
 tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                            bool out_f32, hipStream_t s) {
+  if (gemv_dot_fits(M, K)) return gemv_dot(x, w, y, M, N, K, out_f32, s);
   if (!stream_regs(M, N, K)) return gemm_bf16_stream_dma(x, w, y, M, N, K, out_f32, s);
   const int waves = stream_waves(N, K);
   const int kw = stream_kw(K, waves);
@@ -271,6 +277,7 @@ tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_
 tp_status gemm_bf16_stream_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
                                int64_t K, int act, hipStream_t s) {
   const int64_t rows = act == TP_ACT_SWIGLU ? 2 * I : I;
+  if (gemv_dot_fits(M, K)) return gemv_dot_act(x, w, h, M, I, K, act, s);
   if (!stream_regs(M, rows, K)) return gemm_bf16_stream_dma_act(x, w, h, M, I, K, act, s);
   const int waves = stream_waves(rows, K);
   const int kw = stream_kw(K, waves);

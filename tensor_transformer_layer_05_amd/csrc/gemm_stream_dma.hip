@@ -16,6 +16,9 @@
 //     through a private S-stage LDS ring with buffer_load_dwordx4 ... lds: one
 //     wave-level load writes 4 rows x 256 contiguous bytes (two whole lines
 //     per row), for weights and tokens alike;
+//   * weight loads are non-temporal (each weight byte is read once per call);
+//     token loads keep the default policy, since every workgroup re-reads
+//     the token rows from L2;
 //   * 256-byte LDS rows keep 16-byte chunk c of row r at c ^ (r % 16), so the
 //     fragment reads of v_mfma_f32_16x16x32_bf16 (16 rows x one chunk per
 //     quarter-wave) hit 16 distinct bank groups;
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_stream_dma_kernel(
       if (d < WROWS / 4) {       // weight rows: tile d / 4, row row % 16 in it
         const __amdgpu_buffer_rsrc_t rs = d < 4 ? wr[0] : wr[RT - 1];
         const uint32_t off = k < ke ? (uint32_t)((row & 15) * K + k) * 2u : kSOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TPL_LDS void*)(dst + d * 4 * 128), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TPL_LDS void*)(dst + d * 4 * 128), 16, off, 0, 0, kLoadStream);
       } else {                   // token rows
         const uint32_t off = k < ke ? (uint32_t)((row - WROWS) * K + k) * 2u : kSOob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (TPL_LDS void*)(dst + d * 4 * 128), 16, off, 0, 0, 0);

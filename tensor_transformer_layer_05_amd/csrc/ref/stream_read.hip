@@ -12,6 +12,10 @@
 //     U = 8 with 8 waves per workgroup, one workgroup per CU);
 //   * the loaded words are folded with XOR into one word per lane, stored once,
 //     so no load can be dropped; the store traffic is negligible.
+// Two options: non-temporal loads (the streaming cache policy), and chunks
+// interleaved over all waves (wave w reads chunks w, w + nw, w + 2 nw, ... of
+// the whole buffer) instead of one contiguous slice per wave.  On MI355X the
+// non-temporal loads read 1 GiB at 6.7 TB/s against 5.9 without them.
 // Loads past the wave's slice use an offset beyond the buffer resource's bound
 // and return zero without touching memory, so the loop has no per-lane branch.
 #include <hip/hip_runtime.h>
@@ -24,26 +28,37 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kOob = 0x80000000u;
 
-template <int U>
+template <int U, int AUX, bool SPREAD>
 __global__ __launch_bounds__(1024) void stream_read_kernel(const uint8_t* __restrict__ src,
                                                            uint64_t per_wave, uint64_t bytes,
                                                            uint32_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
+  const uint64_t nw = (uint64_t)gridDim.x * (blockDim.x >> 6);
   const uint64_t gw = (uint64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const uint64_t begin = gw * per_wave;
-  const uint64_t len = begin < bytes ? (bytes - begin < per_wave ? bytes - begin : per_wave) : 0;
+  constexpr uint32_t kChunk = U * 1024u;
+  uint64_t begin, len;
+  uint32_t nc;
+  if constexpr (SPREAD) {   // the whole buffer (below 2 GiB); chunks gw, gw + nw, ...
+    begin = 0;
+    len = bytes;
+    const uint64_t total = (bytes + kChunk - 1) / kChunk;
+    nc = gw < total ? (uint32_t)((total - gw + nw - 1) / nw) : 0;
+  } else {
+    begin = gw * per_wave;
+    len = begin < bytes ? (bytes - begin < per_wave ? bytes - begin : per_wave) : 0;
+    nc = (uint32_t)((len + kChunk - 1) / kChunk);
+  }
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(src + (begin < bytes ? begin : 0)), 0, (uint32_t)len, 0x00020000);
-  constexpr uint32_t kChunk = U * 1024u;
-  const uint32_t nc = (uint32_t)((len + kChunk - 1) / kChunk);
   u32x4 a[U], b[U];
   uint32_t acc = 0;
   auto load = [&](uint32_t c, u32x4 (&v)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint64_t off = (uint64_t)c * kChunk + (uint32_t)u * 1024u + (uint32_t)lane * 16u;
+      const uint64_t cc = SPREAD ? (uint64_t)c * nw + gw : (uint64_t)c;
+      const uint64_t off = cc * kChunk + (uint32_t)u * 1024u + (uint32_t)lane * 16u;
       v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            r, off < len ? (uint32_t)off : kOob, 0, 0));
+                                            r, off < len ? (uint32_t)off : kOob, 0, AUX));
     }
   };
   auto fold = [&](const u32x4 (&v)[U]) {
@@ -68,11 +83,23 @@ __global__ __launch_bounds__(1024) void stream_read_kernel(const uint8_t* __rest
 
 }  // namespace
 
+template <int U>
+static void launch_u(const uint8_t* src, uint64_t per, uint64_t bytes, uint32_t* out, int flags,
+                     dim3 grid, dim3 block, hipStream_t s) {
+  switch (flags) {
+    case 0: hipLaunchKernelGGL((stream_read_kernel<U, 0, false>), grid, block, 0, s, src, per, bytes, out); break;
+    case 1: hipLaunchKernelGGL((stream_read_kernel<U, 2, false>), grid, block, 0, s, src, per, bytes, out); break;
+    case 2: hipLaunchKernelGGL((stream_read_kernel<U, 0, true>), grid, block, 0, s, src, per, bytes, out); break;
+    default: hipLaunchKernelGGL((stream_read_kernel<U, 2, true>), grid, block, 0, s, src, per, bytes, out); break;
+  }
+}
+
 extern "C" int tpref_stream_read(const void* buf, uint64_t bytes, uint32_t* out, int workgroups,
-                                 int waves, int loads_per_lane, void* stream) {
+                                 int waves, int loads_per_lane, int flags, void* stream) {
   if (!buf || !out) return 1;
   if (workgroups <= 0 || workgroups > 65536 || (waves != 4 && waves != 8 && waves != 16)) return 2;
   if (bytes == 0 || (reinterpret_cast<uintptr_t>(buf) % 16) != 0) return 2;
+  if (flags < 0 || flags > 3 || ((flags & 2) && bytes >= (uint64_t{1} << 31))) return 2;
   const uint64_t nw = (uint64_t)workgroups * waves;
   // each wave's slice is a whole number of 1 KB wave loads, below 2^31 bytes
   const uint64_t per = ((bytes + nw - 1) / nw + 1023) / 1024 * 1024;
@@ -81,9 +108,9 @@ extern "C" int tpref_stream_read(const void* buf, uint64_t bytes, uint32_t* out,
   dim3 grid((unsigned)workgroups), block((unsigned)(waves * 64));
   auto src = static_cast<const uint8_t*>(buf);
   switch (loads_per_lane) {
-    case 4: hipLaunchKernelGGL(stream_read_kernel<4>, grid, block, 0, s, src, per, bytes, out); break;
-    case 8: hipLaunchKernelGGL(stream_read_kernel<8>, grid, block, 0, s, src, per, bytes, out); break;
-    case 16: hipLaunchKernelGGL(stream_read_kernel<16>, grid, block, 0, s, src, per, bytes, out); break;
+    case 4: launch_u<4>(src, per, bytes, out, flags, grid, block, s); break;
+    case 8: launch_u<8>(src, per, bytes, out, flags, grid, block, s); break;
+    case 16: launch_u<16>(src, per, bytes, out, flags, grid, block, s); break;
     default: return 2;
   }
   return hipGetLastError() == hipSuccess ? 0 : 6;

@@ -549,6 +549,7 @@ python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
 
 DECODE_SRCS = ["tensor_transformer_layer_05_amd/csrc/gemm_stream.hip",
                "tensor_transformer_layer_05_amd/csrc/gemm_stream_dma.hip",
+               "tensor_transformer_layer_05_amd/csrc/gemv_dot.hip",
                "tensor_transformer_layer_05_amd/csrc/attention_decode.hip",
                "tensor_transformer_layer_05_amd/csrc/argmax.hip",
                "tensor_transformer_layer_05_amd/csrc/tplayer_api.hip",

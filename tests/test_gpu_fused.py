@@ -41,7 +41,10 @@ def _unfused(X, W, act, I_):
 ACT_SHAPES = [
     (1, 1024, 448),      # one token tile, 4 waves
     (1, 8192, 1000),     # one token tile, 16 waves
-    (1, 8192, 3584),     # decode gate|up shard (7168 rows), 8 waves
+    (1, 8192, 3584),     # decode gate|up shard (7168 rows): dot-product kernel
+    (2, 8192, 3584),     # two tokens, two 8-row groups per part
+    (3, 4104, 4100),     # three tokens, ragged K ranges, four row groups per part
+    (3, 16384, 40),      # the largest staged K, one row per workgroup
     (5, 520, 130),       # ragged K range per wave, ragged rows
     (8, 8192, 3584),     # decode gate|up shard at 8 tokens: register kernel, 8 waves
     (13, 16384, 200),    # register kernel, 16 waves, ragged tokens
@@ -115,7 +118,8 @@ def test_column_linear_act(act, M, K, I_):
 
 
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
-@pytest.mark.parametrize("M,K,I_", [(1, 64, 40), (40, 136, 130), (200, 264, 300), (11, 264, 4096)])
+@pytest.mark.parametrize("M,K,I_", [(1, 64, 40), (3, 520, 700), (40, 136, 130), (200, 264, 300),
+                                    (11, 264, 4096)])
 def test_column_linear_act_integer(act, M, K, I_):
     """Integer inputs: every projection is an exact integer in float32, so the
     fused route's only roundings are the fp32 activation and one bf16 store;
@@ -134,6 +138,26 @@ def test_column_linear_act_integer(act, M, K, I_):
         ref = O.local_activation(gg, uu, act)
         cond = 8 + np.abs(gg) * np.abs(gg) + np.abs(gg)
         assert_within(h, ref, (U16 * (1 + 1e-5) + cond * U32) * np.abs(ref) + 1e-30, f"{name} {act}")
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+@pytest.mark.parametrize("M,K,I_", [(1, 8192, 3584), (2, 520, 700), (3, 4104, 1000), (8, 8192, 3584),
+                                    (4, 3584, 4096)])
+def test_fused_equals_activation_of_float32_sums(act, M, K, I_):
+    """Decode routes (dot-product kernel at 1..3 tokens, register kernel,
+    one-token-tile LDS ring): the fused call's float32 sums are the plain
+    call's on the same weight (same K split), so its output is, bit for bit,
+    the activation kernel applied to the float32 partials, rounded to bf16."""
+    log(f"fused == act(fp32 partials) {act} M={M} K={K} I={I_}")
+    rows = 2 * I_ if act == "swiglu" else I_
+    X = dev(I.normal(43, "x", (M, K)))
+    W = dev(I.normal(43, "w", (rows, K), 1.5 / np.sqrt(K)))
+    h = tpl.column_linear_act(X, W, act)
+    P = tpl.row_linear_partial(X, W)
+    a = tpl.swiglu_local(P[:, :I_], P[:, I_:] if act == "swiglu" else None, act)
+    expect = O.round_bf16(a.cpu().numpy().astype(np.float64))
+    got = h.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, expect), f"{np.sum(got != expect)} of {got.size} differ"
 
 
 def test_column_linear_act_none_is_column_linear():

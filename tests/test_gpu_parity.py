@@ -73,6 +73,11 @@ INT_SHAPES = [
     # the ping-pong loop with one k-step (256x256; 256x192 with ragged K, M
     # and N) and with two (256x256, ragged K, M and N)
     (4096, 64, 4096), (2000, 40, 4100), (4000, 72, 4000),
+    # 1..3 tokens: the whole-line dot-product kernel with 1, 2, 4 and 8 row groups
+    # per workgroup, ragged K ranges, a grid of more than one round, the largest
+    # staged K; past it (K = 16392) the register kernel
+    (1, 8192, 16032), (2, 3584, 8192), (3, 8200, 3000), (1, 4104, 20000), (3, 16384, 300),
+    (2, 72, 256), (1, 16392, 64),
     # element path (K not a multiple of 8)
     (5, 13, 7), (70, 37, 50),
 ]
