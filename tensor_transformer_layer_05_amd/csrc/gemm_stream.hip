@@ -1,4 +1,8 @@
-// Decode bf16 linear for 1..3 tokens, and up to 16 on long-K weights: weight streaming.
+// Decode bf16 linear for 4..16 tokens on long-K weights (and 1..3 tokens where
+// K is too long for the dot-product kernel's token stage): weight streaming.
+// The entry points below route 1..3 tokens, and 4..8 on tall weights, to the
+// dot-product kernel (gemv_dot.hip) and the rest of 4..64 tokens to the
+// LDS-ring kernel (gemm_stream_dma.hip).
 //
 //   Y[m, n] = sum_k X[m, k] * W[n, k]
 //
@@ -204,7 +208,7 @@ static void launch_stream(const void* x, const void* w, void* y, int M, int N, i
 
 tp_status gemm_bf16_stream_dma(const void* x, const void* w, void* y, int64_t M, int64_t N,
                                int64_t K, bool out_f32, hipStream_t s);
-bool gemv_dot_fits(int64_t M, int64_t K);
+bool gemv_dot_fits(int64_t M, int64_t rows, int64_t K);
 tp_status gemv_dot(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                    bool out_f32, hipStream_t s);
 tp_status gemv_dot_act(const void* x, const void* w, void* h, int64_t M, int64_t I, int64_t K,
@@ -254,7 +258,7 @@ static bool stream_regs(int64_t M, int64_t N, int64_t K) {
 
 tp_status gemm_bf16_stream(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                            bool out_f32, hipStream_t s) {
-  if (gemv_dot_fits(M, K)) return gemv_dot(x, w, y, M, N, K, out_f32, s);
+  if (gemv_dot_fits(M, N, K)) return gemv_dot(x, w, y, M, N, K, out_f32, s);
   if (!stream_regs(M, N, K)) return gemm_bf16_stream_dma(x, w, y, M, N, K, out_f32, s);
   const int waves = stream_waves(N, K);
   const int kw = stream_kw(K, waves);
@@ -277,7 +281,7 @@ tp_status gemm_bf16_stream_dma_act(const void* x, const void* w, void* h, int64_
 tp_status gemm_bf16_stream_act(const void* x, const void* w, void* h, int64_t M, int64_t I,
                                int64_t K, int act, hipStream_t s) {
   const int64_t rows = act == TP_ACT_SWIGLU ? 2 * I : I;
-  if (gemv_dot_fits(M, K)) return gemv_dot_act(x, w, h, M, I, K, act, s);
+  if (gemv_dot_fits(M, rows, K)) return gemv_dot_act(x, w, h, M, I, K, act, s);
   if (!stream_regs(M, rows, K)) return gemm_bf16_stream_dma_act(x, w, h, M, I, K, act, s);
   const int waves = stream_waves(rows, K);
   const int kw = stream_kw(K, waves);

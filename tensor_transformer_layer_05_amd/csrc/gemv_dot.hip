@@ -1,4 +1,5 @@
-// Decode bf16 linear for 1..3 tokens: weight streaming with whole-line loads.
+// Decode bf16 linear for 1..3 tokens (1..8 on tall weights): weight streaming
+// with whole-line loads.
 //
 //   Y[m, n] = sum_k X[m, k] * W[n, k]
 //
@@ -31,10 +32,12 @@ namespace {
 
 constexpr uint32_t kDotOob = 0x80000000u;   // offset past any buffer bound -> reads 0
 constexpr int kDotWaves = 8;
-constexpr int kDotMaxK = 16384;             // token rows staged in LDS: 3 x 32 KB at most
-// zeroed k past the last 64-k step: a wave's last two batches may read up to
-// 2 T - 1 <= 15 steps past its range
-constexpr int kDotPad = 17 * 64;
+constexpr int kDotMaxTokens = 8;           // calls with more tokens take the MFMA kernels
+// Longest K whose MT token rows are staged in LDS (at most 96 KB of them).
+constexpr int dot_max_k(int mt) { return mt <= 3 ? 16384 : 8192; }
+// Zeroed k past the last 64-k step: a wave's last two batches of T steps may
+// read up to 2 T - 1 steps past its range.
+constexpr int dot_pad(int t) { return (2 * t + 1) * 64; }
 
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
@@ -65,18 +68,19 @@ __device__ __forceinline__ float sum8(float v) {
   return v;
 }
 
-// MT tokens; GROUPS 8-row groups per workgroup; PARTS = 2 pairs gate rows n
+// M <= MT tokens (token rows M..MT-1 read as zero); GROUPS 8-row groups per workgroup; PARTS = 2 pairs gate rows n
 // with up rows N + n of a [2N, K] weight (SwiGLU), else 1; EPI: 0 plain,
 // 1 SwiGLU, 2 GELU.  ksw = 64-k steps per wave; rows_wg = output rows per
 // workgroup (<= 8 GROUPS).
 template <int MT, int GROUPS, int PARTS, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(kDotWaves * 64) void gemv_dot_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
-    int N, int K, int ksw, int rows_wg) {
+    int M, int N, int K, int ksw, int rows_wg) {
   static_assert(GROUPS * PARTS <= 8 && 8 % (GROUPS * PARTS) == 0, "8 loads per batch");
   static_assert(EPI != 1 || PARTS == 2, "SwiGLU pairs gate and up rows");
   constexpr int T = 8 / (GROUPS * PARTS);     // 64-k steps per batch of 8 loads
-  __shared__ __attribute__((aligned(16))) uint16_t xs[MT * (kDotMaxK + kDotPad)];
+  constexpr int kPad = dot_pad(T);
+  __shared__ __attribute__((aligned(16))) uint16_t xs[MT * (dot_max_k(MT) + kPad)];
   __shared__ float red[kDotWaves * GROUPS * 8 * PARTS * MT];
 
   const int lane = threadIdx.x & 63;
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(kDotWaves * 64) void gemv_dot_kernel(
   const int n0 = blockIdx.x * rows_wg;
   const int nrows = min(rows_wg, N - n0);
   const int slot = lane >> 3, kq = lane & 7;
-  const int KP = (K + 63) / 64 * 64 + kDotPad;   // LDS row pitch of the staged tokens
+  const int KP = (K + 63) / 64 * 64 + kPad;   // LDS row pitch of the staged tokens
 
   // one resource per part, based at its first row and bounded to the valid rows
   __amdgpu_buffer_rsrc_t wr[PARTS];
@@ -150,9 +154,9 @@ __global__ __launch_bounds__(kDotWaves * 64) void gemv_dot_kernel(
   {
     const int per_row = K / 8;                      // 16-byte pieces per token row
     const int total = MT * per_row;
-    constexpr int kMaxPieces = MT * kDotMaxK / 8 / (kDotWaves * 64);
+    constexpr int kMaxPieces = MT * dot_max_k(MT) / 8 / (kDotWaves * 64);
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)X, 0, (uint32_t)total * 16u, 0x00020000);
+        (void*)X, 0, (uint32_t)M * (uint32_t)per_row * 16u, 0x00020000);
     u32x4 xv[kMaxPieces];
 #pragma unroll
     for (int i = 0; i < kMaxPieces; ++i)
@@ -200,6 +204,7 @@ __global__ __launch_bounds__(kDotWaves * 64) void gemv_dot_kernel(
   __syncthreads();
   for (int v = threadIdx.x; v < nrows * MT; v += kDotWaves * 64) {
     const int r = v / MT, m = v - r * MT;
+    if (m >= M) continue;
     float s[PARTS];
 #pragma unroll
     for (int p = 0; p < PARTS; ++p) {
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(kDotWaves * 64) void gemv_dot_kernel(
 constexpr int kDotCUs = 256;   // compute units of an MI355X
 
 template <int MT, int PARTS, int EPI, bool OUT_F32>
-static void launch_dot(const void* x, const void* w, void* y, int N, int K, hipStream_t s) {
+static void launch_dot(const void* x, const void* w, void* y, int M, int N, int K, hipStream_t s) {
   // rows per workgroup: one workgroup per CU while that needs at most 64 rows
   // (32 gate|up pairs); 8-row groups, at most 8 loads per 64-k step
   constexpr int kMaxRows = 64 / PARTS;
@@ -234,7 +239,7 @@ static void launch_dot(const void* x, const void* w, void* y, int N, int K, hipS
   dim3 grid((N + rows_wg - 1) / rows_wg), block(kDotWaves * 64);
   auto X = static_cast<const uint16_t*>(x);
   auto Wp = static_cast<const uint16_t*>(w);
-#define TPL_DOT(G) hipLaunchKernelGGL((gemv_dot_kernel<MT, G, PARTS, EPI, OUT_F32>), grid, block, 0, s, X, Wp, y, N, K, ksw, rows_wg)
+#define TPL_DOT(G) hipLaunchKernelGGL((gemv_dot_kernel<MT, G, PARTS, EPI, OUT_F32>), grid, block, 0, s, X, Wp, y, M, N, K, ksw, rows_wg)
   if (groups <= 1) TPL_DOT(1);
   else if (groups <= 2) TPL_DOT(2);
   else if constexpr (PARTS == 1) {
@@ -248,21 +253,35 @@ static void launch_dot(const void* x, const void* w, void* y, int N, int K, hipS
 
 }  // namespace
 
-// Whether gemv_dot serves a call: 1..3 tokens, token rows that fit the LDS
-// stage.  K % 8 == 0 and 16-byte aligned x and w are the caller's conditions.
-bool gemv_dot_fits(int64_t M, int64_t K) { return M >= 1 && M <= 3 && K >= 8 && K <= kDotMaxK; }
+// Whether gemv_dot serves a call on a weight of `rows` x K: 1..3 tokens, or
+// 4..8 tokens on weights of more than 8192 rows, with token rows that fit the
+// LDS stage.  Measured per call over weight copies larger than the Infinity
+// Cache: the lm_head vocab shard [16032, 8192] at 4 / 5 / 8 tokens took 45.9 /
+// 49.0 / 49.2 us here against 54.8 / 53.6 / 54.0 on the LDS-ring kernel,
+// while the decode down projection [8192, 3584] at 5 and 8 tokens took 16.6
+// and 16.7 us against 13.6 (and QKV [1536, 4096] 14.5 against 13.5).  The
+// rule looks only at the weight's shape, so a fused-activation call and the
+// plain call on the same weight take the same kernel.  K % 8 == 0 and 16-byte
+// aligned x and w are the caller's conditions.
+bool gemv_dot_fits(int64_t M, int64_t rows, int64_t K) {
+  if (M < 1 || K < 8) return false;
+  if (M <= 3) return K <= dot_max_k((int)M);
+  return M <= kDotMaxTokens && rows > 8192 && K <= dot_max_k(8);
+}
 
 tp_status gemv_dot(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                    bool out_f32, hipStream_t s) {
-  const int Ni = (int)N, Ki = (int)K;
+  const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
 #define TPL_DOTM(MT)                                                         \
   do {                                                                       \
-    if (out_f32) launch_dot<MT, 1, 0, true>(x, w, y, Ni, Ki, s);             \
-    else launch_dot<MT, 1, 0, false>(x, w, y, Ni, Ki, s);                    \
+    if (out_f32) launch_dot<MT, 1, 0, true>(x, w, y, Mi, Ni, Ki, s);         \
+    else launch_dot<MT, 1, 0, false>(x, w, y, Mi, Ni, Ki, s);                \
   } while (0)
   if (M == 1) TPL_DOTM(1);
   else if (M == 2) TPL_DOTM(2);
-  else TPL_DOTM(3);
+  else if (M == 3) TPL_DOTM(3);
+  else if (M == 4) TPL_DOTM(4);
+  else TPL_DOTM(8);
 #undef TPL_DOTM
   TPL_LAUNCH_CHECK("gemv_dot");
   return TP_OK;
@@ -272,15 +291,17 @@ tp_status gemv_dot(const void* x, const void* w, void* y, int64_t M, int64_t N, 
 // (w is [I, K]); output bf16 [M, I].
 tp_status gemv_dot_act(const void* x, const void* w, void* h, int64_t M, int64_t I, int64_t K,
                        int act, hipStream_t s) {
-  const int Ii = (int)I, Ki = (int)K;
-#define TPL_DOTA(MT)                                                         \
-  do {                                                                       \
-    if (act == TP_ACT_SWIGLU) launch_dot<MT, 2, 1, false>(x, w, h, Ii, Ki, s); \
-    else launch_dot<MT, 1, 2, false>(x, w, h, Ii, Ki, s);                    \
+  const int Mi = (int)M, Ii = (int)I, Ki = (int)K;
+#define TPL_DOTA(MT)                                                                \
+  do {                                                                              \
+    if (act == TP_ACT_SWIGLU) launch_dot<MT, 2, 1, false>(x, w, h, Mi, Ii, Ki, s);  \
+    else launch_dot<MT, 1, 2, false>(x, w, h, Mi, Ii, Ki, s);                       \
   } while (0)
   if (M == 1) TPL_DOTA(1);
   else if (M == 2) TPL_DOTA(2);
-  else TPL_DOTA(3);
+  else if (M == 3) TPL_DOTA(3);
+  else if (M == 4) TPL_DOTA(4);
+  else TPL_DOTA(8);
 #undef TPL_DOTA
   TPL_LAUNCH_CHECK("gemv_dot_act");
   return TP_OK;

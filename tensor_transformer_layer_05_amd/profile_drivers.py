@@ -25,8 +25,9 @@ FETCH_SIZE`` and, separately, ``--pmc WRITE_SIZE``; a shard's bytes are the
 sums over the dispatches between its two markers.
 
 ``stream_ref``: 20 reads of 1 GiB by the reference stream kernel of
-``libtpref`` in the configuration the benchmark finds fastest, for
-``rocprofv3 --kernel-trace``.
+``libtpref`` in a given configuration (workgroups, waves, KB per wave per
+chunk, load flags: 1 = non-temporal, 2 = chunks interleaved over all waves),
+for ``rocprofv3 --kernel-trace``.
 
 ``vendor_gemm``: the plain gate|up GEMM (M=4096, K=8192, N=28672, bf16
 output) three times through ``torch.matmul`` (the vendor library's GEMM) and
@@ -213,14 +214,14 @@ def decode_traffic() -> None:
         del w
 
 
-def stream_ref(workgroups: int = 256, waves: int = 8, loads: int = 8) -> None:
+def stream_ref(workgroups: int = 256, waves: int = 8, loads: int = 8, flags: int = 0) -> None:
     from . import ref
     ref.lib()
     buf = torch.ones(HBM_REF_BYTES, dtype=torch.uint8, device="cuda")
     words = torch.empty(workgroups * waves * 64, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
     for _ in range(HBM_REF_CALLS):
-        ref.stream_read(buf, words, workgroups, waves, loads)
+        ref.stream_read(buf, words, workgroups, waves, loads, flags)
     torch.cuda.synchronize()
     print("stream_ref done", flush=True)
 

@@ -139,7 +139,9 @@ per rank-0 call):
 - `attn_prefill_tr_kernel`: causal 4096-token attention over 32 local q heads / 4 KV heads.
 - `reduce_rmsnorm_reg_kernel<4>`: sum of the two ranks' attention partials + residual, then the MLP's RMSNorm.
 - `reduce_kernel`, `rmsnorm_reg_kernel<4>`: the final sum of MLP partials; the first RMSNorm.
-- `gemm_stream_kernel<*, 1, *, *, *>`: decode linears with 1..3 tokens, and 4..16 tokens on the decode gate|up weight; `gemm_stream_dma_kernel<...>`: the other decode linears up to 64 tokens
+- `gemv_dot_kernel<...>`: decode linears with 1..3 tokens, and 4..8 tokens on weights of more than 8192 rows (the
+  lm_head shard); `gemm_stream_kernel<*, 1, *, *, *>`: 4..16 tokens on the decode gate|up weight;
+  `gemm_stream_dma_kernel<...>`: the other decode linears up to 64 tokens
   (weights and tokens through the per-wave LDS ring).
 - `attn_decode_kernel<false|true>` + `attn_decode_combine_kernel`: decode attention (contiguous / paged cache).
 - `vocab_argmax_kernel`: the lm_head shard's local greedy step.
@@ -523,8 +525,8 @@ def hbm_reference(out):
     med = lambda v: sorted(v)[len(v) // 2]
     copy = [dur(r) for r in ks if "copyBuffer" in r["Kernel_Name"]]    # the runtime's blit kernel
     red = [dur(r) for r in ks if "reduce_kernel" in r["Kernel_Name"]]
-    gemv = [dur(r) for r in ks if "gemm_stream_kernel" in r["Kernel_Name"]]
-    gemv_name = next(r["Kernel_Name"] for r in ks if "gemm_stream_kernel" in r["Kernel_Name"])
+    gemv = [dur(r) for r in ks if "gemv_dot_kernel" in r["Kernel_Name"]]
+    gemv_name = _short(next(r["Kernel_Name"] for r in ks if "gemv_dot_kernel" in r["Kernel_Name"]))
     wbytes = 7168 * 8192 * 2
     rows = [("device-to-device copy, 1 GiB read + 1 GiB written", copy, 2 * HBM_REF_BYTES),
             ("torch sum of a 1 GiB float32 tensor (read only)", red, HBM_REF_BYTES),
@@ -557,6 +559,7 @@ DECODE_SRCS = ["tensor_transformer_layer_05_amd/csrc/gemm_stream.hip",
 
 
 def _short(name):
+    name = name.replace("(anonymous namespace)::", "")
     return name.split("(")[0].replace("void ", "").replace("tpl::", "")[:90]
 
 
@@ -608,11 +611,11 @@ def decode_traffic(out):
 ## The read ceiling: the reference stream under the kernel trace
 
 ```
-rocprofv3 --kernel-trace --output-format csv -d gpurun_out/prof_stream -o s -- python3 -m tensor_transformer_layer_05_amd.profile_drivers stream_ref 256 8 8
+rocprofv3 --kernel-trace --output-format csv -d gpurun_out/prof_stream -o s -- python3 -m tensor_transformer_layer_05_amd.profile_drivers stream_ref 512 8 8 1
 ```
 
-{len(d)} reads of 1 GiB by `stream_read_kernel<8>` (256 workgroups x 8 waves, 8 KB per wave per chunk, the next chunk
-in flight: the register GEMV's load width and bytes in flight): median {med:.1f} us = {2 ** 30 / med / 1e3:.0f} GB/s
+{len(d)} reads of 1 GiB by `stream_read_kernel` with non-temporal loads (512 workgroups x 8 waves, 16-byte loads
+per lane, 8 KB per wave per chunk with the next chunk in flight): median {med:.1f} us = {2 ** 30 / med / 1e3:.0f} GB/s
 ({2 ** 30 / med / 1e3 / 8000:.3f} of 8 TB/s); min {d[0]:.1f} us, max {d[-1]:.1f} us.
 """
         data["stream_ref_median_us"] = round(med, 2)

@@ -45,6 +45,7 @@ ACT_SHAPES = [
     (2, 8192, 3584),     # two tokens, two 8-row groups per part
     (3, 4104, 4100),     # three tokens, ragged K ranges, four row groups per part
     (3, 16384, 40),      # the largest staged K, one row per workgroup
+    (8, 4096, 4100),     # SwiGLU on 8200 rows: dot-product kernel at 8 tokens; GELU not
     (5, 520, 130),       # ragged K range per wave, ragged rows
     (8, 8192, 3584),     # decode gate|up shard at 8 tokens: register kernel, 8 waves
     (13, 16384, 200),    # register kernel, 16 waves, ragged tokens
@@ -142,10 +143,11 @@ def test_column_linear_act_integer(act, M, K, I_):
 
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
 @pytest.mark.parametrize("M,K,I_", [(1, 8192, 3584), (2, 520, 700), (3, 4104, 1000), (8, 8192, 3584),
-                                    (4, 3584, 4096)])
+                                    (4, 3584, 4096), (6, 4096, 4100)])
 def test_fused_equals_activation_of_float32_sums(act, M, K, I_):
-    """Decode routes (dot-product kernel at 1..3 tokens, register kernel,
-    one-token-tile LDS ring): the fused call's float32 sums are the plain
+    """Decode routes (dot-product kernel at 1..3 tokens and at 4..8 on tall
+    weights, register kernel, one-token-tile LDS ring): the fused call's
+    float32 sums are the plain
     call's on the same weight (same K split), so its output is, bit for bit,
     the activation kernel applied to the float32 partials, rounded to bf16."""
     log(f"fused == act(fp32 partials) {act} M={M} K={K} I={I_}")

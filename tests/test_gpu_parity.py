@@ -78,6 +78,10 @@ INT_SHAPES = [
     # staged K; past it (K = 16392) the register kernel
     (1, 8192, 16032), (2, 3584, 8192), (3, 8200, 3000), (1, 4104, 20000), (3, 16384, 300),
     (2, 72, 256), (1, 16392, 64),
+    # 4..8 tokens on weights of more than 8192 rows: the dot-product kernel (a
+    # ragged last workgroup, 4 and 8 staged token rows with 5..8 tokens); K past
+    # its 8-token stage (8200) stays on the LDS-ring kernel
+    (4, 4096, 8200), (6, 1000, 9001), (8, 8192, 16032), (7, 8200, 9000),
     # element path (K not a multiple of 8)
     (5, 13, 7), (70, 37, 50),
 ]
