@@ -62,7 +62,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 v) { return __builtin_bi
 
 template <int ACT>
 __device__ __forceinline__ float act_fn(float g, float u) {
-  if constexpr (ACT == TP_ACT_SWIGLU) return g / (1.0f + expf(-g)) * u;
+  // SiLU(g) = g / (1 + e^-g) from the hardware base-2 exponential and
+  // reciprocal (about 1 ulp each), e^-g = 2^(-g log2 e): a few instructions
+  // where expf and an IEEE division take some twenty, which is the fused
+  // gate|up epilogue's cost.  Below g of about -88 the exponential is +inf and
+  // the reciprocal 0, giving -0 (the limit); a NaN stays NaN.
+  if constexpr (ACT == TP_ACT_SWIGLU)
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f)) * u;
   // GELU(g) = g * Phi(g) with Phi(g) = erfc(-g / sqrt 2) / 2: the erfc form
   // keeps full relative accuracy for negative g, where 1 + erf(.) cancels.
   else if constexpr (ACT == TP_ACT_GELU) return 0.5f * g * erfcf(-g * 0.70710678118654752f);
