@@ -120,7 +120,11 @@ def test_column_linear_act(act, M, K, I_):
 
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
 @pytest.mark.parametrize("M,K,I_", [(1, 64, 40), (3, 520, 700), (40, 136, 130), (200, 264, 300),
-                                    (11, 264, 4096)])
+                                    (11, 264, 4096),
+                                    # 256x256 tiles (outputs staged through LDS when full):
+                                    # SwiGLU full and ragged (GELU on 128x128 there), then both
+                                    # full
+                                    (4096, 136, 2048), (4000, 136, 2048), (4096, 136, 4096)])
 def test_column_linear_act_integer(act, M, K, I_):
     """Integer inputs: every projection is an exact integer in float32, so the
     fused route's only roundings are the fp32 activation and one bf16 store;
