@@ -359,6 +359,31 @@ __global__ __launch_bounds__(512) void attn_prefill_tr_kernel(TrArgs a) {
   // d = 8 (r/4) + 4 hl + r%4
   const float ltot = pair_sum(lrun);
   const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+  const bool o16 = ((a.os0 | a.os1 | a.os2) & 7) == 0 && (reinterpret_cast<uintptr_t>(a.o) & 15) == 0;
+  if (o16) {
+    // the wave's 32 rows go through LDS (free once every wave has passed the
+    // last barrier), so that each store instruction writes 4 whole rows of
+    // 256 bytes; 16-byte chunk c of row r sits at c ^ (r % 16)
+    uint16_t* sl = lds + wave * (kQW * 128);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int ch = (db * 4 + grp) ^ (c32 & 15);
+        *reinterpret_cast<u32x2*>(sl + c32 * 128 + ch * 8 + 4 * hl) =
+            u32x2{pack_bf2(oacc[db][grp * 4 + 0] * inv, oacc[db][grp * 4 + 1] * inv),
+                  pack_bf2(oacc[db][grp * 4 + 2] * inv, oacc[db][grp * 4 + 3] * inv)};
+      }
+#pragma unroll
+    for (int it = 0; it < kQW / 4; ++it) {
+      const int row = 4 * it + (lane >> 4), c = lane & 15;
+      const int sr = qw0 + row;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sl + row * 128 + ((c ^ (row & 15)) * 8));
+      if (sr < a.Sq)
+        *reinterpret_cast<u32x4*>(a.o + b * a.os0 + (int64_t)sr * a.os1 + h * a.os2 + c * 8) = v;
+    }
+    return;
+  }
   const int s = qw0 + c32;
   if (s < a.Sq) {
     uint16_t* orow = a.o + b * a.os0 + (int64_t)s * a.os1 + h * a.os2;
