@@ -452,6 +452,54 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_dma_kernel(
       return;
     }
   }
+  // The in-step loop's 8-wave tiles (256x320): the bf16 output tile is larger
+  // than the LDS, so it goes through in row groups of whole waves.
+  if constexpr (!kPP && C::NW == 8 && !OUT_F32 && VEC_OUT && EPI != 1) {
+    constexpr int OB = C::BN, CPR = OB / 8;
+    constexpr int H = (C::BM * OB * 2 + 2 * C::STAGE * 2 - 1) / (2 * C::STAGE * 2);   // row groups
+    constexpr int RG = C::BM / H;
+    static_assert(C::BM % H == 0 && RG % C::TM == 0 && CPR % 8 == 0 && (RG * CPR) % C::NT == 0,
+                  "row groups of whole waves, swizzle groups, store rounds");
+    if (m0 + C::BM <= M && n0 + OB <= N) {
+      uint16_t* ot = lds;   // [RG][OB]; 16-byte chunk c of row r at c ^ (r & 7)
+#pragma unroll
+      for (int hg = 0; hg < H; ++hg) {
+        if ((wm * C::TM) / RG == hg) {
+#pragma unroll
+          for (int i = 0; i < C::FA; ++i) {
+#pragma unroll
+            for (int j = 0; j < C::FB; ++j) {
+              const int row = wm * C::TM + 32 * j + frow - hg * RG;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  if constexpr (EPI == 2) v[e] = act_fn<TP_ACT_GELU>(acc[i][j][4 * q + e], 0.f);
+                  else v[e] = acc[i][j][4 * q + e];
+                }
+                const int col = wn * C::TN + 32 * i + 8 * q + 4 * fh;
+                const int ch = (col >> 3) ^ (row & 7);
+                *reinterpret_cast<u32x2*>(ot + row * OB + ch * 8 + (col & 7)) =
+                    u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+              }
+            }
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < RG * CPR / C::NT; ++it) {
+          const int idx = it * C::NT + threadIdx.x;
+          const int row = idx / CPR, c = idx % CPR;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(ot + row * OB + (c ^ (row & 7)) * 8);
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(Y) + (int64_t)(m0 + hg * RG + row) * N + n0 +
+                                    c * 8) = val;
+        }
+        if (hg + 1 < H) __syncthreads();
+      }
+      return;
+    }
+  }
   if constexpr (kPairInWave) {
     // acc[i] holds gate sums and acc[i + FA/2] the up sums of the same outputs
     // n = n0 + wn*TN/2 + 32i + 8*(r/4) + 4*(lane/32) + r%4.
