@@ -22,6 +22,12 @@ GEMM_SRCS = ["tensor_transformer_layer_05_amd/csrc/gemm_dma.hip",
 FUSED = "DmaTile<256, 256, 2, 4>, false, true, 1>"
 
 
+def _od(out):
+    """The raw-output directory as it appears in the commands of a summary
+    (the directory the summary script was given)."""
+    return os.path.normpath(out)
+
+
 def _csv(pattern):
     files = glob.glob(pattern, recursive=True)
     if not files:
@@ -67,9 +73,9 @@ Commands (from the repository root; the driver runs one plain 256 MiB device-to-
 gate|up launch with the SwiGLU epilogue, then one plain gate|up launch; M=4096 K=8192 2I=28672 bf16):
 
 ```
-rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o f -- python3 -m tensor_transformer_layer_05_amd.profile_drivers gemm_traffic
-rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o w -- python3 -m tensor_transformer_layer_05_amd.profile_drivers gemm_traffic
-python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d {_od(out)}/pmc_fetch -o f -- python3 -m tensor_transformer_layer_05_amd.profile_drivers gemm_traffic
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d {_od(out)}/pmc_write -o w -- python3 -m tensor_transformer_layer_05_amd.profile_drivers gemm_traffic
+python3 -m tensor_transformer_layer_05_amd.profile_summary {_od(out)}
 ```
 
 | dispatch | FETCH_SIZE KiB | WRITE_SIZE KiB |
@@ -115,8 +121,8 @@ def kernel_stats(out):
 Command (from /tmp with TMPDIR=/tmp; REPO = repository root), then the summary script:
 
 ```
-rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_bench -o bench -- python3 $REPO/bench.py --steps 5 --warmup 2 --no-cpu-baseline
-python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
+rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/{_od(out)}/prof_bench -o bench -- python3 $REPO/bench.py --steps 5 --warmup 2 --no-cpu-baseline
+python3 -m tensor_transformer_layer_05_amd.profile_summary {_od(out)}
 ```
 
 The bench line of the same run (under the profiler): value {d['value']} TFLOP/s, {d['ms_per_step']} ms per step;
@@ -196,9 +202,9 @@ def counters(out):
 Commands (from the repository root), then the summary script:
 
 ```
-rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/pmc_mfma -o m -- python3 -m tensor_transformer_layer_05_amd.profile_drivers gemm_traffic
-rocprofv3 --pmc SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/pmc_lds -o l -- python3 -m tensor_transformer_layer_05_amd.profile_drivers gemm_traffic
-python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
+rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE --output-format csv -d {_od(out)}/pmc_mfma -o m -- python3 -m tensor_transformer_layer_05_amd.profile_drivers gemm_traffic
+rocprofv3 --pmc SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE --output-format csv -d {_od(out)}/pmc_lds -o l -- python3 -m tensor_transformer_layer_05_amd.profile_drivers gemm_traffic
+python3 -m tensor_transformer_layer_05_amd.profile_summary {_od(out)}
 ```
 
 Fused gate|up launch (M=4096, K=8192, 2I=28672, SwiGLU epilogue), as profiled: {gm[1]:.1f} us.
@@ -293,7 +299,7 @@ def vendor_counters(out):
                      for q, (_, _, f) in ratios.items())
     craw = sorted(set(rmed["vendor"]) | set(rmed["library"]))
     raw_rows = "\n".join(f"| `{c}` | {rmed['vendor'].get(c, 0):.4g} | {rmed['library'].get(c, 0):.4g} |" for c in craw)
-    cmds = "\n".join(f"rocprofv3 --pmc {p} --output-format csv -d $REPO/gpurun_out/pmc_vendor{i + 1} -o v -- "
+    cmds = "\n".join(f"rocprofv3 --pmc {p} --output-format csv -d $REPO/{_od(out)}/pmc_vendor{i + 1} -o v -- "
                       f"python3 -m tensor_transformer_layer_05_amd.profile_drivers vendor_gemm"
                       for i, p in enumerate(VENDOR_PASSES))
     data = {"vendor_kernel": names.get("vendor"), "library_kernel": names.get("library"),
@@ -305,7 +311,7 @@ Commands (from /tmp with TMPDIR=/tmp and PYTHONPATH=$REPO, REPO = repository roo
 
 ```
 {cmds}
-python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out gate_up_vendor_counters
+python3 -m tensor_transformer_layer_05_amd.profile_summary {_od(out)} gate_up_vendor_counters
 ```
 
 M=4096, K=8192, N=28672, bf16 in and out, the same operands for both. Three launches of each kernel per
@@ -378,7 +384,7 @@ def ffn_counters(out):
         m["traffic_bytes"] = m["fetch_bytes"] + m["write_bytes"]
         m["tflops_as_profiled"] = alg[k]["flop"] / m["duration_us"] / 1e6
         m["algorithmic_bytes"] = alg[k]["bytes"]
-    cmds = "\n".join(f"timeout -s KILL 90 rocprofv3 --pmc {p} --output-format csv -d $REPO/gpurun_out/{d} -o f -- "
+    cmds = "\n".join(f"timeout -s KILL 90 rocprofv3 --pmc {p} --output-format csv -d $REPO/{_od(out)}/{d} -o f -- "
                       f"python3 -m tensor_transformer_layer_05_amd.profile_drivers ffn_gemms"
                       for d, p in FFN_PASSES)
 
@@ -404,7 +410,7 @@ Commands (from /tmp with TMPDIR=/tmp and PYTHONPATH=$REPO, REPO = repository roo
 
 ```
 {cmds}
-python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out ffn_gemm_counters
+python3 -m tensor_transformer_layer_05_amd.profile_summary {_od(out)} ffn_gemm_counters
 ```
 
 Rank 0 of the GELU FFN at TP=8: fc1 = [2048, 12288] x [6144, 12288]^T with GELU in the epilogue (bf16 out),
@@ -457,8 +463,8 @@ Command (from /tmp with TMPDIR=/tmp and PYTHONPATH=$REPO, REPO = repository root
 (from the repository root):
 
 ```
-timeout -s KILL 90 rocprofv3 --pmc {ATTN_PASS} --output-format csv -d $REPO/gpurun_out/pmc_attn -o a -- python3 -m tensor_transformer_layer_05_amd.profile_drivers prefill_attention
-python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out prefill_attention_counters
+timeout -s KILL 90 rocprofv3 --pmc {ATTN_PASS} --output-format csv -d $REPO/{_od(out)}/pmc_attn -o a -- python3 -m tensor_transformer_layer_05_amd.profile_drivers prefill_attention
+python3 -m tensor_transformer_layer_05_amd.profile_summary {_od(out)} prefill_attention_counters
 ```
 
 One sequence of 4096 tokens, causal, 32 q / 4 KV heads of 128 on strided views of the fused QKV output;
@@ -500,8 +506,8 @@ def decode_span(out):
 Command (from /tmp with TMPDIR=/tmp; REPO = repository root), then the summary script:
 
 ```
-rocprofv3 --kernel-trace --output-format csv -d $REPO/gpurun_out/prof_span -o s -- python3 -m tensor_transformer_layer_05_amd.profile_drivers decode_attn_span
-python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
+rocprofv3 --kernel-trace --output-format csv -d $REPO/{_od(out)}/prof_span -o s -- python3 -m tensor_transformer_layer_05_amd.profile_drivers decode_attn_span
+python3 -m tensor_transformer_layer_05_amd.profile_summary {_od(out)}
 ```
 
 The TP=4 decode attention shard shape (32 sequences, 8 q / 2 KV heads of 128, bf16 cache), {n} calls per key
@@ -538,8 +544,8 @@ def hbm_reference(out):
 Command (from /tmp with TMPDIR=/tmp; REPO = repository root), then the summary script:
 
 ```
-rocprofv3 --kernel-trace --output-format csv -d $REPO/gpurun_out/prof_hbm -o h -- python3 -m tensor_transformer_layer_05_amd.profile_drivers hbm_reference
-python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
+rocprofv3 --kernel-trace --output-format csv -d $REPO/{_od(out)}/prof_hbm -o h -- python3 -m tensor_transformer_layer_05_amd.profile_drivers hbm_reference
+python3 -m tensor_transformer_layer_05_amd.profile_summary {_od(out)}
 ```
 
 {HBM_REF_CALLS} calls each; median kernel durations from the trace; the fraction is of the 8 TB/s HBM peak.
@@ -611,7 +617,7 @@ def decode_traffic(out):
 ## The read ceiling: the reference stream under the kernel trace
 
 ```
-rocprofv3 --kernel-trace --output-format csv -d gpurun_out/prof_stream -o s -- python3 -m tensor_transformer_layer_05_amd.profile_drivers stream_ref 512 8 8 1
+rocprofv3 --kernel-trace --output-format csv -d {_od(out)}/prof_stream -o s -- python3 -m tensor_transformer_layer_05_amd.profile_drivers stream_ref 512 8 8 1
 ```
 
 {len(d)} reads of 1 GiB by `stream_read_kernel` with non-temporal loads (512 workgroups x 8 waves, 16-byte loads
@@ -625,9 +631,9 @@ per lane, 8 KB per wave per chunk with the next chunk in flight): median {med:.1
 Commands (from the repository root):
 
 ```
-rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_dfetch -o f -- python3 -m tensor_transformer_layer_05_amd.profile_drivers decode_traffic
-rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_dwrite -o w -- python3 -m tensor_transformer_layer_05_amd.profile_drivers decode_traffic
-python3 -m tensor_transformer_layer_05_amd.profile_summary gpurun_out
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d {_od(out)}/pmc_dfetch -o f -- python3 -m tensor_transformer_layer_05_amd.profile_drivers decode_traffic
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d {_od(out)}/pmc_dwrite -o w -- python3 -m tensor_transformer_layer_05_amd.profile_drivers decode_traffic
+python3 -m tensor_transformer_layer_05_amd.profile_summary {_od(out)}
 ```
 
 The driver runs one plain 256 MiB copy (calibration: {cf:.1f} KiB fetched, {cw:.1f} KiB written for 262144 KiB
@@ -655,7 +661,9 @@ def main(argv=None):
     decode_attention_span, hbm_reference; default: all
     whose raw outputs are present)."""
     argv = argv or sys.argv[1:]
-    out = argv[0] if argv else "gpurun_out"
+    if not argv:
+        raise SystemExit("usage: python3 -m tensor_transformer_layer_05_amd.profile_summary <out_dir> [summary ...]")
+    out = argv[0]
     only = set(argv[1:])
     raw = lambda d, pat: glob.glob(os.path.join(out, d, "**", pat), recursive=True)
     has = lambda name, d, pat: (not only or name in only) and raw(d, pat)
